@@ -1,0 +1,68 @@
+"""W4A4 GEMM: exact INT4 x INT4 -> INT32 product and the scale epilogue.
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Definition (QuaRot paper, activation-quantization paragraph; performance
+paragraph: INT4 GEMM with an INT32 accumulator): acc[t, n] = sum_k
+A_q[t, k] W_q[n, k] exactly, then the output is acc times the token (row)
+scale times the channel (column) scale.
+
+Reading taken: the pages cast the INT32 result to FP16 before scaling; that
+overflows once |acc| > 65504 (|acc| can reach 64 K), so the epilogue works in
+fp32 as Y = fp16_rne(fp32(fp32(acc) * a_s[t]) * w_s[n]).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .quant import unpack_int4
+
+F32 = np.float32
+F16 = np.float16
+
+
+def int4_matmul_exact(a_codes: np.ndarray, w_codes: np.ndarray) -> np.ndarray:
+    """acc = A W^T for int codes, exact, as int64.
+
+    float64 BLAS is exact here: every product and partial sum is an integer of
+    magnitude <= 64 K < 2^53, so no rounding happens in any summation order.
+    """
+    a = np.asarray(a_codes, dtype=np.float64)
+    w = np.asarray(w_codes, dtype=np.float64)
+    assert a.shape[-1] == w.shape[-1]
+    assert a.shape[-1] * 64 < 2 ** 53
+    return (a @ w.T).astype(np.int64)
+
+
+def int4_matmul_bruteforce(a_codes: np.ndarray, w_codes: np.ndarray) -> np.ndarray:
+    """Triple loop in Python integers (tiny shapes only)."""
+    a = np.asarray(a_codes).astype(int).tolist()
+    w = np.asarray(w_codes).astype(int).tolist()
+    return np.array([[sum(x * y for x, y in zip(ar, wr)) for wr in w] for ar in a], dtype=np.int64)
+
+
+def w4a4_acc(a_packed: np.ndarray, w_packed: np.ndarray) -> np.ndarray:
+    """Exact int64 accumulators from packed operands [T, K/2] and [N, K/2]."""
+    return int4_matmul_exact(unpack_int4(a_packed), unpack_int4(w_packed))
+
+
+def epilogue_recipe(acc: np.ndarray, a_scale: np.ndarray, w_scale: np.ndarray) -> np.ndarray:
+    """fp16 Y = fp16_rne(fp32(fp32(acc) * a_s[t]) * w_s[n])."""
+    acc32 = np.asarray(acc).astype(F32)   # |acc| < 2^24: exact
+    a_s = np.asarray(a_scale, dtype=F16).astype(F32)[:, None]
+    w_s = np.asarray(w_scale, dtype=F16).astype(F32)[None, :]
+    with np.errstate(over="ignore"):
+        y = ((acc32 * a_s).astype(F32) * w_s).astype(F32)
+        return y.astype(F16)
+
+
+def epilogue_math(acc: np.ndarray, a_scale: np.ndarray, w_scale: np.ndarray) -> np.ndarray:
+    """float64 acc * a_s[t] * w_s[n]."""
+    a_s = np.asarray(a_scale, dtype=F16).astype(np.float64)[:, None]
+    w_s = np.asarray(w_scale, dtype=F16).astype(np.float64)[None, :]
+    return np.asarray(acc, dtype=np.float64) * a_s * w_s
+
+
+def w4a4_gemm(a_packed, a_scale, w_packed, w_scale) -> tuple[np.ndarray, np.ndarray]:
+    """(fp16 Y, int64 acc) of the W4A4 linear layer."""
+    acc = w4a4_acc(a_packed, w_packed)
+    return epilogue_recipe(acc, a_scale, w_scale), acc

@@ -1,0 +1,154 @@
+"""Pins for the oracle's symmetric INT4 quantizer, packing and GEMM."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import gemm, hadamard as had, quant
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_pack_order_hand_built():
+    # byte j: code 2j in the low nibble, code 2j+1 in the high nibble, two's complement
+    codes = np.array([[1, -1, 7, -8, 0, 3]])
+    assert quant.pack_int4(codes).tolist() == [[0xF1, 0x87, 0x30]]
+    assert quant.unpack_int4(np.array([[0xF1, 0x87, 0x30]], dtype=np.uint8)).tolist() == codes.tolist()
+
+
+def test_pack_roundtrip_all_pairs():
+    a, b = np.meshgrid(np.arange(-8, 8), np.arange(-8, 8))
+    codes = np.stack([a.ravel(), b.ravel()], axis=1)
+    packed = quant.pack_int4(codes)
+    assert sorted(packed.ravel().tolist()) == list(range(256))
+    assert np.array_equal(quant.unpack_int4(packed), codes)
+
+
+def test_scale_one_gives_plain_rounding():
+    # max|y| = 7 -> s = 1 exactly, so codes are round-half-even(y)
+    y = np.array([[7.0, 2.5, -2.5, 3.5, -0.5, 0.5, 1.5, 0.0, -6.49, 4.51]])
+    q, s = quant.sym_quant_math(y)
+    assert s.tolist() == [1.0]
+    assert q.tolist() == [[7, 2, -2, 4, 0, 0, 2, 0, -6, 5]]
+    q2, s2 = quant.sym_quant_recipe(y.astype(np.float32), 10, rotated=False)
+    assert q2.tolist() == q.tolist() and s2.tolist() == [1.0]
+
+
+def test_blog_bucket_example():
+    g = json.load(open(os.path.join(GOLDEN, "blog_quant_bucket_example.json")))
+    a, b = g["values_same_bucket"]
+    y = np.array([[g["row_max"], a, b, -1.0]])
+    q, s = quant.sym_quant_math(y)
+    assert float(s[0]) == pytest.approx(g["expected_scale"], rel=1e-3)  # fp16 scale
+    assert q[0, 0] == g["expected_code_of_max"]
+    assert q[0, 1] == q[0, 2]
+
+
+def test_clip_drives_plus_eight_to_seven():
+    # clip 0.9: s = 0.9 for max 7, 7/0.9 = 7.78 rounds to 8 -> clamped to 7; -7.78 -> -8 is kept
+    y = np.array([[7.0, -7.0, 0.9, -0.40]])
+    q, s = quant.sym_quant_math(y, clip=0.9)
+    assert float(s[0]) == pytest.approx(0.9, rel=1e-3)
+    assert q.tolist() == [[7, -8, 1, 0]]
+    q2, _ = quant.sym_quant_recipe(y.astype(np.float32), 4, rotated=False, clip=0.9)
+    assert q2.tolist() == q.tolist()
+
+
+def test_zero_row():
+    y = np.zeros((2, 16))
+    y[1, 3] = 1.0
+    q, s = quant.sym_quant_math(y)
+    assert s[0] == 0 and not q[0].any()
+    q2, s2 = quant.sym_quant_recipe(y.astype(np.float32), 16, rotated=True)
+    assert s2[0] == 0 and not q2[0].any()
+
+
+def test_recipe_agrees_with_math_away_from_ties():
+    d = 4096
+    x = wl.activations(1, 0, 64, d, n_outliers=4, lo=50, hi=50)
+    s = wl.signs(1, d)
+    y64 = had.rotate(x.astype(np.float64), s)
+    z32 = had.rotate_unnormalised(x.astype(np.float64), s).astype(np.float32)
+    qm, sm = quant.sym_quant_math(y64)
+    qr, sr = quant.sym_quant_recipe(z32, d, rotated=True)
+    # scales: equal or one fp16 ulp apart
+    ulp = np.abs(sm.astype(np.float32).view(np.int32) - sr.astype(np.float32).view(np.int32))
+    assert (sm == sr).mean() > 0.9
+    assert np.all(np.abs(sm.view(np.int16).astype(int) - sr.view(np.int16).astype(int)) <= 1), ulp
+    diff = qm.astype(int) - qr.astype(int)
+    assert np.abs(diff).max() <= 1
+    near = quant.tie_distance(y64, sm) < 4e-3
+    assert not np.any((diff != 0) & ~near)
+
+
+def test_rotation_removes_outliers_and_improves_sqnr():
+    # Qualitative pin (QuaRot paper Fig. 1; QuaRot blog outlier demo): after the
+    # rotation the per-token INT4 quantization error drops sharply.
+    d = 4096
+    x = wl.activations(1, 0, 32, d, n_outliers=4, lo=50, hi=50).astype(np.float64)
+    s = wl.signs(1, d)
+
+    def sqnr(y):
+        q, sc = quant.sym_quant_math(y)
+        err = quant.dequant(q, sc) - y
+        return 10 * np.log10((y ** 2).sum() / (err ** 2).sum())
+
+    plain, rotated = sqnr(x), sqnr(had.rotate(x, s))
+    assert rotated > plain + 10.0
+
+
+# ----------------------------- GEMM ----------------------------------------
+
+def test_gemm_exact_vs_bruteforce():
+    rng = np.random.default_rng(3)
+    a = rng.integers(-8, 8, size=(5, 64))
+    w = rng.integers(-8, 8, size=(7, 64))
+    assert np.array_equal(gemm.int4_matmul_exact(a, w), gemm.int4_matmul_bruteforce(a, w))
+    # from packed bytes, through the unpack path
+    ap, wp = quant.pack_int4(a), quant.pack_int4(w)
+    assert np.array_equal(gemm.w4a4_acc(ap, wp), gemm.int4_matmul_bruteforce(a, w))
+
+
+def test_gemm_extreme_magnitude():
+    k = 28672
+    a = np.full((2, k), -8)
+    w = np.full((3, k), -8)
+    w[1] = 7
+    acc = gemm.int4_matmul_exact(a, w)
+    assert acc[0, 0] == 64 * k and acc[0, 1] == -56 * k
+
+
+def test_epilogue_values():
+    acc = np.array([[1000, -3, 0], [1835008, 7, 65536 * 16]])
+    a_s = np.array([0.5, 0.25], dtype=np.float16)
+    w_s = np.array([0.25, 2.0, 1.0], dtype=np.float16)
+    y = gemm.epilogue_recipe(acc, a_s, w_s)
+    assert y[0].tolist() == [125.0, -3.0, 0.0]
+    assert y[1, 1] == np.float16(3.5)
+    assert np.isinf(y[1, 2])  # 262144 overflows fp16 -> +inf
+    np.testing.assert_allclose(gemm.epilogue_math(acc, a_s, w_s)[0], [125.0, -3.0, 0.0])
+
+
+def test_tiny_w4a4_linear_tracks_fp_product():
+    # End-to-end on the tiny workload shape (scaled down in N): rotate both X and W
+    # with the same R, quantize, multiply: the result tracks X W^T.
+    d, n = 4096, 64
+    x = wl.activations(1, 0, 32, d, n_outliers=4, lo=50, hi=50).astype(np.float64)
+    w = wl.weights(1, 1, n, d).astype(np.float64)
+    s = wl.signs(1, d)
+    qa, sa = quant.sym_quant_math(had.rotate(x, s))
+    qw, sw = quant.sym_quant_math(had.rotate(w, s))
+    y, acc = gemm.w4a4_gemm(quant.pack_int4(qa), sa, quant.pack_int4(qw), sw)
+    ref = x @ w.T
+    rel = np.linalg.norm(y.astype(np.float64) - ref) / np.linalg.norm(ref)
+    # Uniform INT4 noise with step max/7 on a Gaussian row whose max is ~4 sigma
+    # has relative rms ~ 4 / (7 sqrt(12)) = 0.165 per operand, ~0.23 for two.
+    assert rel < 0.3
+    # without the rotation the same quantization is far worse
+    qa0, sa0 = quant.sym_quant_math(x)
+    qw0, sw0 = quant.sym_quant_math(w)
+    y0, _ = gemm.w4a4_gemm(quant.pack_int4(qa0), sa0, quant.pack_int4(qw0), sw0)
+    rel0 = np.linalg.norm(y0.astype(np.float64) - ref) / np.linalg.norm(ref)
+    assert rel0 > 2 * rel
