@@ -1,0 +1,232 @@
+"""Python binding of libquarot_hip.so (QuaRot online Hadamard + INT4 hot path on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/qr.h``.  PyTorch supplies device
+memory and the current stream.  If the shared library is missing the import
+still succeeds, but the first call raises, naming the build command; nothing
+falls back to a CPU or PyTorch implementation.
+
+Functions (same names as the C entry points without the ``qr_`` prefix):
+  hadamard_quant(x, signs, clip_ratio, rotate=True, z_dbg=False) -> (q_u8, scale_f16[, z])
+  hadamard(x, signs, out_dtype=torch.float32) -> y
+  w4a4_gemm(a_q, a_scale, w_q, w_scale, acc_dbg=False) -> y_f16[, acc_i32]
+  kv_rotate_quant(kv, signs, group, clip_ratio, cache_q, cache_meta, start_pos,
+                  rotate=True, z_dbg=False) -> None[, z]
+  hadamard_factor(d) -> (n, m);  abi_version();  status_str(code)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+
+LIB_PATH = Path(__file__).resolve().parent / "lib" / "libquarot_hip.so"
+
+QR_ROT_NONE = 0
+QR_ROT_HADAMARD = 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m hadamard_rotation_int4_amd.build`"
+            " (there is no CPU or PyTorch fallback)")
+    lib = ctypes.CDLL(str(LIB_PATH))
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.qr_abi_version.restype = ctypes.c_int
+    lib.qr_abi_version.argtypes = []
+    lib.qr_status_str.restype = ctypes.c_char_p
+    lib.qr_status_str.argtypes = [ctypes.c_int]
+    lib.qr_hadamard_factor.restype = ctypes.c_int
+    lib.qr_hadamard_factor.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.qr_hadamard_quant.restype = ctypes.c_int
+    lib.qr_hadamard_quant.argtypes = [vp, i64, i32, i64, ctypes.c_int, vp, f32, vp, vp, vp, vp]
+    lib.qr_hadamard.restype = ctypes.c_int
+    lib.qr_hadamard.argtypes = [vp, i64, i32, i64, vp, vp, i32, vp]
+    lib.qr_w4a4_gemm.restype = ctypes.c_int
+    lib.qr_w4a4_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp, vp]
+    lib.qr_kv_rotate_quant.restype = ctypes.c_int
+    lib.qr_kv_rotate_quant.argtypes = [vp, i32, i32, i32, i32, i64, ctypes.c_int, vp, i32, f32,
+                                       vp, vp, i32, i32, vp, vp]
+    _lib = lib
+    return lib
+
+
+def lib_loaded_path() -> str:
+    _load()
+    return str(LIB_PATH)
+
+
+def abi_version() -> int:
+    return int(_load().qr_abi_version())
+
+
+def status_str(code: int) -> str:
+    return _load().qr_status_str(int(code)).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise RuntimeError(f"{what}: {status_str(code)}")
+
+
+def hadamard_factor(d: int) -> tuple[int, int]:
+    n, m = ctypes.c_int32(), ctypes.c_int32()
+    _check(_load().qr_hadamard_factor(int(d), ctypes.byref(n), ctypes.byref(m)),
+           f"qr_hadamard_factor({d})")
+    return n.value, m.value
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _signs(signs, d, device):
+    torch = _torch()
+    if signs is None:
+        return None
+    _need(signs, torch.int8, "signs", 1)
+    if signs.numel() != d or not signs.is_contiguous():
+        raise ValueError(f"signs must be a contiguous int8 vector of length {d}")
+    if signs.device != device:
+        raise ValueError("signs must be on the same device as x")
+    return signs
+
+
+def hadamard_quant(x, signs=None, clip_ratio: float = 1.0, rotate: bool = True,
+                   z_dbg: bool = False, out=None, stream=None):
+    """Rotate (optionally) and quantize the rows of x [T, d] (fp16, row stride % 8 == 0).
+
+    Returns (q uint8 [T, d/2], scale fp16 [T]) and, with z_dbg, z fp32 [T, d].
+    ``out`` may pass preallocated (q, scale) tensors.
+    """
+    torch = _torch()
+    _need(x, torch.float16, "x", 2)
+    if x.numel() and x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous (stride(1) == 1)")
+    T, d = x.shape
+    s = _signs(signs, d, x.device) if rotate else None
+    if out is None:
+        q = torch.empty((T, d // 2), dtype=torch.uint8, device=x.device)
+        sc = torch.empty((T,), dtype=torch.float16, device=x.device)
+    else:
+        q, sc = out
+        _need(q, torch.uint8, "q")
+        _need(sc, torch.float16, "scale")
+        if q.numel() != T * (d // 2) or not q.is_contiguous() or sc.numel() != T:
+            raise ValueError("out tensors have the wrong size or layout")
+    z = torch.empty((T, d), dtype=torch.float32, device=x.device) if z_dbg else None
+    code = _load().qr_hadamard_quant(_ptr(x), T, d, x.stride(0) if T > 0 else d,
+                                     QR_ROT_HADAMARD if rotate else QR_ROT_NONE, _ptr(s),
+                                     float(clip_ratio), _ptr(q), _ptr(sc), _ptr(z), _stream(stream))
+    _check(code, "qr_hadamard_quant")
+    return (q, sc, z) if z_dbg else (q, sc)
+
+
+def hadamard(x, signs=None, out_dtype=None, stream=None):
+    """y = H_d diag(s) x / sqrt(d) row-wise; x fp16 [T, d]; y fp32 (default) or fp16."""
+    torch = _torch()
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    _need(x, torch.float16, "x", 2)
+    if x.numel() and x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous (stride(1) == 1)")
+    if out_dtype not in (torch.float32, torch.float16):
+        raise ValueError("out_dtype must be float32 or float16")
+    T, d = x.shape
+    s = _signs(signs, d, x.device)
+    y = torch.empty((T, d), dtype=out_dtype, device=x.device)
+    code = _load().qr_hadamard(_ptr(x), T, d, x.stride(0) if T > 0 else d, _ptr(s), _ptr(y),
+                               1 if out_dtype == torch.float32 else 0, _stream(stream))
+    _check(code, "qr_hadamard")
+    return y
+
+
+def w4a4_gemm(a_q, a_scale, w_q, w_scale, acc_dbg: bool = False, out=None, stream=None):
+    """Y fp16 [T, N] = dequant(A_q W_q^T); a_q uint8 [T, K/2], w_q uint8 [N, K/2]."""
+    torch = _torch()
+    _need(a_q, torch.uint8, "a_q", 2)
+    _need(w_q, torch.uint8, "w_q", 2)
+    _need(a_scale, torch.float16, "a_scale", 1)
+    _need(w_scale, torch.float16, "w_scale", 1)
+    for name, t in (("a_q", a_q), ("w_q", w_q), ("a_scale", a_scale), ("w_scale", w_scale)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    T, kh = a_q.shape
+    N, kh2 = w_q.shape
+    if kh != kh2 or a_scale.numel() != T or w_scale.numel() != N:
+        raise ValueError("inconsistent GEMM operand shapes")
+    K = 2 * kh
+    y = torch.empty((T, N), dtype=torch.float16, device=a_q.device) if out is None else out
+    if out is not None:
+        _need(y, torch.float16, "out", 2)
+        if tuple(y.shape) != (T, N) or not y.is_contiguous():
+            raise ValueError("out must be a contiguous fp16 [T, N] tensor")
+    acc = torch.empty((T, N), dtype=torch.int32, device=a_q.device) if acc_dbg else None
+    code = _load().qr_w4a4_gemm(_ptr(a_q), _ptr(a_scale), T, _ptr(w_q), _ptr(w_scale), N, K,
+                                _ptr(y), _ptr(acc), _stream(stream))
+    _check(code, "qr_w4a4_gemm")
+    return (y, acc) if acc_dbg else y
+
+
+def kv_rotate_quant(kv, signs, group: int, clip_ratio: float, cache_q, cache_meta,
+                    start_pos: int, rotate: bool = True, z_dbg: bool = False, stream=None):
+    """Quantize kv fp16 [B, S_new, H, Dh] (last dim contiguous, heads packed) into the cache.
+
+    cache_q uint8 [B, H, S_max, Dh/2]; cache_meta fp16 [B, H, S_max, Dh/group, 2].
+    Returns z fp32 [B, S_new, H, Dh] when z_dbg.
+    """
+    torch = _torch()
+    _need(kv, torch.float16, "kv", 4)
+    _need(cache_q, torch.uint8, "cache_q", 4)
+    _need(cache_meta, torch.float16, "cache_meta", 5)
+    B, S_new, H, Dh = kv.shape
+    if kv.stride(3) != 1 or kv.stride(2) != Dh or (S_new > 1 and kv.stride(0) != S_new * kv.stride(1)):
+        raise ValueError("kv must be [B, S_new, H, Dh] with heads packed and one token stride")
+    if not cache_q.is_contiguous() or not cache_meta.is_contiguous():
+        raise ValueError("cache tensors must be contiguous")
+    S_max = cache_q.shape[2]
+    if tuple(cache_q.shape) != (B, H, S_max, Dh // 2) or \
+            tuple(cache_meta.shape) != (B, H, S_max, Dh // group, 2):
+        raise ValueError("cache tensors have the wrong shape")
+    ld = kv.stride(1) if S_new > 1 else (kv.stride(0) if B > 1 else H * Dh)
+    s = _signs(signs, Dh, kv.device) if rotate else None
+    z = torch.empty((B, S_new, H, Dh), dtype=torch.float32, device=kv.device) if z_dbg else None
+    code = _load().qr_kv_rotate_quant(_ptr(kv), B, S_new, H, Dh, ld,
+                                      QR_ROT_HADAMARD if rotate else QR_ROT_NONE, _ptr(s),
+                                      int(group), float(clip_ratio), _ptr(cache_q),
+                                      _ptr(cache_meta), S_max, int(start_pos), _ptr(z),
+                                      _stream(stream))
+    _check(code, "qr_kv_rotate_quant")
+    return z

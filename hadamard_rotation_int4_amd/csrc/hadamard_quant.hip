@@ -1,0 +1,666 @@
+// Online randomized Hadamard rotation fused with per-token symmetric INT4
+// quantization and nibble packing (qr_hadamard_quant), and the rotation alone
+// (qr_hadamard), for gfx950.
+//
+// What is computed (QuaRot paper, background on Hadamard matrices and the
+// activation-quantization paragraph): z = H_d (s * x) with H_d = H_{2^n} (x) H_m,
+// y = z / sqrt(d), scale = fp16(clip * max|y| / 7), q = clamp(rne(y / scale), -8, 7),
+// two codes per byte.  The exact fp32 recipe is stated in include/qr.h.
+//
+// Three kernel families:
+//  * k_hq_pow2   d = 512 .. 8192 (powers of two), one wavefront per row, no LDS
+//                traffic for data.  H_d = H_{d/32} (x) H_32: the H_32 factor runs
+//                on the matrix cores (v_mfma_f32_16x16x32_f16) directly on the
+//                fp16 input with the signs applied by flipping sign bits, which is
+//                exact (the products are +-x and the accumulation is fp32).  The
+//                remaining log2(d) - 5 butterfly stages run in fp32 VALU: 4 across
+//                lanes through DPP (one v_fmac_f32_dpp per element and stage, with
+//                a per-lane +-1 multiplier) and the rest between registers of a
+//                lane.  amax, scale, rounding and packing follow in registers; the
+//                row makes exactly one HBM round trip.
+//  * k_hq_small  d = 8 .. 256 (and the head-wise K/V path): d/8 lanes per row,
+//                three in-register stages and the rest through lane shuffles.
+//  * k_hq_lds    d = 2^n * m, m in {28, 172}, and quantization without rotation:
+//                one workgroup per row, the row staged in LDS as fp32, the dense
+//                +-1 H_m products on contiguous m-chunks followed by radix-32
+//                butterfly passes in LDS.
+#include "common.hpp"
+
+namespace qr {
+
+__constant__ HTable<28> g_h28 = make_h28();
+__constant__ HTable<172> g_h172 = make_h172();
+
+enum { MODE_QUANT = 0, MODE_ROT_F32 = 1, MODE_ROT_F16 = 2 };
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Per-row scale recipe (identical for every kernel): returns the fp16 scale
+// bits and the multiplier m = c * (1 / s_h) (0 if s_h == 0).
+__device__ __forceinline__ void sym_scale(float amax_z, float c, float clip, uint16_t* sh_out,
+                                          float* m_out) {
+  const float a = __fmul_rn(amax_z, c);
+  const float s = __fdiv_rn(__fmul_rn(clip, a), 7.0f);
+  const uint16_t sh = f2h(s);
+  const float shf = h2f(sh);
+  const float inv = shf > 0.0f ? __fdiv_rn(1.0f, shf) : 0.0f;
+  *sh_out = sh;
+  *m_out = __fmul_rn(c, inv);
+}
+
+// Eight fp32 values times m -> eight offset-binary nibbles (q + 8), packed
+// into one little-endian dword and converted to two's complement.
+template <bool CLAMP>
+__device__ __forceinline__ uint32_t quant_pack8(const float* v, float m) {
+  uint32_t f[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float t = fmaf(v[j], m, kMagic + 8.0f);  // kMagic + 8 + rne(v*m)
+    if (CLAMP) t = __builtin_amdgcn_fmed3f(t, kMagic, kMagic + 15.0f);
+    f[j] = __float_as_uint(t);
+  }
+  // low byte of each pair word: (q_odd + 8) << 4 | (q_even + 8)
+  const uint32_t p0 = (f[1] << 4) | f[0];
+  const uint32_t p1 = (f[3] << 4) | f[2];
+  const uint32_t p2 = (f[5] << 4) | f[4];
+  const uint32_t p3 = (f[7] << 4) | f[6];
+  const uint32_t lo = __builtin_amdgcn_perm(p1, p0, 0x0c0c0400u);  // [p0.b0, p1.b0, 0, 0]
+  const uint32_t hi = __builtin_amdgcn_perm(p3, p2, 0x04000c0cu);  // [0, 0, p2.b0, p3.b0]
+  return lo ^ hi ^ 0x88888888u;  // offset binary -> two's complement nibbles
+}
+
+// ===========================================================================
+// k_hq_pow2: d = NB * 512
+// ===========================================================================
+
+// Lane-in-row c (0..15) -> 32-element chunk index inside a 512-element block.
+// Linear over GF(2) with gmap(1) = 1, gmap(2) = 2, gmap(7) = 4, gmap(15) = 8, so
+// that the DPP partner patterns xor 1 (quad_perm), xor 2 (quad_perm), xor 7
+// (row_half_mirror) and xor 15 (row_mirror) each flip exactly one chunk bit.
+__device__ __forceinline__ int gmap(int c) {
+  const int c0 = c & 1, c1 = (c >> 1) & 1, c2 = (c >> 2) & 1, c3 = (c >> 3) & 1;
+  return (c0 ^ c2) | ((c1 ^ c2) << 1) | ((c2 ^ c3) << 2) | (c3 << 3);
+}
+
+// One butterfly stage across lanes for eight registers: r += dpp(r) * s.
+// The leading s_nop covers the VALU-write -> DPP-read hazard for values
+// produced just before; within the block every register is distinct.
+#define QR_DPP8(CTRL, r, s)                                                            \
+  asm volatile(                                                                        \
+      "s_nop 1\n\t"                                                                    \
+      "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"                  \
+      : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), \
+        "+v"(r[7])                                                                     \
+      : "v"(s))
+
+template <int NB, int MODE, bool CLAMP>
+__global__ __launch_bounds__(256) void k_hq_pow2(const uint16_t* __restrict__ x, int64_t T,
+                                                 int64_t ld, const int8_t* __restrict__ signs,
+                                                 float c, float clip, uint8_t* __restrict__ q,
+                                                 uint16_t* __restrict__ scale,
+                                                 float* __restrict__ zdbg,
+                                                 void* __restrict__ yout) {
+  constexpr int D = NB * 512;
+  __shared__ v4u s_mask[NB * 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cl = lane & 15, g = lane >> 4;
+  const int gc = gmap(cl);
+  const int lane_off = gc * 32 + g * 8;  // first of the lane's 8 elements in a 512-block
+
+  // Sign-bit masks for the lane's 8 fp16 values of every block (same for all rows).
+  for (int i = tid; i < NB * 64; i += 256) {
+    const int b = i >> 6, ln = i & 63;
+    const int e = b * 512 + gmap(ln & 15) * 32 + (ln >> 4) * 8;
+    v4u m = {0u, 0u, 0u, 0u};
+    if (signs) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        m[j] = (signs[e + 2 * j] < 0 ? 0x8000u : 0u) | (signs[e + 2 * j + 1] < 0 ? 0x80000000u : 0u);
+    }
+    s_mask[i] = m;
+  }
+  __syncthreads();
+
+  // A operands: rows of H_32 permuted so that MFMA m, row i produces output
+  // element o = 8 (i >> 2) + 4 m + (i & 3) of the chunk; with the 16x16 output
+  // layout (lane = n + 16 (i >> 2), register i & 3) each lane then holds the
+  // 8 consecutive outputs at the same offsets it loaded.
+  v8h a0, a1;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k = 8 * g + j;
+    const int o0 = 8 * (cl >> 2) + (cl & 3);
+    const int o1 = o0 + 4;
+    a0[j] = (__builtin_popcount(o0 & k) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
+    a1[j] = (__builtin_popcount(o1 & k) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
+  }
+  // DPP stage multipliers: +1 on the lane holding the lower chunk of the pair.
+  const float s0 = (gc & 1) ? -1.0f : 1.0f;
+  const float s1 = (gc & 2) ? -1.0f : 1.0f;
+  const float s2 = (gc & 4) ? -1.0f : 1.0f;
+  const float s3 = (gc & 8) ? -1.0f : 1.0f;
+  // After the four DPP stages the lane holds sigma * z.
+  const float sigma = (__builtin_popcount(gc) & 1) ? -1.0f : 1.0f;
+
+  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < T; row += (int64_t)gridDim.x * 4) {
+    const uint16_t* xr = x + row * ld + lane_off;
+    v4u raw[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) raw[b] = *(const v4u*)(xr + b * 512);
+
+    float w[NB][8];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const v4u v = raw[b] ^ s_mask[b * 64 + lane];
+      const v8h bop = __builtin_bit_cast(v8h, v);
+      const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      const v4f r0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bop, zero, 0, 0, 0);
+      const v4f r1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bop, zero, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w[b][j] = r0[j];
+        w[b][4 + j] = r1[j];
+      }
+    }
+    // Butterflies over the block index (element bits 9 ..), inside the lane.
+#pragma unroll
+    for (int h = 1; h < NB; h <<= 1)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (!(b & h))
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float u = w[b][j], v = w[b + h][j];
+            w[b][j] = u + v;
+            w[b + h][j] = u - v;
+          }
+    if (NB == 1) {
+      // keep a compiler-visible VALU op between the MFMA results and the DPP asm
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[0][j] = __fadd_rn(w[0][j], 0.0f);
+    }
+    // Butterflies over the chunk index (element bits 5..8), across lanes.
+#pragma unroll
+    for (int b = 0; b < NB; ++b) QR_DPP8("quad_perm:[1,0,3,2]", w[b], s0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) QR_DPP8("quad_perm:[2,3,0,1]", w[b], s1);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) QR_DPP8("row_half_mirror", w[b], s2);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) QR_DPP8("row_mirror", w[b], s3);
+
+    if (zdbg) {
+      float* zr = zdbg + row * D + lane_off;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        v4f lo = {w[b][0] * sigma, w[b][1] * sigma, w[b][2] * sigma, w[b][3] * sigma};
+        v4f hi = {w[b][4] * sigma, w[b][5] * sigma, w[b][6] * sigma, w[b][7] * sigma};
+        *(v4f*)(zr + b * 512) = lo;
+        *(v4f*)(zr + b * 512 + 4) = hi;
+      }
+    }
+
+    if (MODE == MODE_QUANT) {
+      float am = 0.0f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(w[b][j]));
+      am = wave_max(am);
+      uint16_t sh;
+      float m;
+      sym_scale(am, c, clip, &sh, &m);
+      const float ml = m * sigma;  // w * ml = z * m exactly
+      uint8_t* qr = q + row * (D / 2) + lane_off / 2;
+      // Without clipping |z m| <= 7 (1 + 2^-10) < 7.5 whenever s_h is a normal
+      // fp16, so the clamp can be skipped; a subnormal s_h carries a larger
+      // relative rounding error and takes the clamped path (wave-uniform branch).
+      if (CLAMP || (sh & 0x7fffu) < 0x0400u) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) *(uint32_t*)(qr + b * 256) = quant_pack8<true>(w[b], ml);
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) *(uint32_t*)(qr + b * 256) = quant_pack8<false>(w[b], ml);
+      }
+      if (lane == 0) scale[row] = sh;
+    } else {
+      const float cs = c * sigma;
+      if (MODE == MODE_ROT_F32) {
+        float* yr = (float*)yout + row * D + lane_off;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          v4f lo = {__fmul_rn(w[b][0], cs), __fmul_rn(w[b][1], cs), __fmul_rn(w[b][2], cs),
+                    __fmul_rn(w[b][3], cs)};
+          v4f hi = {__fmul_rn(w[b][4], cs), __fmul_rn(w[b][5], cs), __fmul_rn(w[b][6], cs),
+                    __fmul_rn(w[b][7], cs)};
+          *(v4f*)(yr + b * 512) = lo;
+          *(v4f*)(yr + b * 512 + 4) = hi;
+        }
+      } else {
+        uint16_t* yr = (uint16_t*)yout + row * D + lane_off;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          v4u o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            o[j] = (uint32_t)f2h(__fmul_rn(w[b][2 * j], cs)) |
+                   ((uint32_t)f2h(__fmul_rn(w[b][2 * j + 1], cs)) << 16);
+          *(v4u*)(yr + b * 512) = o;
+        }
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// k_hq_small: d = 8 .. 256 (powers of two), d/8 lanes per row
+// ===========================================================================
+template <int LPR, int MODE, bool CLAMP>
+__global__ __launch_bounds__(256) void k_hq_small(const uint16_t* __restrict__ x, int64_t T,
+                                                  int64_t ld, const int8_t* __restrict__ signs,
+                                                  int rot, float c, float clip,
+                                                  uint8_t* __restrict__ q,
+                                                  uint16_t* __restrict__ scale,
+                                                  float* __restrict__ zdbg,
+                                                  void* __restrict__ yout) {
+  constexpr int D = LPR * 8;
+  constexpr int RPW = 64 / LPR;  // rows per wavefront
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int sub = lane % LPR;  // lane within the row
+  const int rw = lane / LPR;   // row within the wavefront
+  float sg[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sg[j] = (rot && signs && signs[sub * 8 + j] < 0) ? -1.0f : 1.0f;
+
+  for (int64_t base = ((int64_t)blockIdx.x * 4 + wave) * RPW; base < T;
+       base += (int64_t)gridDim.x * 4 * RPW) {
+    const int64_t row = base + rw;
+    const bool valid = row < T;
+    float v[8];
+    if (valid) {
+      const v4u raw = *(const v4u*)(x + row * ld + sub * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = h2f((uint16_t)(raw[j] & 0xffffu)) * sg[2 * j];
+        v[2 * j + 1] = h2f((uint16_t)(raw[j] >> 16)) * sg[2 * j + 1];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+    if (rot) {
+#pragma unroll
+      for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (!(j & h)) {
+            const float a = v[j], b = v[j + h];
+            v[j] = a + b;
+            v[j + h] = a - b;
+          }
+#pragma unroll
+      for (int h = 1; h < LPR; h <<= 1) {
+        const float s = (sub & h) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = __shfl_xor(v[j], h);
+          v[j] = fmaf(v[j], s, p);  // low lane: mine + partner; high lane: partner - mine
+        }
+      }
+    }
+    if (valid && zdbg) {
+      float* zr = zdbg + row * D + sub * 8;
+      *(v4f*)zr = v4f{v[0], v[1], v[2], v[3]};
+      *(v4f*)(zr + 4) = v4f{v[4], v[5], v[6], v[7]};
+    }
+    if (MODE == MODE_QUANT) {
+      float am = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
+#pragma unroll
+      for (int h = 1; h < LPR; h <<= 1) am = fmaxf(am, __shfl_xor(am, h));
+      uint16_t sh;
+      float m;
+      sym_scale(am, c, clip, &sh, &m);
+      if (valid) {
+        *(uint32_t*)(q + row * (D / 2) + sub * 4) = (CLAMP || (sh & 0x7fffu) < 0x0400u)
+                                                        ? quant_pack8<true>(v, m)
+                                                        : quant_pack8<false>(v, m);
+        if (sub == 0) scale[row] = sh;
+      }
+    } else if (valid) {
+      if (MODE == MODE_ROT_F32) {
+        float* yr = (float*)yout + row * D + sub * 8;
+        *(v4f*)yr = v4f{__fmul_rn(v[0], c), __fmul_rn(v[1], c), __fmul_rn(v[2], c),
+                        __fmul_rn(v[3], c)};
+        *(v4f*)(yr + 4) = v4f{__fmul_rn(v[4], c), __fmul_rn(v[5], c), __fmul_rn(v[6], c),
+                              __fmul_rn(v[7], c)};
+      } else {
+        v4u o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[j] = (uint32_t)f2h(__fmul_rn(v[2 * j], c)) |
+                 ((uint32_t)f2h(__fmul_rn(v[2 * j + 1], c)) << 16);
+        *(v4u*)((uint16_t*)yout + row * D + sub * 8) = o;
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// k_hq_lds: d = 2^n * M (M in {28, 172}), or quantization without rotation
+// ===========================================================================
+__device__ __forceinline__ int pad(int e) { return e + (e >> 5); }
+
+// R in-register butterfly stages on 2^R values at LDS stride `stride`.
+template <int R, int M>
+__device__ __forceinline__ void lds_pass(float* buf, int d, int b0, int tid) {
+  constexpr int G = 1 << R;
+  const int groups = d >> R;
+  const int stride = M << b0;
+  for (int gi = tid; gi < groups; gi += 256) {
+    const int mi = gi % M;
+    const int rest = gi / M;
+    const int alow = rest & ((1 << b0) - 1);
+    const int ahigh = rest >> b0;
+    const int base = ((ahigh << (b0 + R)) | alow) * M + mi;
+    float v[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) v[j] = buf[pad(base + j * stride)];
+#pragma unroll
+    for (int h = 1; h < G; h <<= 1)
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        if (!(j & h)) {
+          const float a = v[j], b = v[j + h];
+          v[j] = a + b;
+          v[j + h] = a - b;
+        }
+#pragma unroll
+    for (int j = 0; j < G; ++j) buf[pad(base + j * stride)] = v[j];
+  }
+}
+
+// Dense +-1 product of one MB-block of H_M with one MB-block of a chunk:
+// acc[o] += H[ob*MB + o][ib*MB + k] * xin[k].  H comes from constant memory
+// with wave-uniform indices (scalar loads).
+template <int M, int MB>
+__device__ __forceinline__ void hm_block(const float* __restrict__ H, int ob, int ib,
+                                         const float* xin, float* acc) {
+#pragma unroll
+  for (int o = 0; o < MB; ++o) {
+    const float* hr = H + (ob * MB + o) * M + ib * MB;
+#pragma unroll
+    for (int k = 0; k < MB; ++k) acc[o] = fmaf(hr[k], xin[k], acc[o]);
+  }
+}
+
+template <int M, int MODE, bool CLAMP, bool ROT>
+__global__ __launch_bounds__(256) void k_hq_lds(const uint16_t* __restrict__ x, int64_t T, int d,
+                                                int n, int64_t ld,
+                                                const int8_t* __restrict__ signs, float c,
+                                                float clip, uint8_t* __restrict__ q,
+                                                uint16_t* __restrict__ scale,
+                                                float* __restrict__ zdbg,
+                                                void* __restrict__ yout) {
+  extern __shared__ float smem[];
+  constexpr int NOB = (M == 172) ? 4 : 1;  // output blocks per chunk
+  constexpr int MB = M / NOB;
+  constexpr bool DOUBLE = (M == 172);  // H_172 writes into a second buffer
+  const int tid = threadIdx.x;
+  const int plen = pad(d) + 1;
+  float* buf0 = smem;
+  float* buf1 = DOUBLE ? smem + plen : smem;
+  float* red = smem + (DOUBLE ? 2 : 1) * plen;  // 8 floats of reduction scratch
+  const float* H = (M == 28) ? &g_h28.v[0][0] : (M == 172 ? &g_h172.v[0][0] : nullptr);
+
+  for (int64_t row = blockIdx.x; row < T; row += gridDim.x) {
+    // 1. fp16 -> fp32 (signs applied) into LDS
+    for (int i = tid * 8; i < d; i += 256 * 8) {
+      const v4u raw = *(const v4u*)(x + row * ld + i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float f = h2f((uint16_t)((raw[j >> 1] >> (16 * (j & 1))) & 0xffffu));
+        if (ROT && signs && signs[i + j] < 0) f = -f;
+        buf0[pad(i + j)] = f;
+      }
+    }
+    __syncthreads();
+    float* buf = buf0;
+    if (ROT) {
+      // 2. H_M on every contiguous M-chunk
+      if (M > 1) {
+        const int chunks = d / M;
+        constexpr int CPR = 256 / NOB;  // chunks per round (all NOB blocks of a chunk together)
+        const int ob = __builtin_amdgcn_readfirstlane(tid / CPR);
+        for (int c0 = 0; c0 < chunks; c0 += CPR) {
+          const int ch = c0 + tid % CPR;
+          const bool active = ch < chunks;
+          float acc[MB];
+#pragma unroll
+          for (int o = 0; o < MB; ++o) acc[o] = 0.0f;
+          if (active) {
+#pragma unroll
+            for (int ib = 0; ib < NOB; ++ib) {
+              float xin[MB];
+#pragma unroll
+              for (int k = 0; k < MB; ++k) xin[k] = buf0[pad(ch * M + ib * MB + k)];
+              hm_block<M, MB>(H, ob, ib, xin, acc);
+            }
+          }
+          if (!DOUBLE) __syncthreads();
+          if (active) {
+#pragma unroll
+            for (int o = 0; o < MB; ++o) buf1[pad(ch * M + ob * MB + o)] = acc[o];
+          }
+          if (!DOUBLE) __syncthreads();
+        }
+        if (DOUBLE) __syncthreads();
+        buf = buf1;
+      }
+      // 3. butterflies over the 2^n index (stride M), five stages per LDS pass
+      for (int b0 = 0; b0 < n; b0 += 5) {
+        const int r = min(5, n - b0);
+        switch (r) {
+          case 1: lds_pass<1, M>(buf, d, b0, tid); break;
+          case 2: lds_pass<2, M>(buf, d, b0, tid); break;
+          case 3: lds_pass<3, M>(buf, d, b0, tid); break;
+          case 4: lds_pass<4, M>(buf, d, b0, tid); break;
+          default: lds_pass<5, M>(buf, d, b0, tid); break;
+        }
+        __syncthreads();
+      }
+    }
+    if (zdbg) {
+      for (int i = tid; i < d; i += 256) zdbg[row * d + i] = buf[pad(i)];
+    }
+    if (MODE == MODE_QUANT) {
+      // 4. amax over the row
+      float am = 0.0f;
+      for (int i = tid; i < d; i += 256) am = fmaxf(am, fabsf(buf[pad(i)]));
+      am = wave_max(am);
+      if ((tid & 63) == 0) red[tid >> 6] = am;
+      __syncthreads();
+      am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      uint16_t sh;
+      float m;
+      sym_scale(am, c, clip, &sh, &m);
+      // 5. quantize + pack, 8 elements per thread and step
+      const bool clamp = CLAMP || (sh & 0x7fffu) < 0x0400u;  // block-uniform
+      for (int i = tid * 8; i < d; i += 256 * 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = buf[pad(i + j)];
+        *(uint32_t*)(q + row * (d / 2) + i / 2) =
+            clamp ? quant_pack8<true>(v, m) : quant_pack8<false>(v, m);
+      }
+      if (tid == 0) scale[row] = sh;
+    } else if (MODE == MODE_ROT_F32) {
+      for (int i = tid; i < d; i += 256) ((float*)yout)[row * d + i] = __fmul_rn(buf[pad(i)], c);
+    } else {
+      for (int i = tid; i < d; i += 256)
+        ((uint16_t*)yout)[row * d + i] = f2h(__fmul_rn(buf[pad(i)], c));
+    }
+    __syncthreads();  // the LDS row is reused by the next iteration
+  }
+}
+
+// ===========================================================================
+// Host side
+// ===========================================================================
+static int grid_for(int64_t work_items, int per_block, int cap) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+template <int MODE, bool CLAMP>
+static qr_status launch_pow2(int nb, const uint16_t* x, int64_t T, int64_t ld, const int8_t* s,
+                             float c, float clip, uint8_t* q, uint16_t* sc, float* z, void* y,
+                             hipStream_t st) {
+  const int grid = grid_for(T, 4, 2048);
+  switch (nb) {
+#define QR_CASE(NBV)                                                                   \
+  case NBV:                                                                            \
+    hipLaunchKernelGGL((k_hq_pow2<NBV, MODE, CLAMP>), dim3(grid), dim3(256), 0, st, x, T, ld, s, \
+                       c, clip, q, sc, z, y);                                          \
+    break;
+    QR_CASE(1)
+    QR_CASE(2)
+    QR_CASE(4)
+    QR_CASE(8)
+    QR_CASE(16)
+#undef QR_CASE
+    default:
+      return QR_ERR_UNSUPPORTED;
+  }
+  return launch_status();
+}
+
+template <int MODE, bool CLAMP>
+static qr_status launch_small(int d, int rot, const uint16_t* x, int64_t T, int64_t ld,
+                              const int8_t* s, float c, float clip, uint8_t* q, uint16_t* sc,
+                              float* z, void* y, hipStream_t st) {
+  const int lpr = d / 8;
+  const int rows_per_block = 4 * (64 / lpr);
+  const int grid = grid_for(T, rows_per_block, 4096);
+  switch (lpr) {
+#define QR_CASE(L)                                                                     \
+  case L:                                                                              \
+    hipLaunchKernelGGL((k_hq_small<L, MODE, CLAMP>), dim3(grid), dim3(256), 0, st, x, T, ld, s, \
+                       rot, c, clip, q, sc, z, y);                                     \
+    break;
+    QR_CASE(1)
+    QR_CASE(2)
+    QR_CASE(4)
+    QR_CASE(8)
+    QR_CASE(16)
+    QR_CASE(32)
+#undef QR_CASE
+    default:
+      return QR_ERR_UNSUPPORTED;
+  }
+  return launch_status();
+}
+
+template <int M, int MODE, bool CLAMP, bool ROT>
+static qr_status launch_lds_t(int d, int n, const uint16_t* x, int64_t T, int64_t ld,
+                              const int8_t* s, float c, float clip, uint8_t* q, uint16_t* sc,
+                              float* z, void* y, hipStream_t st) {
+  const int plen = (d + (d >> 5)) + 1;
+  const size_t bytes = ((size_t)((M == 172 && ROT) ? 2 : 1) * plen + 8) * sizeof(float);
+  if (bytes > 160 * 1024) return QR_ERR_UNSUPPORTED;
+  auto kern = k_hq_lds<M, MODE, CLAMP, ROT>;
+  if (bytes > 64 * 1024 &&
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)bytes) != hipSuccess)
+    return QR_ERR_LAUNCH;
+  const int grid = grid_for(T, 1, 2048);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), bytes, st, x, T, d, n, ld, s, c, clip, q, sc, z,
+                     y);
+  return launch_status();
+}
+
+template <int MODE, bool CLAMP>
+static qr_status dispatch(const void* x_f16, int64_t T, int32_t d, int64_t ld, int rot,
+                          const int8_t* signs, float clip, void* q, void* sc, float* z, void* y,
+                          hipStream_t st) {
+  const uint16_t* x = (const uint16_t*)x_f16;
+  uint8_t* qq = (uint8_t*)q;
+  uint16_t* ss = (uint16_t*)sc;
+  if (!rot)
+    return launch_lds_t<1, MODE, CLAMP, false>(d, 0, x, T, ld, signs, 1.0f, clip, qq, ss, z, y, st);
+  int n = 0, m = 0;
+  if (!factor_width(d, &n, &m)) return QR_ERR_UNSUPPORTED;
+  const float c = norm_constant(d);
+  if (m == 1) {
+    if (d >= 512)
+      return launch_pow2<MODE, CLAMP>(d / 512, x, T, ld, signs, c, clip, qq, ss, z, y, st);
+    return launch_small<MODE, CLAMP>(d, 1, x, T, ld, signs, c, clip, qq, ss, z, y, st);
+  }
+  if (m == 28)
+    return launch_lds_t<28, MODE, CLAMP, true>(d, n, x, T, ld, signs, c, clip, qq, ss, z, y, st);
+  return launch_lds_t<172, MODE, CLAMP, true>(d, n, x, T, ld, signs, c, clip, qq, ss, z, y, st);
+}
+
+}  // namespace qr
+
+using namespace qr;
+
+extern "C" qr_status qr_hadamard_quant(const void* x_f16, int64_t T, int32_t d, int64_t ld_x,
+                                       qr_rot rot, const int8_t* signs, float clip_ratio,
+                                       void* q_u8, void* scale_f16, float* z_dbg,
+                                       hipStream_t stream) {
+  if (T < 0 || d <= 0 || ld_x < d) return QR_ERR_SHAPE;
+  if (rot != QR_ROT_NONE && rot != QR_ROT_HADAMARD) return QR_ERR_ARG;
+  if (!valid_clip(clip_ratio)) return QR_ERR_ARG;
+  int n = 0, m = 0;
+  if (rot == QR_ROT_HADAMARD) {
+    if (!factor_width(d, &n, &m)) return QR_ERR_UNSUPPORTED;
+  } else if (d % 8 != 0 || d > 32768) {
+    return QR_ERR_UNSUPPORTED;
+  }
+  if (T == 0) return QR_OK;
+  if (!x_f16 || !q_u8 || !scale_f16) return QR_ERR_NULL;
+  if (ld_x % 8 != 0 || !aligned(x_f16, 16) || !aligned(q_u8, 4) || !aligned(scale_f16, 2) ||
+      (z_dbg && !aligned(z_dbg, 16)))
+    return QR_ERR_ALIGN;
+  const int r = rot == QR_ROT_HADAMARD ? 1 : 0;
+  if (clip_ratio < 1.0f)
+    return dispatch<MODE_QUANT, true>(x_f16, T, d, ld_x, r, signs, clip_ratio, q_u8, scale_f16,
+                                      z_dbg, nullptr, stream);
+  return dispatch<MODE_QUANT, false>(x_f16, T, d, ld_x, r, signs, clip_ratio, q_u8, scale_f16,
+                                     z_dbg, nullptr, stream);
+}
+
+extern "C" qr_status qr_hadamard(const void* x_f16, int64_t T, int32_t d, int64_t ld_x,
+                                 const int8_t* signs, void* y, int32_t y_is_f32,
+                                 hipStream_t stream) {
+  if (T < 0 || d <= 0 || ld_x < d) return QR_ERR_SHAPE;
+  int n = 0, m = 0;
+  if (!factor_width(d, &n, &m)) return QR_ERR_UNSUPPORTED;
+  if (T == 0) return QR_OK;
+  if (!x_f16 || !y) return QR_ERR_NULL;
+  if (ld_x % 8 != 0 || !aligned(x_f16, 16) || !aligned(y, 16)) return QR_ERR_ALIGN;
+  if (y_is_f32)
+    return dispatch<MODE_ROT_F32, false>(x_f16, T, d, ld_x, 1, signs, 1.0f, nullptr, nullptr,
+                                         nullptr, y, stream);
+  return dispatch<MODE_ROT_F16, false>(x_f16, T, d, ld_x, 1, signs, 1.0f, nullptr, nullptr,
+                                       nullptr, y, stream);
+}

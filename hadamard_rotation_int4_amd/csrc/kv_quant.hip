@@ -1,0 +1,191 @@
+// Head-wise Hadamard rotation of new K (or V) tokens fused with asymmetric
+// 4-bit group quantization, written straight into the packed KV cache
+// (qr_kv_rotate_quant), for gfx950.
+//
+// QuaRot paper: keys (and queries) get an online head-wise Hadamard after the
+// positional embedding so q.k is unchanged (keys/queries paragraph, post-RoPE
+// caching); the cache is quantized asymmetrically in groups of 128 with a
+// clipping ratio of 0.95 (implementation paragraph; Table 6); Init fills the
+// cache from the prompt and Append quantizes one new token per decode step
+// (attention-routines paragraph).  The exact fp32 recipe is in include/qr.h.
+//
+// Layout: one (token, head) row of Dh elements is spread over Dh/8 lanes, each
+// lane loading 8 contiguous fp16 (16 bytes).  Three butterfly stages run inside
+// the lane, log2(Dh/8) across lanes.  Group min/max reduce over the G/8 lanes
+// of a group; each lane then writes one dword of codes and the first lane of a
+// group writes its (scale, min) pair.  The kernel is HBM-bound: per element it
+// reads 2 bytes and writes 0.5 byte plus 4 bytes of metadata per group.
+#include "common.hpp"
+
+namespace qr {
+
+template <int LPR, bool ROT>
+__global__ __launch_bounds__(256) void k_kv_quant(
+    const uint16_t* __restrict__ x, int64_t rows, int S_new, int H, int64_t ld_token,
+    const int8_t* __restrict__ signs, int group, float c, float clip, uint8_t* __restrict__ cq,
+    uint16_t* __restrict__ meta, int S_max, int start_pos, float* __restrict__ zdbg) {
+  constexpr int DH = LPR * 8;
+  constexpr int RPW = 64 / LPR;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int sub = lane % LPR;
+  const int rw = lane / LPR;
+  const int lpg = group / 8;  // lanes per group
+  const int ngroups = DH / group;
+  float sg[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sg[j] = (ROT && signs && signs[sub * 8 + j] < 0) ? -1.0f : 1.0f;
+
+  for (int64_t base = ((int64_t)blockIdx.x * 4 + wave) * RPW; base < rows;
+       base += (int64_t)gridDim.x * 4 * RPW) {
+    const int64_t row = base + rw;  // row = (b * S_new + s) * H + h
+    const bool valid = row < rows;
+    const int64_t tok = row / H;
+    const int h = (int)(row - tok * H);
+    float v[8];
+    if (valid) {
+      const v4u raw = *(const v4u*)(x + tok * ld_token + (int64_t)h * DH + sub * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = h2f((uint16_t)(raw[j] & 0xffffu)) * sg[2 * j];
+        v[2 * j + 1] = h2f((uint16_t)(raw[j] >> 16)) * sg[2 * j + 1];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+    if (ROT) {
+#pragma unroll
+      for (int hh = 1; hh < 8; hh <<= 1)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (!(j & hh)) {
+            const float a = v[j], b = v[j + hh];
+            v[j] = a + b;
+            v[j + hh] = a - b;
+          }
+#pragma unroll
+      for (int hh = 1; hh < LPR; hh <<= 1) {
+        const float s = (sub & hh) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = __shfl_xor(v[j], hh);
+          v[j] = fmaf(v[j], s, p);
+        }
+      }
+    }
+    if (valid && zdbg) {
+      float* zr = zdbg + row * DH + sub * 8;
+      *(v4f*)zr = v4f{v[0], v[1], v[2], v[3]};
+      *(v4f*)(zr + 4) = v4f{v[4], v[5], v[6], v[7]};
+    }
+    // y = fp32(z * c)
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = ROT ? __fmul_rn(v[j], c) : v[j];
+    float mx = y[0], mn = y[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      mx = fmaxf(mx, y[j]);
+      mn = fminf(mn, y[j]);
+    }
+    for (int hh = 1; hh < lpg; hh <<= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, hh));
+      mn = fminf(mn, __shfl_xor(mn, hh));
+    }
+    const float mxc = __fmul_rn(clip, mx);
+    const float mnc = __fmul_rn(clip, mn);
+    const uint16_t sh = f2h(__fdiv_rn(__fsub_rn(mxc, mnc), 15.0f));
+    const uint16_t mh = f2h(mnc);
+    const float shf = h2f(sh);
+    const float mhf = h2f(mh);
+    const float inv = shf > 0.0f ? __fdiv_rn(1.0f, shf) : 0.0f;
+    uint32_t f[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // kMagic + rne((y - m_h) * inv), clamped to [0, 15].  The clamp is needed
+      // even without clipping: m_h is mn rounded to fp16 and s_h is rounded too.
+      float t = fmaf(__fsub_rn(y[j], mhf), inv, kMagic);
+      t = __builtin_amdgcn_fmed3f(t, kMagic, kMagic + 15.0f);
+      f[j] = __float_as_uint(t);
+    }
+    const uint32_t p0 = (f[1] << 4) | (f[0] & 0xfu);
+    const uint32_t p1 = (f[3] << 4) | (f[2] & 0xfu);
+    const uint32_t p2 = (f[5] << 4) | (f[4] & 0xfu);
+    const uint32_t p3 = (f[7] << 4) | (f[6] & 0xfu);
+    const uint32_t word = __builtin_amdgcn_perm(p1, p0, 0x0c0c0400u) |
+                          __builtin_amdgcn_perm(p3, p2, 0x04000c0cu);
+    if (valid) {
+      const int64_t b = tok / S_new;
+      const int s = (int)(tok - b * S_new);
+      const int64_t crow = (b * H + h) * (int64_t)S_max + start_pos + s;
+      *(uint32_t*)(cq + crow * (DH / 2) + sub * 4) = word;
+      if ((sub % lpg) == 0) {
+        const int gi = sub / lpg;
+        *(uint32_t*)(meta + (crow * ngroups + gi) * 2) = (uint32_t)sh | ((uint32_t)mh << 16);
+      }
+    }
+  }
+}
+
+template <bool ROT>
+static qr_status launch_kv(int dh, const uint16_t* x, int64_t rows, int S_new, int H,
+                           int64_t ld_token, const int8_t* signs, int group, float c, float clip,
+                           uint8_t* cq, uint16_t* meta, int S_max, int start_pos, float* zdbg,
+                           hipStream_t st) {
+  const int lpr = dh / 8;
+  const int64_t rows_per_block = 4 * (64 / lpr);
+  int64_t grid = (rows + rows_per_block - 1) / rows_per_block;
+  if (grid > 8192) grid = 8192;
+  switch (lpr) {
+#define QR_CASE(L)                                                                              \
+  case L:                                                                                       \
+    hipLaunchKernelGGL((k_kv_quant<L, ROT>), dim3((int)grid), dim3(256), 0, st, x, rows, \
+                       S_new, H, ld_token, signs, group, c, clip, cq, meta, S_max, start_pos,   \
+                       zdbg);                                                                   \
+    break;
+    QR_CASE(1)
+    QR_CASE(2)
+    QR_CASE(4)
+    QR_CASE(8)
+    QR_CASE(16)
+    QR_CASE(32)
+#undef QR_CASE
+    default:
+      return QR_ERR_UNSUPPORTED;
+  }
+  return launch_status();
+}
+
+}  // namespace qr
+
+using namespace qr;
+
+extern "C" qr_status qr_kv_rotate_quant(const void* kv_f16, int32_t B, int32_t S_new, int32_t H,
+                                        int32_t Dh, int64_t ld_token, qr_rot rot,
+                                        const int8_t* signs, int32_t group, float clip_ratio,
+                                        void* cache_q, void* cache_meta, int32_t S_max,
+                                        int32_t start_pos, float* z_dbg, hipStream_t stream) {
+  if (B < 1 || H < 1 || S_new < 0 || S_max < 0 || start_pos < 0) return QR_ERR_SHAPE;
+  if ((int64_t)start_pos + S_new > S_max) return QR_ERR_SHAPE;
+  if (Dh < 8 || Dh > 256 || (Dh & (Dh - 1))) return QR_ERR_UNSUPPORTED;
+  if (group < 8 || group > Dh || Dh % group != 0 || (group & (group - 1))) return QR_ERR_UNSUPPORTED;
+  if (ld_token < (int64_t)H * Dh) return QR_ERR_SHAPE;
+  if (rot != QR_ROT_NONE && rot != QR_ROT_HADAMARD) return QR_ERR_ARG;
+  if (!valid_clip(clip_ratio)) return QR_ERR_ARG;
+  if (S_new == 0) return QR_OK;
+  if (!kv_f16 || !cache_q || !cache_meta) return QR_ERR_NULL;
+  if (ld_token % 8 != 0 || !aligned(kv_f16, 16) || !aligned(cache_q, 4) ||
+      !aligned(cache_meta, 4) || (z_dbg && !aligned(z_dbg, 16)))
+    return QR_ERR_ALIGN;
+  const int64_t rows = (int64_t)B * S_new * H;
+  const uint16_t* x = (const uint16_t*)kv_f16;
+  uint8_t* cq = (uint8_t*)cache_q;
+  uint16_t* meta = (uint16_t*)cache_meta;
+  if (rot == QR_ROT_HADAMARD)
+    return launch_kv<true>(Dh, x, rows, S_new, H, ld_token, signs, group, norm_constant(Dh),
+                           clip_ratio, cq, meta, S_max, start_pos, z_dbg, stream);
+  return launch_kv<false>(Dh, x, rows, S_new, H, ld_token, signs, group, 1.0f, clip_ratio, cq,
+                          meta, S_max, start_pos, z_dbg, stream);
+}

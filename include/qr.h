@@ -1,0 +1,172 @@
+/*
+ * qr.h - C ABI of libquarot_hip.so: QuaRot's online Hadamard rotation fused
+ * with INT4 quantization, the W4A4 GEMM, and the head-wise K/V rotation with
+ * 4-bit cache quantization, as HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (QuaRot: Outlier-Free 4-Bit Inference in Rotated
+ * LLMs, arXiv 2404.00456; "QuaRot paper" below is its text, "QuaRot blog" is
+ * "QuaRot: Rotating Away the Outliers That Make 4-Bit LLMs Impossible"):
+ *   - randomized Hadamard H diag(s), Kronecker H_{2^n} (x) H_m for widths that
+ *     are not powers of two: QuaRot paper, background on Hadamard matrices;
+ *   - online Hadamard before the down projection, in fp32: QuaRot paper, FFN
+ *     paragraph and the FP16-vs-FP32 Hadamard study (Table 10);
+ *   - per-token symmetric INT4 (scale = max|x| / 7, round to nearest) and the
+ *     INT32-accumulating 4-bit GEMM with row x column scale dequantization:
+ *     QuaRot paper, activation-quantization and performance paragraphs;
+ *   - post-RoPE head-wise rotation of queries and keys, asymmetric group-128
+ *     KV quantization with Init/Append routines: QuaRot paper, keys/queries
+ *     paragraph, implementation paragraph, attention-routines paragraph.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronizes; it launches on `stream` and
+ *     returns.  Results are ready when the stream reaches that point.
+ *   - Arguments are validated on the host before any launch; on error nothing
+ *     is launched and the status says why.  Empty work (T == 0, N == 0,
+ *     S_new == 0) returns QR_OK without launching.  A kernel fault surfaces at
+ *     the caller's next synchronization, not here.
+ *   - Packed INT4: byte j of a row holds element 2j in its low nibble and
+ *     element 2j+1 in its high nibble.  Symmetric codes are two's-complement
+ *     nibbles in [-8, 7]; asymmetric (KV) codes are unsigned nibbles in [0, 15].
+ *   - fp16 is IEEE binary16, fp32 is IEEE binary32; all rounding is
+ *     round-half-to-even.  Entry points are thread-safe (no global state is
+ *     written).
+ *   - Supported rotation widths d: 2^n for 3 <= n <= 13, 2^n * 28 for
+ *     1 <= n <= 10 and 2^n * 172 for 1 <= n <= 6 (H_28: Paley's second construction over
+ *     GF(13); H_172: Williamson's construction of order 4 * 43).  Use
+ *     qr_hadamard_factor() to query.
+ */
+#ifndef QR_H_
+#define QR_H_
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QR_ABI_VERSION 1
+
+typedef enum {
+  QR_OK = 0,
+  QR_ERR_NULL = 1,        /* a required pointer is NULL */
+  QR_ERR_SHAPE = 2,       /* negative size, inconsistent sizes, out-of-range position */
+  QR_ERR_UNSUPPORTED = 3, /* width/group/head size the kernels do not implement */
+  QR_ERR_ALIGN = 4,       /* pointer or stride not aligned as required */
+  QR_ERR_LAUNCH = 5,      /* the kernel launch itself failed */
+  QR_ERR_ARG = 6          /* a scalar argument is out of range (clip ratio, enum) */
+} qr_status;
+
+typedef enum {
+  QR_ROT_NONE = 0,     /* quantize only */
+  QR_ROT_HADAMARD = 1  /* rotate by H_d diag(s) / sqrt(d), then quantize */
+} qr_rot;
+
+/* Library ABI version (QR_ABI_VERSION of the build). */
+int qr_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* qr_status_str(int status);
+
+/* Host-only query: d = 2^(*log2_pow2) * (*m) as the kernels factor it.
+ * Returns QR_ERR_UNSUPPORTED (outputs untouched) if d is not a supported
+ * width; QR_ERR_NULL if an output pointer is NULL. */
+qr_status qr_hadamard_factor(int32_t d, int32_t* log2_pow2, int32_t* m);
+
+/*
+ * Fused online Hadamard rotation + per-token symmetric INT4 quantization.
+ *
+ *   x_f16      [T, ld_x] fp16, row t holds x_t in its first d entries.
+ *   rot        QR_ROT_HADAMARD: z = H_d (s * x) in fp32, y = z / sqrt(d);
+ *              QR_ROT_NONE: y = z = x.
+ *   signs      [d] int8, each +1 or -1 (the randomized Hadamard's s), or NULL
+ *              for all +1.  Ignored when rot == QR_ROT_NONE.
+ *   clip_ratio in [1/1024, 1].  Per row: a = max_i |y_i|,
+ *              scale = fp16(clip_ratio * a / 7), q_i = clamp(rne(y_i / scale), -8, 7),
+ *              q = 0 when scale == 0 (an overflowing scale is +Inf and gives q = 0).
+ *   q_u8       [T, d/2] packed codes (output, row-major, contiguous).
+ *   scale_f16  [T] fp16 scales (output).
+ *   z_dbg      NULL, or [T, d] fp32 (output): the transform output z before the
+ *              1/sqrt(d) factor (x itself for QR_ROT_NONE).
+ *
+ * The exact fp32 recipe the kernel implements, per row (c = the fp32 nearest
+ * to 1/sqrt(d), or 1 for QR_ROT_NONE; every step rounds to fp32):
+ *   a_z = max|z|; a = a_z * c; s_h = fp16(fp32(clip * a) / 7);
+ *   m = c * (1 / s_h)  (m = 0 if s_h == 0);
+ *   q_i = clamp(round_half_even(exact z_i * m), -8, 7).
+ * The order of the fp32 additions inside z is not specified.
+ *
+ * Requirements: T >= 0; d supported; ld_x >= d and ld_x % 8 == 0; x_f16
+ * 16-byte aligned; q_u8 4-byte aligned; z_dbg 16-byte aligned if given.
+ */
+qr_status qr_hadamard_quant(const void* x_f16, int64_t T, int32_t d, int64_t ld_x, qr_rot rot,
+                            const int8_t* signs, float clip_ratio, void* q_u8, void* scale_f16,
+                            float* z_dbg, hipStream_t stream);
+
+/*
+ * Rotation only (for example post-RoPE queries, whose rotation cancels against
+ * the rotated keys in q.k):  y = H_d (s * x) / sqrt(d), computed as
+ * fp32(z * c) with z and c as in qr_hadamard_quant, written as fp32
+ * (y_is_f32 != 0) or rounded to fp16.
+ *   x_f16 [T, ld_x] fp16; signs [d] int8 or NULL; y [T, d] contiguous.
+ * Requirements as qr_hadamard_quant (y 16-byte aligned).
+ */
+qr_status qr_hadamard(const void* x_f16, int64_t T, int32_t d, int64_t ld_x, const int8_t* signs,
+                      void* y, int32_t y_is_f32, hipStream_t stream);
+
+/*
+ * W4A4 GEMM with fused dequantization epilogue:
+ *   acc[t, n] = sum_k A[t, k] W[n, k]   (int32, exact)
+ *   Y[t, n]   = fp16(fp32(fp32(acc) * a_scale[t]) * w_scale[n])
+ *   a_q        [T, K/2] packed signed INT4 (row-major, contiguous).
+ *   a_scale    [T] fp16 token scales.
+ *   w_q        [N, K/2] packed signed INT4 (row-major, contiguous: one output
+ *              channel per row, the layout qr_hadamard_quant writes when run
+ *              on W with T := N).
+ *   w_scale    [N] fp16 channel scales.
+ *   y_f16      [T, N] fp16 output (contiguous).
+ *   acc_dbg    NULL, or [T, N] int32 (output): the exact accumulators.
+ * Requirements: T, N >= 0; K > 0, K % 64 == 0, K <= 131072; a_q and w_q
+ * 16-byte aligned; y_f16 and acc_dbg 4-byte aligned.
+ */
+qr_status qr_w4a4_gemm(const void* a_q, const void* a_scale_f16, int64_t T, const void* w_q,
+                       const void* w_scale_f16, int64_t N, int64_t K, void* y_f16,
+                       int32_t* acc_dbg, hipStream_t stream);
+
+/*
+ * Head-wise rotation + asymmetric 4-bit group quantization of new K or V
+ * tokens, written into a packed cache (Init: start_pos = 0, S_new = prompt
+ * length; Append: S_new = 1 at the next position).
+ *   kv_f16      [B, S_new, H, Dh] fp16; token (b, s) starts at element
+ *               (b * S_new + s) * ld_token, head h at + h * Dh.
+ *   rot         QR_ROT_HADAMARD: y = H_Dh (s * x) / sqrt(Dh) per head (keys);
+ *               QR_ROT_NONE: y = x (values, whose rotation is fused offline).
+ *   signs       [Dh] int8 +-1 or NULL (all +1).
+ *   group       group size G dividing Dh (G even, G >= 8).
+ *   clip_ratio  in [1/1024, 1].  Per group: mx = clip * max y, mn = clip * min y,
+ *               scale = fp16((mx - mn) / 15), min = fp16(mn),
+ *               q = clamp(rne((y - min) / scale), 0, 15), q = 0 if scale == 0.
+ *               fp32 recipe: y = fp32(z * c); s_h = fp16(fp32(mx_c - mn_c) / 15);
+ *               m_h = fp16(mn_c); q = clamp(rne(exact fp32(y - m_h) * fp32(1/s_h)), 0, 15).
+ *   cache_q     [B, H, S_max, Dh/2] uint8 packed unsigned codes.
+ *   cache_meta  [B, H, S_max, Dh/G, 2] fp16 (scale, min) pairs.
+ *   start_pos   first cache position written; positions start_pos ..
+ *               start_pos + S_new - 1 are overwritten, nothing else is touched.
+ *   z_dbg       NULL, or [B, S_new, H, Dh] fp32: z before the 1/sqrt(Dh) factor.
+ * Requirements: B, H >= 1, S_new >= 0; Dh a power of two, 8 <= Dh <= 256;
+ * ld_token >= H * Dh, ld_token % 8 == 0; 0 <= start_pos and
+ * start_pos + S_new <= S_max; kv_f16 16-byte aligned; cache_q 4-byte aligned;
+ * cache_meta 4-byte aligned.
+ */
+qr_status qr_kv_rotate_quant(const void* kv_f16, int32_t B, int32_t S_new, int32_t H, int32_t Dh,
+                             int64_t ld_token, qr_rot rot, const int8_t* signs, int32_t group,
+                             float clip_ratio, void* cache_q, void* cache_meta, int32_t S_max,
+                             int32_t start_pos, float* z_dbg, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QR_H_ */

@@ -1,0 +1,152 @@
+"""The C-ABI library loads, exports every symbol include/qr.h declares, and its
+host-side validation rejects bad arguments before any launch (no GPU needed:
+every call here returns before touching the device)."""
+import ctypes
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+
+import hadamard_rotation_int4_amd as qr
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "qr.h"
+
+QR_OK, QR_ERR_NULL, QR_ERR_SHAPE, QR_ERR_UNSUPPORTED, QR_ERR_ALIGN, QR_ERR_LAUNCH, QR_ERR_ARG = range(7)
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qr_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not qr.LIB_PATH.exists():
+        pytest.fail(f"{qr.LIB_PATH} not built: run `python -m hadamard_rotation_int4_amd.build`")
+    return qr._load()
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for must in ("qr_hadamard_quant", "qr_hadamard", "qr_w4a4_gemm", "qr_kv_rotate_quant",
+                 "qr_hadamard_factor", "qr_status_str", "qr_abi_version"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", str(qr.LIB_PATH)], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def test_version_and_status_strings(lib):
+    assert qr.abi_version() == 1
+    for code in range(7):
+        assert qr.status_str(code).startswith("QR_")
+    assert "unknown" in qr.status_str(99)
+
+
+@pytest.mark.parametrize("d,expect", [(4096, (12, 1)), (8192, (13, 1)), (128, (7, 1)),
+                                      (11008, (6, 172)), (28672, (10, 28)), (56, (1, 28)),
+                                      (344, (1, 172))])
+def test_factor(lib, d, expect):
+    assert qr.hadamard_factor(d) == expect
+
+
+@pytest.mark.parametrize("d", [0, 4, 43, 100, 16384, 172 * 128, 28 * 2048, 4097])
+def test_factor_rejects(lib, d):
+    n, m = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    assert lib.qr_hadamard_factor(d, ctypes.byref(n), ctypes.byref(m)) == QR_ERR_UNSUPPORTED
+    assert n.value == -1 and m.value == -1
+    assert lib.qr_hadamard_factor(4096, None, None) == QR_ERR_NULL
+
+
+A16 = 1 << 20  # a fake, 16-byte-aligned non-null address (never dereferenced on the host)
+
+
+def hq(lib, x=A16, T=4, d=4096, ld=4096, rot=1, signs=None, clip=1.0, q=A16, sc=A16, z=None):
+    return lib.qr_hadamard_quant(x, T, d, ld, rot, signs, clip, q, sc, z, None)
+
+
+def test_hadamard_quant_validation(lib):
+    assert hq(lib, T=0) == QR_OK                       # empty: no launch
+    assert hq(lib, T=-1) == QR_ERR_SHAPE
+    assert hq(lib, ld=4000) == QR_ERR_SHAPE            # ld < d
+    assert hq(lib, d=4100, ld=4104) == QR_ERR_UNSUPPORTED
+    assert hq(lib, d=43, ld=48) == QR_ERR_UNSUPPORTED
+    assert hq(lib, rot=7) == QR_ERR_ARG
+    assert hq(lib, clip=0.0) == QR_ERR_ARG
+    assert hq(lib, clip=1.5) == QR_ERR_ARG
+    assert hq(lib, clip=1e-4) == QR_ERR_ARG
+    assert hq(lib, x=None) == QR_ERR_NULL
+    assert hq(lib, q=None) == QR_ERR_NULL
+    assert hq(lib, sc=None) == QR_ERR_NULL
+    assert hq(lib, x=A16 + 8) == QR_ERR_ALIGN
+    assert hq(lib, ld=4100) == QR_ERR_ALIGN
+    assert hq(lib, q=A16 + 2) == QR_ERR_ALIGN
+    assert hq(lib, z=A16 + 4) == QR_ERR_ALIGN
+    # quantization without rotation accepts any width that is a multiple of 8
+    assert hq(lib, T=0, d=4000, ld=4000, rot=0) == QR_OK
+    assert hq(lib, d=4004, ld=4008, rot=0) == QR_ERR_UNSUPPORTED
+
+
+def test_hadamard_validation(lib):
+    assert lib.qr_hadamard(A16, 0, 128, 128, None, A16, 1, None) == QR_OK
+    assert lib.qr_hadamard(A16, 3, 100, 100, None, A16, 1, None) == QR_ERR_UNSUPPORTED
+    assert lib.qr_hadamard(None, 3, 128, 128, None, A16, 1, None) == QR_ERR_NULL
+    assert lib.qr_hadamard(A16, 3, 128, 128, None, A16 + 4, 1, None) == QR_ERR_ALIGN
+
+
+def gemm(lib, a=A16, asc=A16, T=16, w=A16, wsc=A16, N=16, K=4096, y=A16, acc=None):
+    return lib.qr_w4a4_gemm(a, asc, T, w, wsc, N, K, y, acc, None)
+
+
+def test_gemm_validation(lib):
+    assert gemm(lib, T=0) == QR_OK
+    assert gemm(lib, N=0) == QR_OK
+    assert gemm(lib, T=-2) == QR_ERR_SHAPE
+    assert gemm(lib, K=0) == QR_ERR_SHAPE
+    assert gemm(lib, K=4100) == QR_ERR_UNSUPPORTED
+    assert gemm(lib, K=131072) == QR_ERR_UNSUPPORTED
+    assert gemm(lib, a=None) == QR_ERR_NULL
+    assert gemm(lib, y=None) == QR_ERR_NULL
+    assert gemm(lib, a=A16 + 4) == QR_ERR_ALIGN
+    assert gemm(lib, y=A16 + 2) == QR_ERR_ALIGN
+
+
+def kvq(lib, B=2, S_new=3, H=8, Dh=128, ld=1024, rot=1, group=128, clip=0.95, cq=A16, meta=A16,
+        S_max=10, start=0, kv=A16):
+    return lib.qr_kv_rotate_quant(kv, B, S_new, H, Dh, ld, rot, None, group, clip, cq, meta, S_max,
+                                  start, None, None)
+
+
+def test_kv_validation(lib):
+    assert kvq(lib, S_new=0) == QR_OK
+    assert kvq(lib, start=8) == QR_ERR_SHAPE          # 8 + 3 > 10: cache overflow
+    assert kvq(lib, start=-1) == QR_ERR_SHAPE
+    assert kvq(lib, B=0) == QR_ERR_SHAPE
+    assert kvq(lib, Dh=96, ld=768) == QR_ERR_UNSUPPORTED
+    assert kvq(lib, group=48) == QR_ERR_UNSUPPORTED
+    assert kvq(lib, group=256) == QR_ERR_UNSUPPORTED
+    assert kvq(lib, ld=1000) == QR_ERR_SHAPE
+    assert kvq(lib, clip=2.0) == QR_ERR_ARG
+    assert kvq(lib, rot=3) == QR_ERR_ARG
+    assert kvq(lib, kv=None) == QR_ERR_NULL
+    assert kvq(lib, cq=A16 + 2) == QR_ERR_ALIGN
+    assert kvq(lib, ld=1028) == QR_ERR_ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((4, 128), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        qr.hadamard_quant(x)
+    with pytest.raises(TypeError):
+        qr.hadamard_quant(x.float())

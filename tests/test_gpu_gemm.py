@@ -1,0 +1,86 @@
+"""GPU parity: qr_w4a4_gemm against the oracle's exact integer GEMM and fp32 epilogue."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import gemm as og
+from oracle import quant as oq
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+qr = pytest.importorskip("hadamard_rotation_int4_amd")
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def run(ap, asc, wp, wsc):
+    y, acc = qr.w4a4_gemm(dev(ap), dev(asc), dev(wp), dev(wsc), acc_dbg=True)
+    return host(y), host(acc)
+
+
+SHAPES = [(1, 1, 64), (7, 100, 128), (300, 260, 192), (33, 17, 4096), (256, 256, 256),
+          (513, 300, 1024), (64, 640, 11008), (257, 513, 320), (2, 4096, 128)]
+
+
+@pytest.mark.parametrize("T,N,K", SHAPES)
+def test_random_codes_bit_exact(T, N, K):
+    ap = wl.packed_codes(1, 0, T, K)
+    wp = wl.packed_codes(1, 1, N, K)
+    asc = wl.positive_scales(1, 0, T)
+    wsc = wl.positive_scales(1, 1, N)
+    y, acc = run(ap, asc, wp, wsc)
+    acc_ref = og.w4a4_acc(ap, wp)
+    assert np.array_equal(acc.astype(np.int64), acc_ref)
+    y_ref = og.epilogue_recipe(acc_ref, asc, wsc)
+    assert np.array_equal(y.view(np.uint16), y_ref.view(np.uint16))
+
+
+def test_extreme_magnitude():
+    T, N, K = 40, 70, 28672
+    ap = np.full((T, K // 2), 0x88, dtype=np.uint8)   # every code -8
+    wp = np.full((N, K // 2), 0x88, dtype=np.uint8)
+    wp[1::2] = 0x77                                   # every code +7
+    asc = np.full(T, 2.0 ** -10, dtype=np.float16)
+    wsc = np.full(N, 2.0 ** -10, dtype=np.float16)
+    y, acc = run(ap, asc, wp, wsc)
+    assert acc[0, 0] == 64 * K and acc[0, 1] == -56 * K
+    assert np.array_equal(y.view(np.uint16), og.epilogue_recipe(og.w4a4_acc(ap, wp), asc, wsc).view(np.uint16))
+
+
+def test_epilogue_overflow_and_zero_scales():
+    T, N, K = 9, 33, 256
+    ap = wl.packed_codes(2, 0, T, K)
+    wp = wl.packed_codes(2, 1, N, K)
+    asc = wl.positive_scales(2, 0, T, 1.0, 1000.0)
+    asc[3] = 0.0
+    wsc = wl.positive_scales(2, 1, N, 1.0, 1000.0)
+    y, acc = run(ap, asc, wp, wsc)
+    y_ref = og.epilogue_recipe(og.w4a4_acc(ap, wp), asc, wsc)
+    assert np.isinf(y_ref).any()
+    assert np.array_equal(y.view(np.uint16), y_ref.view(np.uint16))
+
+
+def test_output_without_debug_matches():
+    T, N, K = 100, 300, 4096
+    ap = wl.packed_codes(3, 0, T, K)
+    wp = wl.packed_codes(3, 1, N, K)
+    asc = wl.positive_scales(3, 0, T)
+    wsc = wl.positive_scales(3, 1, N)
+    y = host(qr.w4a4_gemm(dev(ap), dev(asc), dev(wp), dev(wsc)))
+    y_ref = og.epilogue_recipe(og.w4a4_acc(ap, wp), asc, wsc)
+    assert np.array_equal(y.view(np.uint16), y_ref.view(np.uint16))
+
+
+def test_empty():
+    z = dev(np.zeros((0, 32), dtype=np.uint8))
+    w = dev(np.zeros((5, 32), dtype=np.uint8))
+    y = qr.w4a4_gemm(z, dev(np.zeros(0, np.float16)), w, dev(np.ones(5, np.float16)))
+    assert tuple(y.shape) == (0, 5)
