@@ -15,42 +15,60 @@
 //    A and W use the same permutation of k, so the dot product is unchanged,
 //    and the int32 accumulator holds 256 * acc exactly (|256 acc| <= 256 * 64 * K
 //    < 2^31 for K <= 131008); the epilogue shifts it back.
-//  * Tiles: 256 x 256 outputs per workgroup of 4 wavefronts, each owning a
-//    128 x 128 block = 4 x 4 MFMA tiles (accumulators in the unified register
-//    file), K advanced 128 at a time through double-buffered LDS (2 x 32 KB).
-//  * LDS layout [kk][half][row][8 bytes]: a 32-lane half wavefront reads 32
-//    consecutive rows x 8 bytes = 256 contiguous bytes, conflict-free.
+//  * Tiles: 256 x 256 outputs per workgroup of 4 wavefronts (one per SIMD), each
+//    owning a 128 x 128 block = 4 x 4 MFMA tiles whose accumulators live in the
+//    AGPR half of the register file.  K advances 256 at a time through two LDS
+//    stages of 64 KB; the next step's panels are fetched into registers while
+//    the current one is multiplied, and written to the other stage at the end.
+//  * Each lane reads whole 16-byte k-chunks (32 codes) and feeds two MFMAs from
+//    one chunk: lane (row, half h) takes chunk 2p + h for MFMA steps 2p and
+//    2p + 1, identically for A and W, so every k is summed exactly once.  The
+//    reads of the next chunk pair and the unpacking of the next half are
+//    interleaved with the current MFMAs (pinned with sched_group_barrier), and
+//    the staging of the next step's panels (LDS writes, global reads) is
+//    spread over the last half-step's MFMAs.
+//  * LDS layout [chunk][row ^ f(chunk)][16 bytes] with f(c) = 2c | parity(c):
+//    a half wavefront reads 32 rows of one chunk (512 contiguous bytes), and the
+//    staging writes -- 8 lanes per row, one per chunk -- land in distinct banks
+//    for both 8- and 16-lane LDS passes (f mod 8 and f >> 1 are permutations).
 //  * Tile order: workgroup ids are remapped so that the ids the hardware places
 //    on one XCD (id % 8) are consecutive, then grouped 8 tile-rows at a time, so
 //    the tiles running together on an XCD share A and W panels in its L2.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace qr {
 
-constexpr int BM = 256, BN = 256, BK = 128;  // BK in int4 elements (64 bytes per row)
+constexpr int BM = 256, BN = 256, BK = 256;  // BK in int4 elements (128 bytes per row)
+constexpr int KCH = BK / 32;                 // 16-byte k-chunks per row and step
 constexpr int GEMM_THREADS = 256;
-constexpr int PANEL_BYTES = 256 * 64;  // one operand's tile per K step: 16 KB
+constexpr int OPER_BYTES = BM * BK / 2;      // one operand's panel per step: 32 KB
+constexpr int STAGE_BYTES = 2 * OPER_BYTES;  // A + W: 64 KB
+constexpr int GEMM_LDS = 2 * STAGE_BYTES;    // two stages: 128 KB
+constexpr int PIECES = BM * KCH / GEMM_THREADS;  // 16-byte global pieces per thread and operand
 
-__device__ __forceinline__ v4i unpack16(uint32_t d0, uint32_t d1) {
+__device__ __forceinline__ v4i unpack16(uint2 d) {
   v4i r;
-  r[0] = (int)((d0 << 4) & 0xF0F0F0F0u);
-  r[1] = (int)(d0 & 0xF0F0F0F0u);
-  r[2] = (int)((d1 << 4) & 0xF0F0F0F0u);
-  r[3] = (int)(d1 & 0xF0F0F0F0u);
+  r[0] = (int)((d.x << 4) & 0xF0F0F0F0u);
+  r[1] = (int)(d.x & 0xF0F0F0F0u);
+  r[2] = (int)((d.y << 4) & 0xF0F0F0F0u);
+  r[3] = (int)(d.y & 0xF0F0F0F0u);
   return r;
 }
 
-// LDS byte offset of the 8-byte half `hf` (0/1) of k-chunk `kk` (0..3) of row r.
-__device__ __forceinline__ int lds_off(int kk, int hf, int r) {
-  return ((kk * 2 + hf) * 256 + r) * 8;
+// LDS byte offset of 16-byte k-chunk `kk` of panel row r (swizzled).
+__device__ __forceinline__ int lds_off(int kk, int r) {
+  const int f = (kk << 1) | (__builtin_popcount(kk) & 1);
+  return kk * 4096 + ((r ^ f) << 4);
 }
 
-template <bool DBG>
+template <bool DBG, bool KTAIL>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
     const uint8_t* __restrict__ A, const uint16_t* __restrict__ a_scale, int T,
     const uint8_t* __restrict__ W, const uint16_t* __restrict__ w_scale, int N, int K,
     uint16_t* __restrict__ Y, int32_t* __restrict__ acc_dbg, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][PANEL_BYTES];  // [stage][A/W]
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   // ---- tile assignment (XCD-aware, grouped) ----
   const int nblk = tiles_m * tiles_n;
@@ -72,44 +90,57 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
   const int li = lane & 31, lg = lane >> 5;                  // MFMA row/col lane, k-half
   const int64_t rowbytes = K / 2;
 
-  // ---- global -> register staging: 4 x 16 B of A and of W per thread ----
-  // chunk id = tid + 256 j: row = id >> 2, kk = id & 3
-  const uint8_t* a_src[4];
-  const uint8_t* w_src[4];
-  int st_row[4], st_kk[4];
+  // ---- global -> register staging: PIECES x 16 B of A and of W per thread ----
+  // piece id = tid + 256 j: row = (tid >> 3) + 32 j, k-chunk = tid & 7 (fixed per
+  // thread).  Raw buffer loads over the tile's own rows: rows past T (or N)
+  // fall outside the buffer's range and read as zero.
+  const int st_kk = tid & (KCH - 1);
+  const int st_r0 = tid / KCH;
+  const int rows_a = min(T - m0, BM), rows_w = min(N - n0, BN);
+  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + (int64_t)m0 * rowbytes), 0, (int)(rows_a * rowbytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_w = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (int64_t)n0 * rowbytes), 0, (int)(rows_w * rowbytes), 0x00020000);
+  const int voff = st_r0 * (int)rowbytes + st_kk * 16;
+  const int rstep = (GEMM_THREADS / KCH) * (int)rowbytes;
+  v4u ra[PIECES], rw[PIECES];
+  auto gload = [&](int k0, bool last) {  // k0 in elements
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int id = tid + 256 * j;
-    st_row[j] = id >> 2;
-    st_kk[j] = id & 3;
-    const int ar = min(m0 + st_row[j], T - 1);
-    const int wr = min(n0 + st_row[j], N - 1);
-    a_src[j] = A + (int64_t)ar * rowbytes + st_kk[j] * 16;
-    w_src[j] = W + (int64_t)wr * rowbytes + st_kk[j] * 16;
-  }
-  v4u ra[4], rw[4];
-  auto gload = [&](int k0) {  // k0 in elements
+    for (int j = 0; j < PIECES; ++j) {
+      // the whole offset goes in the VGPR operand: the range check of a raw
+      // buffer covers the VGPR offset, not the SGPR one
+      const int off = voff + j * rstep + k0 / 2;
+      ra[j] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, off, 0, 0));
+      rw[j] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_w, off, 0, 0));
+    }
+    if (KTAIL && last && k0 + st_kk * 32 >= K) {  // chunk past K (K is a multiple of 32)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (k0 + st_kk[j] * 32 < K) {
-        ra[j] = *(const v4u*)(a_src[j] + k0 / 2);
-        rw[j] = *(const v4u*)(w_src[j] + k0 / 2);
-      } else {
+      for (int j = 0; j < PIECES; ++j) {
         ra[j] = v4u{0u, 0u, 0u, 0u};
         rw[j] = v4u{0u, 0u, 0u, 0u};
       }
     }
   };
   auto lstore = [&](int stage) {
+    uint8_t* pa = smem + stage * STAGE_BYTES;
+    uint8_t* pw = pa + OPER_BYTES;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint8_t* pa = &smem[stage][0][0];
-      uint8_t* pw = &smem[stage][1][0];
-      *(uint2*)(pa + lds_off(st_kk[j], 0, st_row[j])) = make_uint2(ra[j][0], ra[j][1]);
-      *(uint2*)(pa + lds_off(st_kk[j], 1, st_row[j])) = make_uint2(ra[j][2], ra[j][3]);
-      *(uint2*)(pw + lds_off(st_kk[j], 0, st_row[j])) = make_uint2(rw[j][0], rw[j][1]);
-      *(uint2*)(pw + lds_off(st_kk[j], 1, st_row[j])) = make_uint2(rw[j][2], rw[j][3]);
+    for (int j = 0; j < PIECES; ++j) {
+      const int r = st_r0 + (GEMM_THREADS / KCH) * j;
+      *(v4u*)(pa + lds_off(st_kk, r)) = ra[j];
+      *(v4u*)(pw + lds_off(st_kk, r)) = rw[j];
     }
+  };
+  // packed fragments of chunk pair p (lane takes chunk 2p + lg): 4 of A
+  // (rows wm + 32 i + li) and 4 of W
+  auto lread = [&](int stage, int p, v4u* fa, v4u* fb) {
+    const uint8_t* pa = smem + stage * STAGE_BYTES;
+    const uint8_t* pw = pa + OPER_BYTES;
+    const int kk = 2 * p + lg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = *(const v4u*)(pa + lds_off(kk, wm + i * 32 + li));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = *(const v4u*)(pw + lds_off(kk, wn + j * 32 + li));
   };
 
   v16i acc[4][4];
@@ -120,59 +151,144 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
+  // Register pipeline per chunk pair p: packed fragments f (read one pair
+  // ahead), unpacked halves ua/ub[0] (e = 0) and [1] (e = 1).  While the MFMAs
+  // of one half run, the VALU unpacks the other and the LDS reads of the next
+  // pair are in flight; sched_group_barrier pins that order.
+  v4u fa[2][4], fb[2][4];
+  v4i ua[2][4], ub[2][4];
+  auto unpack_half = [&](const v4u* xa, const v4u* xb, int e, v4i* oa, v4i* ob) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oa[i] = unpack16(make_uint2(xa[i][2 * e], xa[i][2 * e + 1]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ob[j] = unpack16(make_uint2(xb[j][2 * e], xb[j][2 * e + 1]));
+  };
+  auto mfma16 = [&](const v4i* a, const v4i* b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+  constexpr int NP = KCH / 2;  // chunk pairs per step
   const int ksteps = (K + BK - 1) / BK;
-  gload(0);
+  // One K step from LDS stage `stage`.  MORE: a next step exists -- stage its
+  // panels (loaded one step earlier) into the other LDS stage during the last
+  // half-step, fetch the step after it, and start reading the other stage.
+  auto kstep = [&](int stage, int ks, auto more_tag) {
+    constexpr bool MORE = decltype(more_tag)::value;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int cur = p & 1, nxt = cur ^ 1;
+      if (p + 1 < NP) {
+        __builtin_amdgcn_sched_barrier(0);
+        lread(stage, p + 1, fa[nxt], fb[nxt]);
+        mfma16(ua[0], ub[0]);
+        unpack_half(fa[cur], fb[cur], 1, ua[1], ub[1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 8 DS reads first
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma16(ua[1], ub[1]);
+        unpack_half(fa[nxt], fb[nxt], 0, ua[0], ub[0]);
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        mfma16(ua[0], ub[0]);
+        unpack_half(fa[cur], fb[cur], 1, ua[1], ub[1]);
+        if (MORE) {
+          lstore(stage ^ 1);
+          gload(min(ks + 2, ksteps - 1) * BK, ks + 3 >= ksteps);
+#pragma unroll
+          for (int m = 0; m < 16; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 2);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 2);  // 1 DS write
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 2);  // 1 VMEM read
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          __syncthreads();
+          lread(stage ^ 1, 0, fa[nxt], fb[nxt]);
+          mfma16(ua[1], ub[1]);
+          unpack_half(fa[nxt], fb[nxt], 0, ua[0], ub[0]);
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 3);
+#pragma unroll
+          for (int m = 0; m < 16; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 3);
+          }
+        } else {
+          mfma16(ua[1], ub[1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  gload(0, ksteps == 1);
   lstore(0);
   __syncthreads();
-  for (int ks = 0; ks < ksteps; ++ks) {
-    const int stage = ks & 1;
-    if (ks + 1 < ksteps) gload((ks + 1) * BK);
-    const uint8_t* pa = &smem[stage][0][0];
-    const uint8_t* pw = &smem[stage][1][0];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      v4i af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint2 v = *(const uint2*)(pa + lds_off(kk, lg, wm + i * 32 + li));
-        af[i] = unpack16(v.x, v.y);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint2 v = *(const uint2*)(pw + lds_off(kk, lg, wn + j * 32 + li));
-        bf[j] = unpack16(v.x, v.y);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    if (ks + 1 < ksteps) lstore(stage ^ 1);
-    __syncthreads();
-  }
+  gload(min(1, ksteps - 1) * BK, ksteps <= 2);
+  lread(0, 0, fa[0], fb[0]);
+  unpack_half(fa[0], fb[0], 0, ua[0], ub[0]);
+  for (int ks = 0; ks + 1 < ksteps; ++ks) kstep(ks & 1, ks, std::true_type{});
+  kstep((ksteps - 1) & 1, ksteps - 1, std::false_type{});
 
   // ---- epilogue: 32x32 accumulator layout: lane (n = li, k-half lg), register r
   //      holds row 8 (r / 4) + 4 lg + (r % 4) ----
+  float wsc[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn + j * 32 + li;
-    if (n >= N) continue;
-    const float ws = h2f(w_scale[n]);
+  for (int j = 0; j < 4; ++j) wsc[j] = h2f(w_scale[min(n0 + wn + j * 32 + li, N - 1)]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 4; ++i) {
+    float asc[16];  // [r]: rows 8 (r / 4) + 4 lg + (r % 4) of block i
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t0 = m0 + wm + i * 32 + 8 * q + 4 * lg;
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) asc[4 * q + s2] = h2f(a_scale[min(t0 + s2, T - 1)]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + j * 32 + li;
+      if (n >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
         if (t < T) {
           const int32_t a = acc[i][j][r] >> 8;  // exact: the accumulator is 256 * acc
-          const float as = h2f(a_scale[t]);
-          Y[(int64_t)t * N + n] = f2h(__fmul_rn(__fmul_rn((float)a, as), ws));
+          Y[(int64_t)t * N + n] = f2h(__fmul_rn(__fmul_rn((float)a, asc[r]), wsc[j]));
           if (DBG) acc_dbg[(int64_t)t * N + n] = a;
         }
       }
     }
   }
+}
+
+template <bool DBG, bool KTAIL>
+static qr_status launch_gemm(const void* a_q, const void* a_scale, int64_t T, const void* w_q,
+                             const void* w_scale, int64_t N, int64_t K, void* y, int32_t* acc,
+                             int tiles_m, int tiles_n, hipStream_t stream) {
+  auto kern = k_w4a4_gemm<DBG, KTAIL>;
+  // Opting in to more than 64 KB of LDS is a per-kernel attribute; setting it
+  // again on every call is cheap and keeps the entry point free of state.
+  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          GEMM_LDS) != hipSuccess)
+    return QR_ERR_LAUNCH;
+  const int64_t nblk = (int64_t)tiles_m * tiles_n;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(GEMM_THREADS), GEMM_LDS, stream,
+                     (const uint8_t*)a_q, (const uint16_t*)a_scale, (int)T, (const uint8_t*)w_q,
+                     (const uint16_t*)w_scale, (int)N, (int)K, (uint16_t*)y, acc, tiles_m,
+                     tiles_n);
+  return launch_status();
 }
 
 }  // namespace qr
@@ -194,15 +310,14 @@ extern "C" qr_status qr_w4a4_gemm(const void* a_q, const void* a_scale_f16, int6
   const int tiles_n = (int)((N + BN - 1) / BN);
   const int64_t nblk = (int64_t)tiles_m * tiles_n;
   if (nblk > INT32_MAX) return QR_ERR_SHAPE;
+  const bool tail = (K % BK) != 0;
   if (acc_dbg)
-    hipLaunchKernelGGL((k_w4a4_gemm<true>), dim3((unsigned)nblk), dim3(GEMM_THREADS), 0, stream,
-                       (const uint8_t*)a_q, (const uint16_t*)a_scale_f16, (int)T,
-                       (const uint8_t*)w_q, (const uint16_t*)w_scale_f16, (int)N, (int)K,
-                       (uint16_t*)y_f16, acc_dbg, tiles_m, tiles_n);
-  else
-    hipLaunchKernelGGL((k_w4a4_gemm<false>), dim3((unsigned)nblk), dim3(GEMM_THREADS), 0, stream,
-                       (const uint8_t*)a_q, (const uint16_t*)a_scale_f16, (int)T,
-                       (const uint8_t*)w_q, (const uint16_t*)w_scale_f16, (int)N, (int)K,
-                       (uint16_t*)y_f16, (int32_t*)nullptr, tiles_m, tiles_n);
-  return launch_status();
+    return tail ? launch_gemm<true, true>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16,
+                                          acc_dbg, tiles_m, tiles_n, stream)
+                : launch_gemm<true, false>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16,
+                                           acc_dbg, tiles_m, tiles_n, stream);
+  return tail ? launch_gemm<false, true>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16,
+                                         nullptr, tiles_m, tiles_n, stream)
+              : launch_gemm<false, false>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16,
+                                          nullptr, tiles_m, tiles_n, stream);
 }
