@@ -521,6 +521,285 @@ __global__ __launch_bounds__(256) void k_hq_lds(const uint16_t* __restrict__ x, 
 }
 
 // ===========================================================================
+// k_hq_k28: d = 1024 * 28 = 28672, one workgroup of 4 wavefronts per row
+// ===========================================================================
+// The row is a [1024 chunks x 28] matrix; z = (H_1024 (x) H_28) (s * x).  With
+// H_1024 = H_256 (x) H_4 the factor H_112 = H_4 (x) H_28 acts on 4 consecutive
+// chunks ("group" G = 0..255, 112 contiguous elements) and is a dense +-1
+// contraction: it runs on the matrix cores (v_mfma_f32_16x16x32_f16) straight
+// on the fp16 input with the signs XORed into the sign bits, which is exact
+// (products are +-x, accumulation fp32).  B column n of an MFMA is one group,
+// K = 112 padded to 4 blocks of 32, M = 112 = 7 tiles of 16.  The A rows are
+// permuted so that lane (n, g) receives all 28 outputs of chunk 4G + g.
+// H_256 over G remains, in fp32 VALU: G = 64 w + 16 ct + gmap(n) with w the
+// wavefront, ct the lane's column tile (4 per wavefront): four stages through
+// DPP across lanes, two between registers, and a radix-4 stage across the
+// wavefronts through LDS (four rounds of 7 chunk positions).  After it each
+// wavefront owns column tile ct = w of all four w'' and so whole chunks; amax
+// is reduced through LDS, and the packed codes are staged in LDS (aliasing the
+// exchange buffer) for coalesced row stores.
+constexpr int K28_XROUND = 4 * 4 * 7 * 64;  // floats per exchange round: [w][ct][7][lane]
+constexpr int K28_AFRAG = 7 * 4 * 64;       // v8h A fragments: [mt][kb][lane]
+
+template <int MODE, bool CLAMP>
+__global__ __launch_bounds__(256, 2) void k_hq_k28(const uint16_t* __restrict__ x, int64_t T,
+                                                   int64_t ld, const int8_t* __restrict__ signs,
+                                                   float c, float clip, uint8_t* __restrict__ q,
+                                                   uint16_t* __restrict__ scale,
+                                                   float* __restrict__ zdbg,
+                                                   void* __restrict__ yout) {
+  constexpr int D = 28672;
+  __shared__ v8h s_afrag[K28_AFRAG];           // 28 KB
+  __shared__ float s_x[K28_XROUND];            // 28 KB, also the packed-row stage
+  __shared__ float s_red[4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int gc = gmap(n);
+
+  // A fragments of H_112 = H_4 (x) H_28: tile mt row i -> output 28 (i >> 2) + 4 mt + (i & 3),
+  // block kb lane (i, g) holds columns 32 kb + 8 g + j (zero past 112).
+  for (int f = tid; f < K28_AFRAG; f += 256) {
+    const int fl = f & 63, mk = f >> 6;
+    const int mt = mk >> 2, kb = mk & 3;
+    const int i = fl & 15, gg = fl >> 4;
+    const int o = 28 * (i >> 2) + 4 * mt + (i & 3);
+    v8h a;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = 32 * kb + 8 * gg + j;
+      float v = 0.0f;
+      if (col < 112) {
+        const int h4 = (__builtin_popcount((o / 28) & (col / 28)) & 1) ? -1 : 1;
+        v = (float)h4 * g_h28.v[o % 28][col % 28];
+      }
+      a[j] = (_Float16)v;
+    }
+    s_afrag[f] = a;
+  }
+  // Signs of the lane's B fragments (the same for every row), one dword per
+  // fragment: bit 15 - j holds the sign of element 2 j, bit 31 - j that of
+  // element 2 j + 1, so (E << j) & 0x80008000 is the sign-bit mask of dword j.
+  uint32_t sbits[4][4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int G = (w * 4 + ct) * 16 + gc;
+      const int e0 = G * 112 + 32 * kb + 8 * g;
+      uint32_t e = 0u;
+      if (signs && 32 * kb + 8 * g < 112) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          e |= (signs[e0 + 2 * j] < 0 ? (0x8000u >> j) : 0u) |
+               (signs[e0 + 2 * j + 1] < 0 ? (0x80000000u >> j) : 0u);
+      }
+      sbits[ct][kb] = e;
+    }
+  const float s0 = (gc & 1) ? -1.0f : 1.0f;
+  const float s1 = (gc & 2) ? -1.0f : 1.0f;
+  const float s2 = (gc & 4) ? -1.0f : 1.0f;
+  const float s3 = (gc & 8) ? -1.0f : 1.0f;
+  const float sigma = (__builtin_popcount(gc) & 1) ? -1.0f : 1.0f;  // lane holds sigma * z
+  __syncthreads();
+
+  for (int64_t row = blockIdx.x; row < T; row += gridDim.x) {
+    const uint16_t* xr = x + row * ld;
+    // ---- B fragments: group G, elements 32 kb + 8 g .. + 7 (16 bytes) ----
+    v4u braw[4][4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int G = (w * 4 + ct) * 16 + gc;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (kb < 3 || g < 2) {
+          v4u raw = *(const v4u*)(xr + G * 112 + 32 * kb + 8 * g);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) raw[j] ^= (sbits[ct][kb] << j) & 0x80008000u;
+          braw[ct][kb] = raw;
+        } else {
+          braw[ct][kb] = v4u{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+    // ---- H_112 on the matrix cores ----
+    float v[4][28];
+#pragma unroll
+    for (int mt = 0; mt < 7; ++mt) {
+      v4f accm[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) accm[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const v8h a = s_afrag[(mt * 4 + kb) * 64 + lane];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const v8h b = __builtin_bit_cast(v8h, braw[ct][kb]);
+          accm[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, accm[ct], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[ct][4 * mt + r] = accm[ct][r];
+    }
+    // keep a compiler-visible VALU op between the MFMA results and the DPP asm
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int k = 0; k < 28; ++k) v[ct][k] = __fadd_rn(v[ct][k], 0.0f);
+    // ---- H_16 over gmap(n): DPP butterflies across lanes ----
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+      for (int k = 0; k < 24; k += 8) QR_DPP8("quad_perm:[1,0,3,2]", (&v[ct][k]), s0);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+      for (int k = 0; k < 24; k += 8) QR_DPP8("quad_perm:[2,3,0,1]", (&v[ct][k]), s1);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+      for (int k = 0; k < 24; k += 8) QR_DPP8("row_half_mirror", (&v[ct][k]), s2);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+      for (int k = 0; k < 24; k += 8) QR_DPP8("row_mirror", (&v[ct][k]), s3);
+    }
+    {
+      // positions 24..27 of the four column tiles, eight registers per call
+      float t8[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          t8[k] = v[2 * h][24 + k];
+          t8[4 + k] = v[2 * h + 1][24 + k];
+        }
+        QR_DPP8("quad_perm:[1,0,3,2]", t8, s0);
+        QR_DPP8("quad_perm:[2,3,0,1]", t8, s1);
+        QR_DPP8("row_half_mirror", t8, s2);
+        QR_DPP8("row_mirror", t8, s3);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[2 * h][24 + k] = t8[k];
+          v[2 * h + 1][24 + k] = t8[4 + k];
+        }
+      }
+    }
+    // ---- H_4 over ct: butterflies between registers ----
+#pragma unroll
+    for (int hb = 1; hb < 4; hb <<= 1)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        if (!(ct & hb))
+#pragma unroll
+          for (int k = 0; k < 28; ++k) {
+            const float a = v[ct][k], b = v[ct + hb][k];
+            v[ct][k] = a + b;
+            v[ct + hb][k] = a - b;
+          }
+    // ---- H_4 over the wavefront index through LDS; afterwards v[w''][k] holds
+    //      chunk 4 G + g, G = (4 w'' + w) 16 + gmap(n), position k ----
+    float o[4][28];
+#pragma unroll
+    for (int rnd = 0; rnd < 4; ++rnd) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int k = 0; k < 7; ++k) s_x[((w * 4 + ct) * 7 + k) * 64 + lane] = v[ct][7 * rnd + k];
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 7; ++k) {
+        const float a0 = s_x[((0 * 4 + w) * 7 + k) * 64 + lane];
+        const float a1 = s_x[((1 * 4 + w) * 7 + k) * 64 + lane];
+        const float a2 = s_x[((2 * 4 + w) * 7 + k) * 64 + lane];
+        const float a3 = s_x[((3 * 4 + w) * 7 + k) * 64 + lane];
+        const float p01 = a0 + a1, m01 = a0 - a1, p23 = a2 + a3, m23 = a2 - a3;
+        o[0][7 * rnd + k] = p01 + p23;
+        o[1][7 * rnd + k] = m01 + m23;
+        o[2][7 * rnd + k] = p01 - p23;
+        o[3][7 * rnd + k] = m01 - m23;
+      }
+      __syncthreads();
+    }
+    // chunk index of o[w2] for this lane
+    auto chunk_of = [&](int w2) { return 4 * ((4 * w2 + w) * 16 + gc) + g; };
+
+    if (zdbg) {
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        float* zr = zdbg + row * D + chunk_of(w2) * 28;
+#pragma unroll
+        for (int k = 0; k < 28; k += 4)
+          *(v4f*)(zr + k) = v4f{o[w2][k] * sigma, o[w2][k + 1] * sigma, o[w2][k + 2] * sigma,
+                                o[w2][k + 3] * sigma};
+      }
+    }
+    if (MODE == MODE_QUANT) {
+      float am = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2)
+#pragma unroll
+        for (int k = 0; k < 28; ++k) am = fmaxf(am, fabsf(o[w2][k]));
+      am = wave_max(am);
+      if (lane == 0) s_red[w] = am;
+      __syncthreads();
+      am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+      uint16_t sh;
+      float m;
+      sym_scale(am, c, clip, &sh, &m);
+      const float ml = m * sigma;
+      const bool clamp = CLAMP || (sh & 0x7fffu) < 0x0400u;  // block-uniform
+      uint16_t* stage16 = (uint16_t*)s_x;  // packed row, 14 bytes per chunk
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const int cb = chunk_of(w2) * 7;  // 16-bit word offset of the chunk
+        uint32_t words[4];
+#pragma unroll
+        for (int k8 = 0; k8 < 3; ++k8)
+          words[k8] = clamp ? quant_pack8<true>(&o[w2][8 * k8], ml)
+                            : quant_pack8<false>(&o[w2][8 * k8], ml);
+        float tail[8] = {o[w2][24], o[w2][25], o[w2][26], o[w2][27], 0.0f, 0.0f, 0.0f, 0.0f};
+        words[3] = clamp ? quant_pack8<true>(tail, ml) : quant_pack8<false>(tail, ml);
+#pragma unroll
+        for (int k = 0; k < 7; ++k)
+          stage16[cb + k] = (uint16_t)((k & 1) ? (words[k >> 1] >> 16) : (words[k >> 1] & 0xffffu));
+      }
+      __syncthreads();
+      const uint32_t* st32 = (const uint32_t*)s_x;
+      uint32_t* qr32 = (uint32_t*)(q + row * (D / 2));
+      for (int i = tid; i < D / 8; i += 256) qr32[i] = st32[i];
+      if (tid == 0) scale[row] = sh;
+      __syncthreads();  // the stage aliases the next row's exchange buffer
+    } else {
+      const float cs = c * sigma;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const int e0 = chunk_of(w2) * 28;
+        if (MODE == MODE_ROT_F32) {
+          float* yr = (float*)yout + row * D + e0;
+#pragma unroll
+          for (int k = 0; k < 28; k += 4)
+            *(v4f*)(yr + k) = v4f{__fmul_rn(o[w2][k], cs), __fmul_rn(o[w2][k + 1], cs),
+                                  __fmul_rn(o[w2][k + 2], cs), __fmul_rn(o[w2][k + 3], cs)};
+        } else {
+          uint32_t* yr = (uint32_t*)((uint16_t*)yout + row * D + e0);
+#pragma unroll
+          for (int k = 0; k < 28; k += 2)
+            yr[k / 2] = (uint32_t)f2h(__fmul_rn(o[w2][k], cs)) |
+                        ((uint32_t)f2h(__fmul_rn(o[w2][k + 1], cs)) << 16);
+        }
+      }
+    }
+  }
+}
+
+// ===========================================================================
 // Host side
 // ===========================================================================
 static int grid_for(int64_t work_items, int per_block, int cap) {
@@ -613,6 +892,12 @@ static qr_status dispatch(const void* x_f16, int64_t T, int32_t d, int64_t ld, i
     if (d >= 512)
       return launch_pow2<MODE, CLAMP>(d / 512, x, T, ld, signs, c, clip, qq, ss, z, y, st);
     return launch_small<MODE, CLAMP>(d, 1, x, T, ld, signs, c, clip, qq, ss, z, y, st);
+  }
+  if (m == 28 && n == 10) {
+    const int grid = grid_for(T, 1, 512);
+    hipLaunchKernelGGL((k_hq_k28<MODE, CLAMP>), dim3(grid), dim3(256), 0, st, x, T, ld, signs, c,
+                       clip, qq, ss, z, y);
+    return launch_status();
   }
   if (m == 28)
     return launch_lds_t<28, MODE, CLAMP, true>(d, n, x, T, ld, signs, c, clip, qq, ss, z, y, st);
