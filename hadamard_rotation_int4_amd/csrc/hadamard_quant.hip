@@ -73,6 +73,19 @@ __device__ __forceinline__ uint32_t quant_pack8(const float* v, float m) {
   return lo ^ hi ^ 0x88888888u;  // offset binary -> two's complement nibbles
 }
 
+// Streaming accesses: every input row is read once and every output written
+// once, so both bypass cache retention (non-temporal).
+#ifndef QR_NT
+#define QR_NT 1
+#endif
+__device__ __forceinline__ v4u ld_stream(const uint16_t* p) {
+  return QR_NT ? __builtin_nontemporal_load((const v4u*)p) : *(const v4u*)p;
+}
+__device__ __forceinline__ void st_stream(uint32_t* p, uint32_t v) {
+  if (QR_NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 // ===========================================================================
 // k_hq_pow2: d = NB * 512
 // ===========================================================================
@@ -104,8 +117,18 @@ __device__ __forceinline__ int gmap(int c) {
         "+v"(r[7])                                                                     \
       : "v"(s))
 
+#ifndef QR_POW2_WAVES_PER_SIMD
+#define QR_POW2_WAVES_PER_SIMD 2
+#endif
+#ifndef QR_POW2_PREFETCH
+#define QR_POW2_PREFETCH 1
+#endif
+#ifndef QR_K28_WAVES_PER_SIMD
+#define QR_K28_WAVES_PER_SIMD 2
+#endif
+
 template <int NB, int MODE, bool CLAMP>
-__global__ __launch_bounds__(256) void k_hq_pow2(const uint16_t* __restrict__ x, int64_t T,
+__global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const uint16_t* __restrict__ x, int64_t T,
                                                  int64_t ld, const int8_t* __restrict__ signs,
                                                  float c, float clip, uint8_t* __restrict__ q,
                                                  uint16_t* __restrict__ scale,
@@ -155,12 +178,20 @@ __global__ __launch_bounds__(256) void k_hq_pow2(const uint16_t* __restrict__ x,
   // After the four DPP stages the lane holds sigma * z.
   const float sigma = (__builtin_popcount(gc) & 1) ? -1.0f : 1.0f;
 
-  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < T; row += (int64_t)gridDim.x * 4) {
-    const uint16_t* xr = x + row * ld + lane_off;
-    v4u raw[NB];
+  // The next row's input is fetched into the same registers as soon as the
+  // MFMAs have consumed the current one, so its latency overlaps this row's work.
+  const int64_t rstride = (int64_t)gridDim.x * 4;
+  int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  v4u raw[NB];
+  if (QR_POW2_PREFETCH && row < T) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) raw[b] = *(const v4u*)(xr + b * 512);
-
+    for (int b = 0; b < NB; ++b) raw[b] = ld_stream(x + row * ld + lane_off + b * 512);
+  }
+  for (; row < T; row += rstride) {
+    if (!QR_POW2_PREFETCH) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) raw[b] = ld_stream(x + row * ld + lane_off + b * 512);
+    }
     float w[NB][8];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -174,6 +205,11 @@ __global__ __launch_bounds__(256) void k_hq_pow2(const uint16_t* __restrict__ x,
         w[b][j] = r0[j];
         w[b][4 + j] = r1[j];
       }
+    }
+    if (QR_POW2_PREFETCH && row + rstride < T) {
+      const uint16_t* xn = x + (row + rstride) * ld + lane_off;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) raw[b] = ld_stream(xn + b * 512);
     }
     // Butterflies over the block index (element bits 9 ..), inside the lane.
 #pragma unroll
@@ -230,10 +266,10 @@ __global__ __launch_bounds__(256) void k_hq_pow2(const uint16_t* __restrict__ x,
       // relative rounding error and takes the clamped path (wave-uniform branch).
       if (CLAMP || (sh & 0x7fffu) < 0x0400u) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) *(uint32_t*)(qr + b * 256) = quant_pack8<true>(w[b], ml);
+        for (int b = 0; b < NB; ++b) st_stream((uint32_t*)(qr + b * 256), quant_pack8<true>(w[b], ml));
       } else {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) *(uint32_t*)(qr + b * 256) = quant_pack8<false>(w[b], ml);
+        for (int b = 0; b < NB; ++b) st_stream((uint32_t*)(qr + b * 256), quant_pack8<false>(w[b], ml));
       }
       if (lane == 0) scale[row] = sh;
     } else {
@@ -542,7 +578,7 @@ constexpr int K28_XROUND = 4 * 4 * 7 * 64;  // floats per exchange round: [w][ct
 constexpr int K28_AFRAG = 7 * 4 * 64;       // v8h A fragments: [mt][kb][lane]
 
 template <int MODE, bool CLAMP>
-__global__ __launch_bounds__(256, 2) void k_hq_k28(const uint16_t* __restrict__ x, int64_t T,
+__global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uint16_t* __restrict__ x, int64_t T,
                                                    int64_t ld, const int8_t* __restrict__ signs,
                                                    float c, float clip, uint8_t* __restrict__ q,
                                                    uint16_t* __restrict__ scale,
@@ -551,6 +587,7 @@ __global__ __launch_bounds__(256, 2) void k_hq_k28(const uint16_t* __restrict__ 
   constexpr int D = 28672;
   __shared__ v8h s_afrag[K28_AFRAG];           // 28 KB
   __shared__ float s_x[K28_XROUND];            // 28 KB, also the packed-row stage
+  __shared__ v4u s_sbits[4 * 4 * 64];         // 16 KB
   __shared__ float s_red[4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -581,9 +618,11 @@ __global__ __launch_bounds__(256, 2) void k_hq_k28(const uint16_t* __restrict__ 
   // Signs of the lane's B fragments (the same for every row), one dword per
   // fragment: bit 15 - j holds the sign of element 2 j, bit 31 - j that of
   // element 2 j + 1, so (E << j) & 0x80008000 is the sign-bit mask of dword j.
-  uint32_t sbits[4][4];
+  // Kept in LDS ([w][ct][lane][kb]) and read once per row: held in registers
+  // they would be recomputed from the sign vector on every row.
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+  for (int ct = 0; ct < 4; ++ct) {
+    v4u ev;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int G = (w * 4 + ct) * 16 + gc;
@@ -595,8 +634,10 @@ __global__ __launch_bounds__(256, 2) void k_hq_k28(const uint16_t* __restrict__ 
           e |= (signs[e0 + 2 * j] < 0 ? (0x8000u >> j) : 0u) |
                (signs[e0 + 2 * j + 1] < 0 ? (0x80000000u >> j) : 0u);
       }
-      sbits[ct][kb] = e;
+      ev[kb] = e;
     }
+    s_sbits[(w * 4 + ct) * 64 + lane] = ev;
+  }
   const float s0 = (gc & 1) ? -1.0f : 1.0f;
   const float s1 = (gc & 2) ? -1.0f : 1.0f;
   const float s2 = (gc & 4) ? -1.0f : 1.0f;
@@ -612,16 +653,17 @@ __global__ __launch_bounds__(256, 2) void k_hq_k28(const uint16_t* __restrict__ 
     for (int ct = 0; ct < 4; ++ct) {
       const int G = (w * 4 + ct) * 16 + gc;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        if (kb < 3 || g < 2) {
-          v4u raw = *(const v4u*)(xr + G * 112 + 32 * kb + 8 * g);
+      for (int kb = 0; kb < 4; ++kb)
+        braw[ct][kb] = (kb < 3 || g < 2) ? ld_stream(xr + G * 112 + 32 * kb + 8 * g)
+                                         : v4u{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) raw[j] ^= (sbits[ct][kb] << j) & 0x80008000u;
-          braw[ct][kb] = raw;
-        } else {
-          braw[ct][kb] = v4u{0u, 0u, 0u, 0u};
-        }
-      }
+    for (int ct = 0; ct < 4; ++ct) {
+      const v4u ev = s_sbits[(w * 4 + ct) * 64 + lane];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) braw[ct][kb][j] ^= (ev[kb] << j) & 0x80008000u;
     }
     // ---- H_112 on the matrix cores ----
     float v[4][28];
@@ -644,11 +686,19 @@ __global__ __launch_bounds__(256, 2) void k_hq_k28(const uint16_t* __restrict__ 
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[ct][4 * mt + r] = accm[ct][r];
     }
-    // keep a compiler-visible VALU op between the MFMA results and the DPP asm
+    // ---- H_4 over ct: butterflies between registers (first, so that plain VALU
+    //      ops and not the DPP asm consume the MFMA results) ----
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+    for (int hb = 1; hb < 4; hb <<= 1)
 #pragma unroll
-      for (int k = 0; k < 28; ++k) v[ct][k] = __fadd_rn(v[ct][k], 0.0f);
+      for (int ct = 0; ct < 4; ++ct)
+        if (!(ct & hb))
+#pragma unroll
+          for (int k = 0; k < 28; ++k) {
+            const float a = v[ct][k], b = v[ct + hb][k];
+            v[ct][k] = a + b;
+            v[ct + hb][k] = a - b;
+          }
     // ---- H_16 over gmap(n): DPP butterflies across lanes ----
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -691,18 +741,6 @@ __global__ __launch_bounds__(256, 2) void k_hq_k28(const uint16_t* __restrict__ 
         }
       }
     }
-    // ---- H_4 over ct: butterflies between registers ----
-#pragma unroll
-    for (int hb = 1; hb < 4; hb <<= 1)
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        if (!(ct & hb))
-#pragma unroll
-          for (int k = 0; k < 28; ++k) {
-            const float a = v[ct][k], b = v[ct + hb][k];
-            v[ct][k] = a + b;
-            v[ct + hb][k] = a - b;
-          }
     // ---- H_4 over the wavefront index through LDS; afterwards v[w''][k] holds
     //      chunk 4 G + g, G = (4 w'' + w) 16 + gmap(n), position k ----
     float o[4][28];
@@ -773,7 +811,7 @@ __global__ __launch_bounds__(256, 2) void k_hq_k28(const uint16_t* __restrict__ 
       __syncthreads();
       const uint32_t* st32 = (const uint32_t*)s_x;
       uint32_t* qr32 = (uint32_t*)(q + row * (D / 2));
-      for (int i = tid; i < D / 8; i += 256) qr32[i] = st32[i];
+      for (int i = tid; i < D / 8; i += 256) st_stream(qr32 + i, st32[i]);
       if (tid == 0) scale[row] = sh;
       __syncthreads();  // the stage aliases the next row's exchange buffer
     } else {
@@ -813,7 +851,10 @@ template <int MODE, bool CLAMP>
 static qr_status launch_pow2(int nb, const uint16_t* x, int64_t T, int64_t ld, const int8_t* s,
                              float c, float clip, uint8_t* q, uint16_t* sc, float* z, void* y,
                              hipStream_t st) {
-  const int grid = grid_for(T, 4, 2048);
+#ifndef QR_POW2_GRID
+#define QR_POW2_GRID 1024
+#endif
+  const int grid = grid_for(T, 4, QR_POW2_GRID);
   switch (nb) {
 #define QR_CASE(NBV)                                                                   \
   case NBV:                                                                            \
@@ -894,7 +935,10 @@ static qr_status dispatch(const void* x_f16, int64_t T, int32_t d, int64_t ld, i
     return launch_small<MODE, CLAMP>(d, 1, x, T, ld, signs, c, clip, qq, ss, z, y, st);
   }
   if (m == 28 && n == 10) {
-    const int grid = grid_for(T, 1, 512);
+#ifndef QR_K28_GRID
+#define QR_K28_GRID 512
+#endif
+    const int grid = grid_for(T, 1, QR_K28_GRID);
     hipLaunchKernelGGL((k_hq_k28<MODE, CLAMP>), dim3(grid), dim3(256), 0, st, x, T, ld, signs, c,
                        clip, qq, ss, z, y);
     return launch_status();
