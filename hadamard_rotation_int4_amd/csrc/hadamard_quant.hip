@@ -838,6 +838,250 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
 }
 
 // ===========================================================================
+// k_hq_k172: d = 64 * 172 = 11008, one workgroup of 4 wavefronts per row
+// ===========================================================================
+// The row is a [64 chunks x 172] matrix; z = (H_64 (x) H_172) (s * x).  H_172,
+// a dense +-1 contraction on every chunk, runs on the matrix cores
+// (v_mfma_f32_16x16x32_f16) on the sign-flipped fp16 input: B column n is
+// chunk a = 16 ct + gmap(n), K = 172 padded to 6 blocks of 32, and the 11
+// output tiles of 16 rows (172 padded to 176) are split over the wavefronts
+// (tiles w, w + 4, w + 8).  Every wavefront therefore sees every chunk, so
+// H_64 over the chunk index stays inside it: four DPP stages across lanes and
+// two between its column-tile registers.  Lane (n, g) of tile mt holds chunk
+// positions 16 mt + 4 g .. + 3, i.e. two bytes of packed codes per (mt, ct),
+// staged in LDS for coalesced row stores.
+constexpr int K172_AFRAG = 11 * 6 * 64;  // A fragments [mt][kb][lane], 8 fp16 each: 66 KB
+
+// H_172 in MFMA A-fragment layout, built at compile time: tile mt row i ->
+// output 16 mt + i, block kb lane (i, g) -> columns 32 kb + 8 g .. + 7; +-1 as
+// fp16 bit patterns, zero past 171 in either index.
+struct H172Frags {
+  uint16_t v[K172_AFRAG][8];
+};
+constexpr H172Frags make_h172_frags() {
+  H172Frags f{};
+  const HTable<172> h = make_h172();
+  for (int idx = 0; idx < K172_AFRAG; ++idx) {
+    const int fl = idx & 63, mk = idx >> 6;
+    const int mt = mk / 6, kb = mk % 6;
+    const int o = 16 * mt + (fl & 15), gg = fl >> 4;
+    for (int j = 0; j < 8; ++j) {
+      const int col = 32 * kb + 8 * gg + j;
+      uint16_t bits = 0;
+      if (o < 172 && col < 172) bits = h.v[o][col] > 0.0f ? 0x3C00u : 0xBC00u;
+      f.v[idx][j] = bits;
+    }
+  }
+  return f;
+}
+__device__ const H172Frags g_h172_frags = make_h172_frags();
+
+template <int MODE, bool CLAMP>
+__global__ __launch_bounds__(256, 2) void k_hq_k172(const uint16_t* __restrict__ x, int64_t T,
+                                                    int64_t ld, const int8_t* __restrict__ signs,
+                                                    float c, float clip, uint8_t* __restrict__ q,
+                                                    uint16_t* __restrict__ scale,
+                                                    float* __restrict__ zdbg,
+                                                    void* __restrict__ yout) {
+  constexpr int D = 11008;
+  __shared__ uint32_t s_sbits[4 * 6 * 64];  // [ct][kb][lane]
+  __shared__ uint16_t s_stage[D / 4];        // packed row: 5504 bytes
+  __shared__ float s_red[4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int gc = gmap(n);
+  const v8h* afrag = (const v8h*)&g_h172_frags.v[0][0];  // read through the caches each row
+
+  // Sign words of the B fragments, as in k_hq_k28: bit 15 - j / 31 - j hold the
+  // signs of elements 2 j / 2 j + 1 of the fragment.
+  for (int f = tid; f < 4 * 6 * 64; f += 256) {
+    const int fl = f & 63, ck = f >> 6;
+    const int ct = ck / 6, kb = ck % 6;
+    const int a = 16 * ct + gmap(fl & 15), gg = fl >> 4;
+    uint32_t e = 0u;
+    if (signs) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int col = 32 * kb + 8 * gg + j;
+        if (col < 172 && signs[a * 172 + col] < 0) e |= (j & 1) ? (0x80000000u >> (j >> 1)) : (0x8000u >> (j >> 1));
+      }
+    }
+    s_sbits[f] = e;
+  }
+  const float s0 = (gc & 1) ? -1.0f : 1.0f;
+  const float s1 = (gc & 2) ? -1.0f : 1.0f;
+  const float s2 = (gc & 4) ? -1.0f : 1.0f;
+  const float s3 = (gc & 8) ? -1.0f : 1.0f;
+  const float sigma = (__builtin_popcount(gc) & 1) ? -1.0f : 1.0f;  // lane holds sigma * z
+  const int nmt = (w < 3) ? 3 : 2;  // tiles w, w + 4, w + 8 (< 11)
+  __syncthreads();
+
+  for (int64_t row = blockIdx.x; row < T; row += gridDim.x) {
+    const uint16_t* xr = x + row * ld;
+    // ---- B fragments (every wavefront reads the whole row) ----
+    v4u b[4][6];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int a = 16 * ct + gc;
+#pragma unroll
+      for (int kb = 0; kb < 6; ++kb) {
+        const int col = 32 * kb + 8 * g;
+        v4u raw = {0u, 0u, 0u, 0u};
+        if (col + 8 <= 172) {
+          raw = ld_stream(xr + a * 172 + col);
+        } else if (col < 172) {  // 168 .. 171
+          const uint2 h = *(const uint2*)(xr + a * 172 + col);
+          raw[0] = h.x;
+          raw[1] = h.y;
+        }
+        const uint32_t e = s_sbits[(ct * 6 + kb) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw[j] ^= (e << j) & 0x80008000u;
+        b[ct][kb] = raw;
+      }
+    }
+    // ---- H_172 on the matrix cores: v[t][ct][r] = output 16 (w + 4 t) + 4 g + r ----
+    float v[3][4][4];
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      if (t < nmt) {
+        const int mt = w + 4 * t;
+        v4f acc[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < 6; ++kb) {
+          const v8h a = afrag[(mt * 6 + kb) * 64 + lane];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(v8h, b[ct][kb]),
+                                                             acc[ct], 0, 0, 0);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[t][ct][r] = acc[ct][r];
+      } else {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[t][ct][r] = 0.0f;
+      }
+    }
+    // ---- H_4 over ct between registers (plain VALU consumes the MFMA results) ----
+#pragma unroll
+    for (int hb = 1; hb < 4; hb <<= 1)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        if (!(ct & hb))
+#pragma unroll
+          for (int t = 0; t < 3; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float p = v[t][ct][r], m = v[t][ct + hb][r];
+              v[t][ct][r] = p + m;
+              v[t][ct + hb][r] = p - m;
+            }
+    // ---- H_16 over gmap(n): DPP butterflies across lanes, 8 registers per call ----
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int c2 = 0; c2 < 4; c2 += 2) {
+        float r8[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          r8[r] = v[t][c2][r];
+          r8[4 + r] = v[t][c2 + 1][r];
+        }
+        QR_DPP8("quad_perm:[1,0,3,2]", r8, s0);
+        QR_DPP8("quad_perm:[2,3,0,1]", r8, s1);
+        QR_DPP8("row_half_mirror", r8, s2);
+        QR_DPP8("row_mirror", r8, s3);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[t][c2][r] = r8[r];
+          v[t][c2 + 1][r] = r8[4 + r];
+        }
+      }
+    // element index of v[t][ct][0]: chunk 16 ct + gc, position 16 (w + 4 t) + 4 g
+    auto elem_of = [&](int t, int ct) { return (16 * ct + gc) * 172 + 16 * (w + 4 * t) + 4 * g; };
+    auto valid = [&](int t) { return t < nmt && 16 * (w + 4 * t) + 4 * g < 172; };
+
+    if (zdbg) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        if (valid(t))
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            *(v4f*)(zdbg + row * D + elem_of(t, ct)) =
+                v4f{v[t][ct][0] * sigma, v[t][ct][1] * sigma, v[t][ct][2] * sigma, v[t][ct][3] * sigma};
+    }
+    if (MODE == MODE_QUANT) {
+      float am = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(v[t][ct][r]));
+      am = wave_max(am);
+      if (lane == 0) s_red[w] = am;
+      __syncthreads();
+      am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+      uint16_t sh;
+      float m;
+      sym_scale(am, c, clip, &sh, &m);
+      const float ml = m * sigma;
+      const bool clamp = CLAMP || (sh & 0x7fffu) < 0x0400u;  // block-uniform
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        if (valid(t))
+#pragma unroll
+          for (int ct = 0; ct < 4; ct += 2) {
+            float e8[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              e8[r] = v[t][ct][r];
+              e8[4 + r] = v[t][ct + 1][r];
+            }
+            const uint32_t word = clamp ? quant_pack8<true>(e8, ml) : quant_pack8<false>(e8, ml);
+            s_stage[elem_of(t, ct) / 4] = (uint16_t)(word & 0xffffu);
+            s_stage[elem_of(t, ct + 1) / 4] = (uint16_t)(word >> 16);
+          }
+      __syncthreads();
+      const uint32_t* st32 = (const uint32_t*)s_stage;
+      uint32_t* qr32 = (uint32_t*)(q + row * (D / 2));
+      for (int i = tid; i < D / 8; i += 256) st_stream(qr32 + i, st32[i]);
+      if (tid == 0) scale[row] = sh;
+      __syncthreads();  // stage and s_red are reused by the next row
+    } else {
+      const float cs = c * sigma;
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        if (valid(t))
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const int e0 = elem_of(t, ct);
+            if (MODE == MODE_ROT_F32) {
+              *(v4f*)((float*)yout + row * D + e0) =
+                  v4f{__fmul_rn(v[t][ct][0], cs), __fmul_rn(v[t][ct][1], cs),
+                      __fmul_rn(v[t][ct][2], cs), __fmul_rn(v[t][ct][3], cs)};
+            } else {
+              uint2 o2;
+              o2.x = (uint32_t)f2h(__fmul_rn(v[t][ct][0], cs)) |
+                     ((uint32_t)f2h(__fmul_rn(v[t][ct][1], cs)) << 16);
+              o2.y = (uint32_t)f2h(__fmul_rn(v[t][ct][2], cs)) |
+                     ((uint32_t)f2h(__fmul_rn(v[t][ct][3], cs)) << 16);
+              *(uint2*)((uint16_t*)yout + row * D + e0) = o2;
+            }
+          }
+    }
+  }
+}
+
+// ===========================================================================
 // Host side
 // ===========================================================================
 static int grid_for(int64_t work_items, int per_block, int cap) {
@@ -945,6 +1189,12 @@ static qr_status dispatch(const void* x_f16, int64_t T, int32_t d, int64_t ld, i
   }
   if (m == 28)
     return launch_lds_t<28, MODE, CLAMP, true>(d, n, x, T, ld, signs, c, clip, qq, ss, z, y, st);
+  if (n == 6) {
+    auto kern = k_hq_k172<MODE, CLAMP>;
+    const int grid = grid_for(T, 1, 512);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, x, T, ld, signs, c, clip, qq, ss, z, y);
+    return launch_status();
+  }
   return launch_lds_t<172, MODE, CLAMP, true>(d, n, x, T, ld, signs, c, clip, qq, ss, z, y, st);
 }
 
