@@ -15,11 +15,14 @@
 //    A and W use the same permutation of k, so the dot product is unchanged,
 //    and the int32 accumulator holds 256 * acc exactly (|256 acc| <= 256 * 64 * K
 //    < 2^31 for K <= 131008); the epilogue shifts it back.
-//  * Tiles: 256 x 256 outputs per workgroup of 4 wavefronts (one per SIMD), each
-//    owning a 128 x 128 block = 4 x 4 MFMA tiles whose accumulators live in the
-//    AGPR half of the register file.  K advances 256 at a time through two LDS
-//    stages of 64 KB; the next step's panels are fetched into registers while
-//    the current one is multiplied, and written to the other stage at the end.
+//  * Tiles: (64 WM) x (64 WN) outputs per workgroup of 4 wavefronts (one per
+//    SIMD, 2 x 2), each owning a (32 WM) x (32 WN) block = WM x WN MFMA tiles
+//    whose accumulators live in the AGPR half of the register file.  256 x 256
+//    (WM = WN = 4) is the default; 256 x 128 and 128 x 256 are used when the
+//    big tile would leave compute units idle.  K advances 256 at a time
+//    through two LDS stages; the next step's panels are fetched into
+//    registers while the current one is multiplied, and written to the other
+//    stage at the end.
 //  * Each lane reads whole 16-byte k-chunks (32 codes) and feeds two MFMAs from
 //    one chunk: lane (row, half h) takes chunk 2p + h for MFMA steps 2p and
 //    2p + 1, identically for A and W, so every k is summed exactly once.  The
@@ -40,13 +43,9 @@
 
 namespace qr {
 
-constexpr int BM = 256, BN = 256, BK = 256;  // BK in int4 elements (128 bytes per row)
-constexpr int KCH = BK / 32;                 // 16-byte k-chunks per row and step
+constexpr int BK = 256;            // K step in int4 elements (128 bytes per row)
+constexpr int KCH = BK / 32;       // 16-byte k-chunks per row and step
 constexpr int GEMM_THREADS = 256;
-constexpr int OPER_BYTES = BM * BK / 2;      // one operand's panel per step: 32 KB
-constexpr int STAGE_BYTES = 2 * OPER_BYTES;  // A + W: 64 KB
-constexpr int GEMM_LDS = 2 * STAGE_BYTES;    // two stages: 128 KB
-constexpr int PIECES = BM * KCH / GEMM_THREADS;  // 16-byte global pieces per thread and operand
 
 __device__ __forceinline__ v4i unpack16(uint2 d) {
   v4i r;
@@ -57,17 +56,33 @@ __device__ __forceinline__ v4i unpack16(uint2 d) {
   return r;
 }
 
-// LDS byte offset of 16-byte k-chunk `kk` of panel row r (swizzled).
+// LDS byte offset of 16-byte k-chunk `kk` of row r of a ROWS-row panel (swizzled).
+template <int ROWS>
 __device__ __forceinline__ int lds_off(int kk, int r) {
   const int f = (kk << 1) | (__builtin_popcount(kk) & 1);
-  return kk * 4096 + ((r ^ f) << 4);
+  return kk * (ROWS * 16) + ((r ^ f) << 4);
 }
 
-template <bool DBG, bool KTAIL>
+template <int WM, int WN>
+struct GemmTile {
+  static constexpr int BM = 64 * WM, BN = 64 * WN;
+  static constexpr int A_BYTES = BM * BK / 2, W_BYTES = BN * BK / 2;
+  static constexpr int STAGE = A_BYTES + W_BYTES;
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int PA = BM * KCH / GEMM_THREADS, PW = BN * KCH / GEMM_THREADS;
+  static constexpr int MF = WM * WN;                      // MFMAs per half step
+  static constexpr int VPM = (6 * (WM + WN) + MF - 1) / MF;  // unpack VALU per MFMA
+  static constexpr int DSR = WM + WN;                     // fragment reads per pair
+  static constexpr int SPM = (PA + PW + MF - 1) / MF;     // staging writes/loads per MFMA
+};
+
+template <int WM, int WN, bool DBG, bool KTAIL>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
     const uint8_t* __restrict__ A, const uint16_t* __restrict__ a_scale, int T,
     const uint8_t* __restrict__ W, const uint16_t* __restrict__ w_scale, int N, int K,
     uint16_t* __restrict__ Y, int32_t* __restrict__ acc_dbg, int tiles_m, int tiles_n) {
+  using Tl = GemmTile<WM, WN>;
+  constexpr int BM = Tl::BM, BN = Tl::BN;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   // ---- tile assignment (XCD-aware, grouped) ----
@@ -86,14 +101,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;  // wave's block inside the tile
-  const int li = lane & 31, lg = lane >> 5;                  // MFMA row/col lane, k-half
+  const int wm = (wave >> 1) * (32 * WM), wn = (wave & 1) * (32 * WN);  // wave's block
+  const int li = lane & 31, lg = lane >> 5;  // MFMA row/col lane, k-half
   const int64_t rowbytes = K / 2;
 
-  // ---- global -> register staging: PIECES x 16 B of A and of W per thread ----
-  // piece id = tid + 256 j: row = (tid >> 3) + 32 j, k-chunk = tid & 7 (fixed per
-  // thread).  Raw buffer loads over the tile's own rows: rows past T (or N)
-  // fall outside the buffer's range and read as zero.
+  // ---- global -> register staging: 16-byte pieces, row = (tid >> 3) + 32 j,
+  //      k-chunk = tid & 7 (fixed per thread).  Raw buffer loads over the tile's
+  //      own rows: rows past T (or N) fall outside the buffer's range and read
+  //      as zero. ----
   const int st_kk = tid & (KCH - 1);
   const int st_r0 = tid / KCH;
   const int rows_a = min(T - m0, BM), rows_w = min(N - n0, BN);
@@ -103,51 +118,50 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
       (void*)(W + (int64_t)n0 * rowbytes), 0, (int)(rows_w * rowbytes), 0x00020000);
   const int voff = st_r0 * (int)rowbytes + st_kk * 16;
   const int rstep = (GEMM_THREADS / KCH) * (int)rowbytes;
-  v4u ra[PIECES], rw[PIECES];
+  v4u ra[Tl::PA], rw[Tl::PW];
   auto gload = [&](int k0, bool last) {  // k0 in elements
+    // the whole offset goes in the VGPR operand: the range check of a raw
+    // buffer covers the VGPR offset, not the SGPR one
 #pragma unroll
-    for (int j = 0; j < PIECES; ++j) {
-      // the whole offset goes in the VGPR operand: the range check of a raw
-      // buffer covers the VGPR offset, not the SGPR one
-      const int off = voff + j * rstep + k0 / 2;
-      ra[j] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, off, 0, 0));
-      rw[j] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_w, off, 0, 0));
-    }
+    for (int j = 0; j < Tl::PA; ++j)
+      ra[j] = __builtin_bit_cast(
+          v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff + j * rstep + k0 / 2, 0, 0));
+#pragma unroll
+    for (int j = 0; j < Tl::PW; ++j)
+      rw[j] = __builtin_bit_cast(
+          v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_w, voff + j * rstep + k0 / 2, 0, 0));
     if (KTAIL && last && k0 + st_kk * 32 >= K) {  // chunk past K (K is a multiple of 32)
 #pragma unroll
-      for (int j = 0; j < PIECES; ++j) {
-        ra[j] = v4u{0u, 0u, 0u, 0u};
-        rw[j] = v4u{0u, 0u, 0u, 0u};
-      }
+      for (int j = 0; j < Tl::PA; ++j) ra[j] = v4u{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < Tl::PW; ++j) rw[j] = v4u{0u, 0u, 0u, 0u};
     }
   };
   auto lstore = [&](int stage) {
-    uint8_t* pa = smem + stage * STAGE_BYTES;
-    uint8_t* pw = pa + OPER_BYTES;
+    uint8_t* pa = smem + stage * Tl::STAGE;
+    uint8_t* pw = pa + Tl::A_BYTES;
 #pragma unroll
-    for (int j = 0; j < PIECES; ++j) {
-      const int r = st_r0 + (GEMM_THREADS / KCH) * j;
-      *(v4u*)(pa + lds_off(st_kk, r)) = ra[j];
-      *(v4u*)(pw + lds_off(st_kk, r)) = rw[j];
-    }
+    for (int j = 0; j < Tl::PA; ++j) *(v4u*)(pa + lds_off<BM>(st_kk, st_r0 + 32 * j)) = ra[j];
+#pragma unroll
+    for (int j = 0; j < Tl::PW; ++j) *(v4u*)(pw + lds_off<BN>(st_kk, st_r0 + 32 * j)) = rw[j];
   };
-  // packed fragments of chunk pair p (lane takes chunk 2p + lg): 4 of A
-  // (rows wm + 32 i + li) and 4 of W
+  // packed fragments of chunk pair p (lane takes chunk 2p + lg): WM of A
+  // (rows wm + 32 i + li) and WN of W
   auto lread = [&](int stage, int p, v4u* fa, v4u* fb) {
-    const uint8_t* pa = smem + stage * STAGE_BYTES;
-    const uint8_t* pw = pa + OPER_BYTES;
+    const uint8_t* pa = smem + stage * Tl::STAGE;
+    const uint8_t* pw = pa + Tl::A_BYTES;
     const int kk = 2 * p + lg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = *(const v4u*)(pa + lds_off(kk, wm + i * 32 + li));
+    for (int i = 0; i < WM; ++i) fa[i] = *(const v4u*)(pa + lds_off<BM>(kk, wm + i * 32 + li));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = *(const v4u*)(pw + lds_off(kk, wn + j * 32 + li));
+    for (int j = 0; j < WN; ++j) fb[j] = *(const v4u*)(pw + lds_off<BN>(kk, wn + j * 32 + li));
   };
 
-  v16i acc[4][4];
+  v16i acc[WM][WN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
@@ -155,19 +169,19 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
   // ahead), unpacked halves ua/ub[0] (e = 0) and [1] (e = 1).  While the MFMAs
   // of one half run, the VALU unpacks the other and the LDS reads of the next
   // pair are in flight; sched_group_barrier pins that order.
-  v4u fa[2][4], fb[2][4];
-  v4i ua[2][4], ub[2][4];
+  v4u fa[2][WM], fb[2][WN];
+  v4i ua[2][WM], ub[2][WN];
   auto unpack_half = [&](const v4u* xa, const v4u* xb, int e, v4i* oa, v4i* ob) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) oa[i] = unpack16(make_uint2(xa[i][2 * e], xa[i][2 * e + 1]));
+    for (int i = 0; i < WM; ++i) oa[i] = unpack16(make_uint2(xa[i][2 * e], xa[i][2 * e + 1]));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ob[j] = unpack16(make_uint2(xb[j][2 * e], xb[j][2 * e + 1]));
+    for (int j = 0; j < WN; ++j) ob[j] = unpack16(make_uint2(xb[j][2 * e], xb[j][2 * e + 1]));
   };
-  auto mfma16 = [&](const v4i* a, const v4i* b) {
+  auto mfma_half = [&](const v4i* a, const v4i* b) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < WN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
   };
   constexpr int NP = KCH / 2;  // chunk pairs per step
@@ -183,50 +197,50 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
       if (p + 1 < NP) {
         __builtin_amdgcn_sched_barrier(0);
         lread(stage, p + 1, fa[nxt], fb[nxt]);
-        mfma16(ua[0], ub[0]);
+        mfma_half(ua[0], ub[0]);
         unpack_half(fa[cur], fb[cur], 1, ua[1], ub[1]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 8 DS reads first
+        __builtin_amdgcn_sched_group_barrier(0x100, Tl::DSR, 0);  // DS reads first
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
+        for (int m = 0; m < Tl::MF; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, Tl::VPM, 0);  // VALU
         }
         __builtin_amdgcn_sched_barrier(0);
-        mfma16(ua[1], ub[1]);
+        mfma_half(ua[1], ub[1]);
         unpack_half(fa[nxt], fb[nxt], 0, ua[0], ub[0]);
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
+        for (int m = 0; m < Tl::MF; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, Tl::VPM, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       } else {
         __builtin_amdgcn_sched_barrier(0);
-        mfma16(ua[0], ub[0]);
+        mfma_half(ua[0], ub[0]);
         unpack_half(fa[cur], fb[cur], 1, ua[1], ub[1]);
         if (MORE) {
           lstore(stage ^ 1);
           gload(min(ks + 2, ksteps - 1) * BK, ks + 3 >= ksteps);
 #pragma unroll
-          for (int m = 0; m < 16; ++m) {
+          for (int m = 0; m < Tl::MF; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 2);
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 2);  // 1 DS write
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 2);  // 1 VMEM read
+            __builtin_amdgcn_sched_group_barrier(0x002, Tl::VPM, 2);
+            __builtin_amdgcn_sched_group_barrier(0x200, Tl::SPM, 2);  // DS writes
+            __builtin_amdgcn_sched_group_barrier(0x020, Tl::SPM, 2);  // VMEM reads
           }
           __builtin_amdgcn_sched_barrier(0);
           __syncthreads();
           lread(stage ^ 1, 0, fa[nxt], fb[nxt]);
-          mfma16(ua[1], ub[1]);
+          mfma_half(ua[1], ub[1]);
           unpack_half(fa[nxt], fb[nxt], 0, ua[0], ub[0]);
-          __builtin_amdgcn_sched_group_barrier(0x100, 8, 3);
+          __builtin_amdgcn_sched_group_barrier(0x100, Tl::DSR, 3);
 #pragma unroll
-          for (int m = 0; m < 16; ++m) {
+          for (int m = 0; m < Tl::MF; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 3);
+            __builtin_amdgcn_sched_group_barrier(0x002, Tl::VPM, 3);
           }
         } else {
-          mfma16(ua[1], ub[1]);
+          mfma_half(ua[1], ub[1]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -244,20 +258,20 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
 
   // ---- epilogue: 32x32 accumulator layout: lane (n = li, k-half lg), register r
   //      holds row 8 (r / 4) + 4 lg + (r % 4) ----
-  float wsc[4];
+  float wsc[WN];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) wsc[j] = h2f(w_scale[min(n0 + wn + j * 32 + li, N - 1)]);
+  for (int j = 0; j < WN; ++j) wsc[j] = h2f(w_scale[min(n0 + wn + j * 32 + li, N - 1)]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < WM; ++i) {
     float asc[16];  // [r]: rows 8 (r / 4) + 4 lg + (r % 4) of block i
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int t0 = m0 + wm + i * 32 + 8 * q + 4 * lg;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int t0 = m0 + wm + i * 32 + 8 * q4 + 4 * lg;
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) asc[4 * q + s2] = h2f(a_scale[min(t0 + s2, T - 1)]);
+      for (int s2 = 0; s2 < 4; ++s2) asc[4 * q4 + s2] = h2f(a_scale[min(t0 + s2, T - 1)]);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < WN; ++j) {
       const int n = n0 + wn + j * 32 + li;
       if (n >= N) continue;
 #pragma unroll
@@ -273,21 +287,151 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
   }
 }
 
-template <bool DBG, bool KTAIL>
+template <int WM, int WN, bool DBG, bool KTAIL>
 static qr_status launch_gemm(const void* a_q, const void* a_scale, int64_t T, const void* w_q,
                              const void* w_scale, int64_t N, int64_t K, void* y, int32_t* acc,
-                             int tiles_m, int tiles_n, hipStream_t stream) {
-  auto kern = k_w4a4_gemm<DBG, KTAIL>;
+                             hipStream_t stream) {
+  using Tl = GemmTile<WM, WN>;
+  auto kern = k_w4a4_gemm<WM, WN, DBG, KTAIL>;
   // Opting in to more than 64 KB of LDS is a per-kernel attribute; setting it
   // again on every call is cheap and keeps the entry point free of state.
   if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          GEMM_LDS) != hipSuccess)
+                          Tl::LDS) != hipSuccess)
     return QR_ERR_LAUNCH;
+  const int tiles_m = (int)((T + Tl::BM - 1) / Tl::BM);
+  const int tiles_n = (int)((N + Tl::BN - 1) / Tl::BN);
   const int64_t nblk = (int64_t)tiles_m * tiles_n;
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(GEMM_THREADS), GEMM_LDS, stream,
+  if (nblk > INT32_MAX) return QR_ERR_SHAPE;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(GEMM_THREADS), Tl::LDS, stream,
                      (const uint8_t*)a_q, (const uint16_t*)a_scale, (int)T, (const uint8_t*)w_q,
                      (const uint16_t*)w_scale, (int)N, (int)K, (uint16_t*)y, acc, tiles_m,
                      tiles_n);
+  return launch_status();
+}
+
+template <int WM, int WN>
+static qr_status launch_tile(const void* a_q, const void* a_scale, int64_t T, const void* w_q,
+                             const void* w_scale, int64_t N, int64_t K, void* y, int32_t* acc,
+                             hipStream_t stream) {
+  const bool tail = (K % BK) != 0;
+  if (acc)
+    return tail ? launch_gemm<WM, WN, true, true>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream)
+                : launch_gemm<WM, WN, true, false>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
+  return tail ? launch_gemm<WM, WN, false, true>(a_q, a_scale, T, w_q, w_scale, N, K, y, nullptr, stream)
+              : launch_gemm<WM, WN, false, false>(a_q, a_scale, T, w_q, w_scale, N, K, y, nullptr, stream);
+}
+
+// Fraction of the machine's workgroup slots a tile grid keeps busy, times a
+// per-tile efficiency (smaller tiles re-read more operand bytes per MAC).
+static double tile_score(int64_t T, int64_t N, int bm, int bn, double eff, int slots) {
+  const int64_t tiles = ((T + bm - 1) / bm) * ((N + bn - 1) / bn);
+  const int64_t rounds = (tiles + slots - 1) / slots;
+  return eff * (double)tiles / (double)(rounds * slots);
+}
+
+
+// ===========================================================================
+// Decode (T <= 64): weight-streaming GEMM
+// ===========================================================================
+// With a handful of tokens the product is bound by reading W once.  A
+// workgroup owns 16 output channels (one MFMA column block) and all T <= 64
+// tokens (up to 4 MFMA row blocks); its 4 wavefronts split K in 128-element
+// blocks and each streams its part of the 16 weight rows exactly once with
+// v_mfma_i32_16x16x64_i8.  Lane (row i, group g) of a block holds packed
+// bytes 16 g .. 16 g + 15 (k = 32 g .. 32 g + 31) and feeds two MFMAs, one per
+// 8-byte half, identically for A and W.  The four partial accumulators are
+// summed through LDS and wavefront 0 applies the fp32 epilogue.  N / 16
+// workgroups: 256 to 768 for the Llama-2 projections.
+constexpr int DEC_BN = 16;
+
+template <int MT, bool DBG>
+__global__ __launch_bounds__(256) void k_w4a4_decode(
+    const uint8_t* __restrict__ A, const uint16_t* __restrict__ a_scale, int T,
+    const uint8_t* __restrict__ W, const uint16_t* __restrict__ w_scale, int N, int K,
+    uint16_t* __restrict__ Y, int32_t* __restrict__ acc_dbg) {
+  __shared__ v4i s_part[3][MT][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * DEC_BN;
+  const int rowbytes = K / 2;
+  // Rows past T (tokens) or N (channels) are outside the buffers' ranges and read as zero.
+  const __amdgpu_buffer_rsrc_t rsrc_a =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, T * rowbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_w = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (int64_t)n0 * rowbytes), 0, min(N - n0, DEC_BN) * rowbytes, 0x00020000);
+  const int kblocks = (K + 127) / 128;
+  const int per = (kblocks + 3) / 4;
+  const int kb0 = wave * per, kb1 = min(kblocks, kb0 + per);
+
+  v4i acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = v4i{0, 0, 0, 0};
+#pragma unroll 4
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const int byte = kb * 64 + 16 * g;  // this lane's 16 bytes of the block
+    const bool inside = byte < rowbytes;  // K % 128 == 64: the last block is half full
+    v4u wv = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_w, i * rowbytes + byte, 0, 0));
+    v4u av[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      av[m] = __builtin_bit_cast(
+          v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, (16 * m + i) * rowbytes + byte, 0, 0));
+    if (!inside) {
+      wv = v4u{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int m = 0; m < MT; ++m) av[m] = v4u{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const v4i b = unpack16(make_uint2(wv[2 * e], wv[2 * e + 1]));
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        acc[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            unpack16(make_uint2(av[m][2 * e], av[m][2 * e + 1])), b, acc[m], 0, 0, 0);
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) s_part[wave - 1][m][lane] = acc[m];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int w2 = 0; w2 < 3; ++w2) acc[m] += s_part[w2][m][lane];
+  // 16x16 accumulator layout: lane (col i, group g), register r -> row 4 g + r
+  const int n = n0 + i;
+  if (n >= N) return;
+  const float ws = h2f(w_scale[n]);
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * m + 4 * g + r;
+      if (t < T) {
+        const int32_t a = acc[m][r] >> 8;  // exact: the accumulator is 256 * acc
+        Y[(int64_t)t * N + n] = f2h(__fmul_rn(__fmul_rn((float)a, h2f(a_scale[t])), ws));
+        if (DBG) acc_dbg[(int64_t)t * N + n] = a;
+      }
+    }
+}
+
+template <int MT>
+static qr_status launch_decode(const void* a_q, const void* a_scale, int64_t T, const void* w_q,
+                               const void* w_scale, int64_t N, int64_t K, void* y, int32_t* acc,
+                               hipStream_t stream) {
+  const int64_t blocks = (N + DEC_BN - 1) / DEC_BN;
+  if (acc)
+    hipLaunchKernelGGL((k_w4a4_decode<MT, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint8_t*)a_q, (const uint16_t*)a_scale, (int)T, (const uint8_t*)w_q,
+                       (const uint16_t*)w_scale, (int)N, (int)K, (uint16_t*)y, acc);
+  else
+    hipLaunchKernelGGL((k_w4a4_decode<MT, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint8_t*)a_q, (const uint16_t*)a_scale, (int)T, (const uint8_t*)w_q,
+                       (const uint16_t*)w_scale, (int)N, (int)K, (uint16_t*)y, (int32_t*)nullptr);
   return launch_status();
 }
 
@@ -306,18 +450,22 @@ extern "C" qr_status qr_w4a4_gemm(const void* a_q, const void* a_scale_f16, int6
   if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(y_f16, 4) || !aligned(a_scale_f16, 2) ||
       !aligned(w_scale_f16, 2) || (acc_dbg && !aligned(acc_dbg, 4)))
     return QR_ERR_ALIGN;
-  const int tiles_m = (int)((T + BM - 1) / BM);
-  const int tiles_n = (int)((N + BN - 1) / BN);
-  const int64_t nblk = (int64_t)tiles_m * tiles_n;
-  if (nblk > INT32_MAX) return QR_ERR_SHAPE;
-  const bool tail = (K % BK) != 0;
-  if (acc_dbg)
-    return tail ? launch_gemm<true, true>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16,
-                                          acc_dbg, tiles_m, tiles_n, stream)
-                : launch_gemm<true, false>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16,
-                                           acc_dbg, tiles_m, tiles_n, stream);
-  return tail ? launch_gemm<false, true>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16,
-                                         nullptr, tiles_m, tiles_n, stream)
-              : launch_gemm<false, false>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16,
-                                          nullptr, tiles_m, tiles_n, stream);
+  if (T <= 64 && (int64_t)T * (K / 2) <= INT32_MAX && N <= INT32_MAX / 2) {
+    if (T <= 16)
+      return launch_decode<1>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
+    if (T <= 32)
+      return launch_decode<2>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
+    return launch_decode<4>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
+  }
+  // One workgroup per compute unit at a time (the accumulators fill the
+  // register file): pick the tile whose grid keeps the 256 CUs busiest.
+  constexpr int kSlots = 256;
+  const double s44 = tile_score(T, N, 256, 256, 1.0, kSlots);
+  const double s42 = tile_score(T, N, 256, 128, 0.9, kSlots);
+  const double s24 = tile_score(T, N, 128, 256, 0.9, kSlots);
+  if (s44 >= s42 && s44 >= s24)
+    return launch_tile<4, 4>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
+  if (s42 >= s24)
+    return launch_tile<4, 2>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
+  return launch_tile<2, 4>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
 }

@@ -29,8 +29,20 @@ def run(ap, asc, wp, wsc):
 SHAPES = [(1, 1, 64), (7, 100, 128), (300, 260, 192), (33, 17, 4096), (256, 256, 256),
           (513, 300, 1024), (64, 640, 11008), (257, 513, 320), (2, 4096, 128)]
 
+# Shapes that steer the entry point to each of its kernels (it picks the tile
+# whose grid keeps the 256 compute units busiest; T <= 64 streams the weights):
+#   (4096, 4096, 512)  -> 256 x 256 tiles (256 tiles fill the machine once)
+#   (2048, 4096, 512)  -> 256 x 128 tiles (128 big tiles would idle half of it)
+#   (640, 384, 256)    -> 128 x 256 tiles (more tiles than 256 x 128 gives)
+#   (1 | 8 | 32 | 64, ...) -> weight-streaming kernel with 1, 1, 2, 4 row blocks,
+#   at the Llama-2-7B decode widths, including K = 11008 (K % 128 == 0) and
+#   K = 4160 (a final half block of 64).
+KERNEL_SHAPES = [(4096, 4096, 512), (2048, 4096, 512), (640, 384, 256), (1, 12288, 4096),
+                 (8, 4096, 4096), (32, 11008, 4096), (64, 4096, 11008), (17, 100, 4160),
+                 (64, 33, 64)]
 
-@pytest.mark.parametrize("T,N,K", SHAPES)
+
+@pytest.mark.parametrize("T,N,K", SHAPES + KERNEL_SHAPES)
 def test_random_codes_bit_exact(T, N, K):
     ap = wl.packed_codes(1, 0, T, K)
     wp = wl.packed_codes(1, 1, N, K)
