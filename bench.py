@@ -1,25 +1,41 @@
 """Benchmark of the QuaRot online-rotation + INT4 hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 70b_prefill|7b_prefill]
-                    [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload 70b_prefill|7b_prefill|7b_decode|70b_kv]
+                    [--no-cpu-baseline] [--copy-calibration]
 
 One step is one pass of the whole hot path over one batch of synthetic input
-(inputs already resident in HBM, weights prepared offline and not timed):
-  * fused Hadamard rotation + per-token INT4 quantization of the four GEMM
-    inputs of a Llama-2 block (attention input, attention output, FFN input --
-    shared by gate and up -- and the down-projection input, d = K of its GEMM);
-  * the five W4A4 GEMMs (QKV, O, gate, up, down) with the scale epilogue;
-  * head-wise Hadamard + asymmetric 4-bit group-128 quantization of K and V
-    into the packed cache (Init of the whole prompt), and the rotation of Q.
-Prints one JSON line (rank 0).  ``value`` is the whole step's throughput in
-TOPS (GEMM int ops per step / step time).  The ``roofline`` object is for the
-dominant kernel (the W4A4 GEMM); ``roofline_hadamard_quant`` is the same for the
-fused rotation + quantization kernel against the HBM roofline.  The
-``cpu_baseline`` is the oracle timed on the host on a bounded sample.
+(inputs resident in HBM; weights prepared offline and not timed):
+
+* prefill (default: Llama-2-70B block, T = 65536 = batch 32 x seq 2048):
+  fused Hadamard rotation + per-token INT4 quantization of the four GEMM inputs
+  (attention input, attention output, FFN input -- shared by gate and up -- and
+  the down-projection input, d = K of its GEMM); the five W4A4 GEMMs (QKV, O,
+  gate, up, down) with the scale epilogue; head-wise Hadamard + asymmetric
+  4-bit group-128 quantization of K and V into the cache (Init of the prompt);
+  the head-wise rotation of Q.
+* 7b_decode: the same four rotations and five GEMMs at T = 1, 8, 32 and 64.
+* 70b_kv: K/V Init of a 32 x 2048-token prompt (8 KV heads of 128), the
+  rotation of its queries (64 heads), then 50 decode steps of Append K, V and
+  rotate one query token.
+
+Prints one JSON line.  ``value`` is the step's GEMM int-ops per second (TOPS)
+for the prefill workloads and its algorithmic HBM bytes per second (GB/s) for
+the memory-bound ones.  ``roofline`` covers the step's dominant kernel;
+``roofline_hadamard_quant`` covers the fused rotation + quantization against
+the HBM roofline.  Each launch is bracketed by HIP events on the stream it runs
+on.  ``traffic`` is read from the committed rocprofv3 counter summary of that
+kernel and workload (profiles/traffic_*.txt) when the kernel source still
+matches the hash recorded there, else null.  ``cpu_baseline`` is the oracle
+timed on the host on a bounded sample.
+
+--copy-calibration runs only a plain device copy of 1 GiB (ten times), the
+reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -33,6 +49,9 @@ sys.path.insert(0, str(ROOT))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POP/s)
 METRIC = "fused Hadamard+INT4-quant HBM GB/s; W4A4 GEMM TOPS at Llama-2 shapes"
+CSRC = ROOT / "hadamard_rotation_int4_amd" / "csrc"
+KERNEL_SOURCE = {"w4a4_gemm": "w4a4_gemm.hip", "hadamard_quant": "hadamard_quant.hip",
+                 "kv_rotate_quant": "kv_quant.hip", "hadamard": "hadamard_quant.hip"}
 
 
 def parse():
@@ -40,15 +59,21 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="70b_prefill", choices=["70b_prefill", "7b_prefill"])
+    ap.add_argument("--workload", default="70b_prefill",
+                    choices=["70b_prefill", "7b_prefill", "7b_decode", "70b_kv"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
 
 
+# ---------------------------------------------------------------------------
+# Algorithmic work per launch (each input read once, each output written once)
+# ---------------------------------------------------------------------------
+
 def hq_bytes(T, d):
-    """Algorithmic HBM bytes of one fused rotate+quant launch: read fp16 x, write
-    packed codes and the fp16 scale (signs are cache resident)."""
+    """Fused rotate + quant: read fp16 x, write packed codes and the fp16 scale
+    (signs and H_m tables are cache resident)."""
     return T * (2 * d + d // 2 + 2)
 
 
@@ -57,20 +82,266 @@ def gemm_ops(T, N, K):
 
 
 def gemm_bytes(T, N, K):
+    """A codes + W codes + both scale vectors + the fp16 output."""
     return T * K // 2 + N * K // 2 + 2 * T + 2 * N + 2 * T * N
 
 
 def kv_bytes(rows, dh, group):
+    """Per (token, head) row: fp16 in, packed codes + fp16 (scale, min) per group out."""
     return rows * (2 * dh + dh // 2 + 4 * (dh // group))
+
+
+def rot_bytes(rows, dh):
+    """Rotation only, fp16 in and out."""
+    return rows * 4 * dh
+
+
+# ---------------------------------------------------------------------------
+# Workload construction: a list of launches (kernel, label, bytes, ops, fn)
+# ---------------------------------------------------------------------------
+
+def make_block(torch, qr, wl, W, T, dev, with_kv):
+    lin = {l.name: l for l in W.linears}
+    H, ffn, wid = W.hidden, lin["down"].k, W.wid
+    inputs = {}
+    for i, name in enumerate(("attn_in", "o_in", "ffn_in", "down_in")):
+        d = ffn if name == "down_in" else H
+        inputs[name] = wl.activations_torch(torch, dev, wid, 10 + i, T, d, W.n_outliers,
+                                            W.outlier_lo, W.outlier_hi)
+    signs = {d: torch.from_numpy(wl.signs(wid, d)).to(dev) for d in (H, ffn)}
+    # weights: random init, rotated by the same R_K and quantized per output
+    # channel with the library's own kernel (offline preparation, not timed)
+    wq = {}
+    for i, (name, l) in enumerate(lin.items()):
+        w = wl.weights_torch(torch, dev, wid, 1 + i, l.n, l.k)
+        wq[name] = qr.hadamard_quant(w, signs[l.k], 1.0)
+        del w
+    qbuf = {n: (torch.empty((T, x.shape[1] // 2), dtype=torch.uint8, device=dev),
+                torch.empty((T,), dtype=torch.float16, device=dev)) for n, x in inputs.items()}
+    ybuf = {n: torch.empty((T, l.n), dtype=torch.float16, device=dev) for n, l in lin.items()}
+    L = []
+    tag = f"T{T}:" if not with_kv else ""
+    for name, x in inputs.items():
+        L.append(("hadamard_quant", tag + name, hq_bytes(T, x.shape[1]), 0,
+                  (lambda x=x, name=name: qr.hadamard_quant(x, signs[x.shape[1]], 1.0,
+                                                            out=qbuf[name])), qbuf[name]))
+    for name, l in lin.items():
+        L.append(("w4a4_gemm", tag + name, gemm_bytes(T, l.n, l.k), gemm_ops(T, l.n, l.k),
+                  (lambda name=name, l=l: qr.w4a4_gemm(*qbuf[l.input], *wq[name],
+                                                        out=ybuf[name])), (ybuf[name],)))
+    desc = None
+    if with_kv:
+        # KV: 70B-shaped heads (8 KV heads, 64 query heads, head_dim 128) over the same tokens
+        Hkv, Hq, Dh, G = 8, H // 128, 128, 128
+        B = 32 if T % 32 == 0 else 1
+        S = T // B
+        k_in = wl.kv_tensor_torch(torch, dev, 5, 0, B, S, Hkv, Dh)
+        v_in = wl.kv_tensor_torch(torch, dev, 5, 1, B, S, Hkv, Dh)
+        q_in = wl.activations_torch(torch, dev, 5, 2, T * Hq, Dh, 0)
+        kv_signs = torch.from_numpy(wl.signs(5, Dh)).to(dev)
+        cache = {n: (torch.empty((B, Hkv, S, Dh // 2), dtype=torch.uint8, device=dev),
+                     torch.empty((B, Hkv, S, Dh // G, 2), dtype=torch.float16, device=dev))
+                 for n in ("k", "v")}
+        qout = torch.empty((T * Hq, Dh), dtype=torch.float16, device=dev)
+        L.append(("kv_rotate_quant", "k", kv_bytes(T * Hkv, Dh, G), 0,
+                  lambda: qr.kv_rotate_quant(k_in, kv_signs, G, 0.95, *cache["k"], 0), cache["k"]))
+        L.append(("kv_rotate_quant", "v", kv_bytes(T * Hkv, Dh, G), 0,
+                  lambda: qr.kv_rotate_quant(v_in, None, G, 0.95, *cache["v"], 0, rotate=False),
+                  cache["v"]))
+        L.append(("hadamard", "q", rot_bytes(T * Hq, Dh), 0,
+                  lambda: qr.hadamard(q_in, kv_signs, torch.float16, out=qout), (qout,)))
+        desc = (f"K/V init into a 4-bit cache ({B}x{S}x{Hkv}x{Dh}, group {G}), "
+                f"Q rotation ({Hq} heads)")
+    return L, lin, desc
+
+
+def make_kv_decode(torch, qr, wl, W, dev):
+    kv = W.kv
+    B, P, Dn, H, Hq, Dh, G = (kv["batch"], kv["prefill"], kv["decode"], kv["kv_heads"],
+                              kv["q_heads"], kv["head_dim"], kv["group"])
+    S = P + Dn
+    k = wl.kv_tensor_torch(torch, dev, W.wid, 0, B, S, H, Dh, kv["outlier"])
+    v = wl.kv_tensor_torch(torch, dev, W.wid, 1, B, S, H, Dh, kv["outlier"])
+    q = wl.kv_tensor_torch(torch, dev, W.wid, 2, B, S, Hq, Dh, 1.0)
+    kp, vp = k[:, :P].contiguous(), v[:, :P].contiguous()
+    qp = q[:, :P].reshape(-1, Dh)
+    s = torch.from_numpy(wl.signs(W.wid, Dh)).to(dev)
+    cache = {n: (torch.empty((B, H, S, Dh // 2), dtype=torch.uint8, device=dev),
+                 torch.empty((B, H, S, Dh // G, 2), dtype=torch.float16, device=dev))
+             for n in ("k", "v")}
+    qo_p = torch.empty((B * P * Hq, Dh), dtype=torch.float16, device=dev)
+    L = [("kv_rotate_quant", "k:init", kv_bytes(B * P * H, Dh, G), 0,
+          lambda: qr.kv_rotate_quant(kp, s, G, 0.95, *cache["k"], 0), cache["k"]),
+         ("kv_rotate_quant", "v:init", kv_bytes(B * P * H, Dh, G), 0,
+          lambda: qr.kv_rotate_quant(vp, None, G, 0.95, *cache["v"], 0, rotate=False), cache["v"]),
+         ("hadamard", "q:prompt", rot_bytes(B * P * Hq, Dh), 0,
+          lambda: qr.hadamard(qp, s, torch.float16, out=qo_p), (qo_p,))]
+    qo_d = [torch.empty((B * Hq, Dh), dtype=torch.float16, device=dev) for _ in range(Dn)]
+    for i in range(Dn):
+        qd = q[:, P + i].reshape(-1, Dh)
+        L.append(("kv_rotate_quant", f"k:append{i}", kv_bytes(B * H, Dh, G), 0,
+                  lambda i=i: qr.kv_rotate_quant(k[:, P + i:P + i + 1], s, G, 0.95, *cache["k"], P + i),
+                  cache["k"]))
+        L.append(("kv_rotate_quant", f"v:append{i}", kv_bytes(B * H, Dh, G), 0,
+                  lambda i=i: qr.kv_rotate_quant(v[:, P + i:P + i + 1], None, G, 0.95, *cache["v"],
+                                                 P + i, rotate=False), cache["v"]))
+        L.append(("hadamard", f"q:decode{i}", rot_bytes(B * Hq, Dh), 0,
+                  lambda qd=qd, i=i: qr.hadamard(qd, s, torch.float16, out=qo_d[i]), (qo_d[i],)))
+    desc = (f"Llama-2-70B KV path: batch {B}, {P}-token prompt + {Dn} decode steps, {H} KV heads "
+            f"and {Hq} query heads of {Dh}; K/V Init + Append into the 4-bit cache (group {G}, "
+            f"clip 0.95), head-wise rotation of K and Q")
+    return L, desc
+
+
+# ---------------------------------------------------------------------------
+# Timing
+# ---------------------------------------------------------------------------
+
+def run_timed(torch, launches, steps, warmup):
+    for _ in range(warmup):
+        for l in launches:
+            l[4]()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in launches] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for k in range(steps):
+        for i, l in enumerate(launches):
+            ev[k][i][0].record()
+            l[4]()
+            ev[k][i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = [sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(steps)) / steps
+           for i in range(len(launches))]
+    return t0.elapsed_time(t1) / steps, per, wall
+
+
+def run_graphed(torch, launches, steps, warmup, reps=20):
+    """Timing for steps made of many short launches, where the host's launch
+    latency would otherwise be measured instead of the kernels: each launch is
+    captured REPS times into a HIP graph and replayed between two events, and
+    the whole step is captured once and replayed STEPS times.  Every output is
+    compared with the eager run's before timing."""
+    for _ in range(max(1, warmup)):
+        for l in launches:
+            l[4]()
+    torch.cuda.synchronize()
+    eager = [[t.clone() for t in l[5]] for l in launches]
+    step_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(step_graph):
+        for l in launches:
+            l[4]()
+    for t_list in (l[5] for l in launches):
+        for t in t_list:
+            t.zero_()
+    step_graph.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for l, e in zip(launches, eager) for a, b in zip(l[5], e))
+    per = []
+    for l in launches:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                l[4]()
+        g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / reps)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        step_graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return t0.elapsed_time(t1) / steps, per, wall, same
+
+
+def kernel_totals(launches, per, kernel):
+    ms = sum(p for l, p in zip(launches, per) if l[0] == kernel)
+    nbytes = sum(l[2] for l in launches if l[0] == kernel)
+    ops = sum(l[3] for l in launches if l[0] == kernel)
+    n = sum(1 for l in launches if l[0] == kernel)
+    return ms, nbytes, ops, n
+
+
+def source_sha(kernel):
+    return hashlib.sha256((CSRC / KERNEL_SOURCE[kernel]).read_bytes()).hexdigest()
+
+
+def profiled_traffic(kernel, workload):
+    """HBM bytes per launch from profiles/traffic_<kernel>_<workload>.txt, or None
+    if that summary is missing or was taken on a different kernel source."""
+    f = ROOT / "profiles" / f"traffic_{kernel}_{workload}.txt"
+    if not f.exists():
+        return None
+    kv = {}
+    for line in f.read_text().splitlines():
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_sha(kernel):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def roofline(kernel, workload, launches, per, bound):
+    ms, nbytes, ops, n = kernel_totals(launches, per, kernel)
+    tr = profiled_traffic(kernel, workload)
+    if bound == "mfma":
+        ach = ops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": kernel, "launches_per_step": n,
+                "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                "op_note": "int8 MFMA operations (2 per multiply-accumulate) over the step's "
+                           "launches of the kernel / their summed event time",
+                "frac": round(ach / INT8_PEAK_TOPS, 4),
+                "traffic": None if tr is None else round(tr)}
+    ach = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "launches_per_step": n,
+            "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None if tr is None else round(tr)}
+
+
+def copy_calibration():
+    import torch
+    dev = torch.device("cuda:0")
+    n = (1 << 30) // 2
+    a = torch.empty(n, dtype=torch.float16, device=dev).normal_()
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": True, "bytes_read_per_launch": 2 * n,
+                      "bytes_written_per_launch": 2 * n, "launches": 10}), flush=True)
+    return 0
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "this path is measured on one GPU only (the per-GPU shard of "
+                                   "a sharded run has the same shapes); run with --gpus 1",
                           "n_gpus": args.gpus}))
         return 2
-    import numpy as np
+    if args.copy_calibration:
+        return copy_calibration()
     import torch
 
     import hadamard_rotation_int4_amd as qr
@@ -78,133 +349,59 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    W = wl.WORKLOADS[args.workload]
-    T = W.tokens[0]
-    H = W.hidden
-    lin = {l.name: l for l in W.linears}
-    ffn = lin["down"].k
-    wid = W.wid
-    print(f"[bench] workload {W.name}: T={T} hidden={H} ffn={ffn}", file=sys.stderr, flush=True)
-
-    # ---- inputs resident in HBM ----
-    inputs = {}
-    for i, name in enumerate(("attn_in", "o_in", "ffn_in", "down_in")):
-        d = ffn if name == "down_in" else H
-        inputs[name] = wl.activations_torch(torch, dev, wid, 10 + i, T, d, W.n_outliers,
-                                            W.outlier_lo, W.outlier_hi)
-    signs = {d: torch.from_numpy(wl.signs(wid, d)).to(dev) for d in (H, ffn)}
-    # ---- weights: random init, rotated by the same R_K and quantized per output channel
-    #      with the library's own kernel (offline preparation, not timed) ----
-    wq = {}
-    for i, (name, l) in enumerate(lin.items()):
-        w = wl.weights_torch(torch, dev, wid, 1 + i, l.n, l.k)
-        wq[name] = qr.hadamard_quant(w, signs[l.k], 1.0)
-        del w
-    # KV: 70B-shaped heads (8 KV heads, 64 query heads, head_dim 128) over the same tokens
-    Hkv, Hq, Dh, G = 8, H // 128, 128, 128
-    B = 32 if T % 32 == 0 else 1
-    S = T // B
-    k_in = wl.kv_tensor_torch(torch, dev, 5, 0, B, S, Hkv, Dh)
-    v_in = wl.kv_tensor_torch(torch, dev, 5, 1, B, S, Hkv, Dh)
-    q_in = wl.activations_torch(torch, dev, 5, 2, T * Hq, Dh, 0)
-    kv_signs = torch.from_numpy(wl.signs(5, Dh)).to(dev)
-    cache = {n: (torch.empty((B, Hkv, S, Dh // 2), dtype=torch.uint8, device=dev),
-                 torch.empty((B, Hkv, S, Dh // G, 2), dtype=torch.float16, device=dev))
-             for n in ("k", "v")}
-    # ---- outputs ----
-    qbuf = {name: (torch.empty((T, t.shape[1] // 2), dtype=torch.uint8, device=dev),
-                   torch.empty((T,), dtype=torch.float16, device=dev))
-            for name, t in inputs.items()}
-    ybuf = {name: torch.empty((T, l.n), dtype=torch.float16, device=dev) for name, l in lin.items()}
-    qout = torch.empty((T * Hq, Dh), dtype=torch.float16, device=dev)
+    wname = args.workload
+    W = wl.WORKLOADS[wname]
+    print(f"[bench] workload {W.name}", file=sys.stderr, flush=True)
+    config = {"workload": None}
+    if wname in ("70b_prefill", "7b_prefill"):
+        T = W.tokens[0]
+        launches, lin, kvdesc = make_block(torch, qr, wl, W, T, dev, True)
+        config.update({
+            "workload": f"{W.name}: T={T} tokens, hidden {W.hidden}, FFN {lin['down'].k}, QKV "
+                        f"{lin['qkv'].n}; 4 fused rotate+quant, 5 W4A4 GEMMs, {kvdesc}",
+            "tokens": T, "hidden": W.hidden, "ffn": lin["down"].k})
+        dominant, bound = "w4a4_gemm", "mfma"
+    elif wname == "7b_decode":
+        launches = []
+        for T in W.tokens:
+            L, lin, _ = make_block(torch, qr, wl, W, T, dev, False)
+            launches += L
+        config.update({
+            "workload": f"{W.name}: T in {list(W.tokens)}; per T 4 fused rotate+quant (d = "
+                        f"{W.hidden}, {lin['down'].k}) and the 5 W4A4 GEMMs (weight streaming)",
+            "tokens": list(W.tokens), "hidden": W.hidden, "ffn": lin["down"].k})
+        dominant, bound = "w4a4_gemm", "hbm"
+    else:
+        launches, desc = make_kv_decode(torch, qr, wl, W, dev)
+        config.update({"workload": desc})
+        dominant, bound = "kv_rotate_quant", "hbm"
     torch.cuda.synchronize()
 
-    # ---- one step, each launch bracketed by events (same stream as the kernels) ----
-    launches = []   # (kernel, label, algorithmic bytes, ops)
-    for name, x in inputs.items():
-        launches.append(("hadamard_quant", name, hq_bytes(T, x.shape[1]), 0))
-    for name, l in lin.items():
-        launches.append(("w4a4_gemm", name, gemm_bytes(T, l.n, l.k), gemm_ops(T, l.n, l.k)))
-    launches.append(("kv_rotate_quant", "k", kv_bytes(T * Hkv, Dh, G), 0))
-    launches.append(("kv_rotate_quant", "v", kv_bytes(T * Hkv, Dh, G), 0))
-    launches.append(("hadamard", "q", T * Hq * Dh * 4, 0))
-
-    def run_launch(i):
-        kern, label = launches[i][0], launches[i][1]
-        if kern == "hadamard_quant":
-            x = inputs[label]
-            qr.hadamard_quant(x, signs[x.shape[1]], 1.0, out=qbuf[label])
-        elif kern == "w4a4_gemm":
-            src = lin[label].input
-            qa, sa = qbuf[src]
-            qw, sw = wq[label]
-            qr.w4a4_gemm(qa, sa, qw, sw, out=ybuf[label])
-        elif kern == "kv_rotate_quant":
-            x = k_in if label == "k" else v_in
-            cq, cm = cache[label]
-            qr.kv_rotate_quant(x, kv_signs if label == "k" else None, G, 0.95, cq, cm, 0,
-                               rotate=(label == "k"))
-
-    # the Q rotation writes into a preallocated output through the C entry point
-    def run_q():
-        code = qr._load().qr_hadamard(qr._ptr(q_in), q_in.shape[0], Dh, Dh, qr._ptr(kv_signs),
-                                      qr._ptr(qout), 0, qr._stream(None))
-        qr._check(code, "qr_hadamard")
-
-    def step(events=None):
-        for i in range(len(launches)):
-            if events is not None:
-                events[i][0].record()
-            if launches[i][0] == "hadamard":
-                run_q()
-            else:
-                run_launch(i)
-            if events is not None:
-                events[i][1].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    K = args.steps
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in launches] for _ in range(K)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record()
-    for k in range(K):
-        step(ev[k])
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = t0.elapsed_time(t1)
-    ms_step = ms_total / K
-
-    per = {}
-    for i, (kern, label, nbytes, ops) in enumerate(launches):
-        ms = sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(K)) / K
-        per[f"{kern}:{label}"] = dict(kernel=kern, ms=ms, bytes=nbytes, ops=ops,
-                                      gbs=nbytes / ms / 1e6, tops=ops / ms / 1e9)
+    graphed = wname in ("7b_decode", "70b_kv")
+    if graphed:
+        ms_step, per, wall, same = run_graphed(torch, launches, args.steps, args.warmup)
+        if not same:
+            print("[bench] graph replay differs from the eager run", file=sys.stderr, flush=True)
+            return 1
+    else:
+        ms_step, per, wall = run_timed(torch, launches, args.steps, args.warmup)
     total_ops = sum(l[3] for l in launches)
-    value = total_ops / (ms_step * 1e-3) / 1e12
+    total_bytes = sum(l[2] for l in launches)
+    if bound == "mfma":
+        value, unit = total_ops / (ms_step * 1e-3) / 1e12, "TOPS"
+    else:
+        value, unit = total_bytes / (ms_step * 1e-3) / 1e9, "GB/s"
 
-    gemm = [v for v in per.values() if v["kernel"] == "w4a4_gemm"]
-    g_ms = sum(v["ms"] for v in gemm)
-    g_ops = sum(v["ops"] for v in gemm)
-    g_tops = g_ops / (g_ms * 1e-3) / 1e12
-    hqk = [v for v in per.values() if v["kernel"] == "hadamard_quant"]
-    h_ms = sum(v["ms"] for v in hqk)
-    h_bytes = sum(v["bytes"] for v in hqk)
-    h_gbs = h_bytes / (h_ms * 1e-3) / 1e9
-
+    kernels = {}
+    for l, p in zip(launches, per):
+        kernels[f"{l[0]}:{l[1]}"] = {"ms": round(p, 4), "GB/s": round(l[2] / p / 1e6, 1),
+                                     "TOPS": round(l[3] / p / 1e9, 1)}
     out = {
         "metric": METRIC,
         "value": round(value, 2),
-        "unit": "TOPS",
+        "unit": unit,
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
@@ -212,28 +409,20 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {
-            "workload": f"{W.name}: T={T} tokens, hidden {H}, FFN {ffn}, QKV {lin['qkv'].n}; "
-                        f"4 fused rotate+quant, 5 W4A4 GEMMs, K/V init into a 4-bit cache "
-                        f"({B}x{S}x{Hkv}x{Dh}, group {G}), Q rotation ({Hq} heads)",
-            "tokens": T, "hidden": H, "ffn": ffn,
-        },
-        "roofline": {
-            "bound": "mfma", "kernel": "qr_w4a4_gemm (all five launches of a step)",
-            "achieved": round(g_tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-            "op_note": "int8 MFMA operations (2 per multiply-accumulate), dense peak 5.0 POP/s",
-            "frac": round(g_tops / INT8_PEAK_TOPS, 4), "traffic": None,
-        },
-        "roofline_hadamard_quant": {
-            "bound": "hbm", "kernel": "qr_hadamard_quant (four launches of a step)",
-            "achieved": round(h_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(h_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-        },
-        "kernels": {k: {"ms": round(v["ms"], 4), "GB/s": round(v["gbs"], 1),
-                        "TOPS": round(v["tops"], 1)} for k, v in per.items()},
-        "wall_s_timed": round(wall, 3),
+        "config": config,
+        "roofline": roofline(dominant, wname, launches, per, bound),
     }
-    if not args.no_cpu_baseline:
+    if any(l[0] == "hadamard_quant" for l in launches):
+        out["roofline_hadamard_quant"] = roofline("hadamard_quant", wname, launches, per, "hbm")
+    out["kernels"] = kernels if len(kernels) <= 40 else {
+        k: {"ms": round(sum(p for l, p in zip(launches, per) if l[0] == k), 4),
+            "launches": sum(1 for l in launches if l[0] == k)}
+        for k in sorted({l[0] for l in launches})}
+    out["wall_s_timed"] = round(wall, 3)
+    out["timing"] = ("HIP graph replay of the step; per-launch times from graphs of 20 "
+                     "back-to-back launches (outputs checked equal to the eager run)" if graphed
+                     else "eager launches, HIP events around each launch on its stream")
+    if not args.no_cpu_baseline and wname == "70b_prefill":
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)
     return 0
@@ -282,8 +471,7 @@ def cpu_baseline(W, t_sample):
         okv.kv_rotate_quant_cache(kx, wl.signs(5, 128), True, 128, 0.95, cq, cm, 0)
     dt = time.perf_counter() - t0
     try:
-        import numpy as _np
-        blas = _np.show_config(mode="dicts").get("Build Dependencies", {}).get("blas", {}).get("name")
+        blas = np.show_config(mode="dicts").get("Build Dependencies", {}).get("blas", {}).get("name")
     except Exception:  # noqa: BLE001
         blas = None
     return {

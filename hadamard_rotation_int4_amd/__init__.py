@@ -8,7 +8,7 @@ falls back to a CPU or PyTorch implementation.
 
 Functions (same names as the C entry points without the ``qr_`` prefix):
   hadamard_quant(x, signs, clip_ratio, rotate=True, z_dbg=False) -> (q_u8, scale_f16[, z])
-  hadamard(x, signs, out_dtype=torch.float32) -> y
+  hadamard(x, signs, out_dtype=torch.float32, out=None) -> y
   w4a4_gemm(a_q, a_scale, w_q, w_scale, acc_dbg=False) -> y_f16[, acc_i32]
   kv_rotate_quant(kv, signs, group, clip_ratio, cache_q, cache_meta, start_pos,
                   rotate=True, z_dbg=False) -> None[, z]
@@ -155,10 +155,12 @@ def hadamard_quant(x, signs=None, clip_ratio: float = 1.0, rotate: bool = True,
     return (q, sc, z) if z_dbg else (q, sc)
 
 
-def hadamard(x, signs=None, out_dtype=None, stream=None):
-    """y = H_d diag(s) x / sqrt(d) row-wise; x fp16 [T, d]; y fp32 (default) or fp16."""
+def hadamard(x, signs=None, out_dtype=None, stream=None, out=None):
+    """y = H_d diag(s) x / sqrt(d) row-wise; x fp16 [T, d]; y fp32 (default) or fp16.
+
+    ``out``: optional preallocated contiguous [T, d] tensor of ``out_dtype``."""
     torch = _torch()
-    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    out_dtype = (out.dtype if out is not None else torch.float32) if out_dtype is None else out_dtype
     _need(x, torch.float16, "x", 2)
     if x.numel() and x.stride(1) != 1:
         raise ValueError("x rows must be contiguous (stride(1) == 1)")
@@ -166,7 +168,13 @@ def hadamard(x, signs=None, out_dtype=None, stream=None):
         raise ValueError("out_dtype must be float32 or float16")
     T, d = x.shape
     s = _signs(signs, d, x.device)
-    y = torch.empty((T, d), dtype=out_dtype, device=x.device)
+    if out is not None:
+        _need(out, out_dtype, "out", 2)
+        if tuple(out.shape) != (T, d) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [T, d] tensor")
+        y = out
+    else:
+        y = torch.empty((T, d), dtype=out_dtype, device=x.device)
     code = _load().qr_hadamard(_ptr(x), T, d, x.stride(0) if T > 0 else d, _ptr(s), _ptr(y),
                                1 if out_dtype == torch.float32 else 0, _stream(stream))
     _check(code, "qr_hadamard")

@@ -73,6 +73,26 @@ __device__ __forceinline__ uint32_t quant_pack8(const float* v, float m) {
   return lo ^ hi ^ 0x88888888u;  // offset binary -> two's complement nibbles
 }
 
+// Sign-bit masks of 8 consecutive fp16 values from their 8 int8 signs (+1 or
+// -1; the int8 sign bit decides): dword j gets bit 15 if sign 2j is negative
+// and bit 31 if sign 2j + 1 is.  Two dword loads; `s` is 4-byte aligned.
+__device__ __forceinline__ v4u sign_masks8(const int8_t* s, bool second_half = true) {
+  const uint32_t w0 = *(const uint32_t*)s;
+  const uint32_t w1 = second_half ? *(const uint32_t*)(s + 4) : 0u;
+  v4u m;
+  m[0] = ((w0 << 8) & 0x8000u) | ((w0 << 16) & 0x80000000u);
+  m[1] = ((w0 >> 8) & 0x8000u) | (w0 & 0x80000000u);
+  m[2] = ((w1 << 8) & 0x8000u) | ((w1 << 16) & 0x80000000u);
+  m[3] = ((w1 >> 8) & 0x8000u) | (w1 & 0x80000000u);
+  return m;
+}
+// The same eight signs as one word: bit 15 - j / 31 - j for elements 2j / 2j + 1,
+// so that (E << j) & 0x80008000 is the mask of dword j.
+__device__ __forceinline__ uint32_t sign_word8(const int8_t* s, bool second_half = true) {
+  const v4u m = sign_masks8(s, second_half);
+  return m[0] | (m[1] >> 1) | (m[2] >> 2) | (m[3] >> 3);
+}
+
 // Streaming accesses: every input row is read once and every output written
 // once, so both bypass cache retention (non-temporal).
 #ifndef QR_NT
@@ -147,13 +167,7 @@ __global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const u
   for (int i = tid; i < NB * 64; i += 256) {
     const int b = i >> 6, ln = i & 63;
     const int e = b * 512 + gmap(ln & 15) * 32 + (ln >> 4) * 8;
-    v4u m = {0u, 0u, 0u, 0u};
-    if (signs) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        m[j] = (signs[e + 2 * j] < 0 ? 0x8000u : 0u) | (signs[e + 2 * j + 1] < 0 ? 0x80000000u : 0u);
-    }
-    s_mask[i] = m;
+    s_mask[i] = signs ? sign_masks8(signs + e) : v4u{0u, 0u, 0u, 0u};
   }
   __syncthreads();
 
@@ -321,7 +335,12 @@ __global__ __launch_bounds__(256) void k_hq_small(const uint16_t* __restrict__ x
   const int rw = lane / LPR;   // row within the wavefront
   float sg[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) sg[j] = (rot && signs && signs[sub * 8 + j] < 0) ? -1.0f : 1.0f;
+  for (int j = 0; j < 8; ++j) sg[j] = 1.0f;
+  if (rot && signs) {
+    const uint32_t w0 = *(const uint32_t*)(signs + sub * 8), w1 = *(const uint32_t*)(signs + sub * 8 + 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sg[j] = (((j < 4 ? w0 : w1) >> (8 * (j & 3) + 7)) & 1u) ? -1.0f : 1.0f;
+  }
 
   for (int64_t base = ((int64_t)blockIdx.x * 4 + wave) * RPW; base < T;
        base += (int64_t)gridDim.x * 4 * RPW) {
@@ -627,14 +646,7 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
     for (int kb = 0; kb < 4; ++kb) {
       const int G = (w * 4 + ct) * 16 + gc;
       const int e0 = G * 112 + 32 * kb + 8 * g;
-      uint32_t e = 0u;
-      if (signs && 32 * kb + 8 * g < 112) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          e |= (signs[e0 + 2 * j] < 0 ? (0x8000u >> j) : 0u) |
-               (signs[e0 + 2 * j + 1] < 0 ? (0x80000000u >> j) : 0u);
-      }
-      ev[kb] = e;
+      ev[kb] = (signs && 32 * kb + 8 * g < 112) ? sign_word8(signs + e0) : 0u;
     }
     s_sbits[(w * 4 + ct) * 64 + lane] = ev;
   }
@@ -900,15 +912,8 @@ __global__ __launch_bounds__(256, 2) void k_hq_k172(const uint16_t* __restrict__
     const int fl = f & 63, ck = f >> 6;
     const int ct = ck / 6, kb = ck % 6;
     const int a = 16 * ct + gmap(fl & 15), gg = fl >> 4;
-    uint32_t e = 0u;
-    if (signs) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int col = 32 * kb + 8 * gg + j;
-        if (col < 172 && signs[a * 172 + col] < 0) e |= (j & 1) ? (0x80000000u >> (j >> 1)) : (0x8000u >> (j >> 1));
-      }
-    }
-    s_sbits[f] = e;
+    const int col = 32 * kb + 8 * gg;  // 8 columns, or 4 (168 .. 171), or none
+    s_sbits[f] = (signs && col < 172) ? sign_word8(signs + a * 172 + col, col + 8 <= 172) : 0u;
   }
   const float s0 = (gc & 1) ? -1.0f : 1.0f;
   const float s1 = (gc & 2) ? -1.0f : 1.0f;
@@ -1218,7 +1223,7 @@ extern "C" qr_status qr_hadamard_quant(const void* x_f16, int64_t T, int32_t d, 
   if (T == 0) return QR_OK;
   if (!x_f16 || !q_u8 || !scale_f16) return QR_ERR_NULL;
   if (ld_x % 8 != 0 || !aligned(x_f16, 16) || !aligned(q_u8, 4) || !aligned(scale_f16, 2) ||
-      (z_dbg && !aligned(z_dbg, 16)))
+      (z_dbg && !aligned(z_dbg, 16)) || (signs && !aligned(signs, 4)))
     return QR_ERR_ALIGN;
   const int r = rot == QR_ROT_HADAMARD ? 1 : 0;
   if (clip_ratio < 1.0f)
@@ -1236,7 +1241,8 @@ extern "C" qr_status qr_hadamard(const void* x_f16, int64_t T, int32_t d, int64_
   if (!factor_width(d, &n, &m)) return QR_ERR_UNSUPPORTED;
   if (T == 0) return QR_OK;
   if (!x_f16 || !y) return QR_ERR_NULL;
-  if (ld_x % 8 != 0 || !aligned(x_f16, 16) || !aligned(y, 16)) return QR_ERR_ALIGN;
+  if (ld_x % 8 != 0 || !aligned(x_f16, 16) || !aligned(y, 16) || (signs && !aligned(signs, 4)))
+    return QR_ERR_ALIGN;
   if (y_is_f32)
     return dispatch<MODE_ROT_F32, false>(x_f16, T, d, ld_x, 1, signs, 1.0f, nullptr, nullptr,
                                          nullptr, y, stream);

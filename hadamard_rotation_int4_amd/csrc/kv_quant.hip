@@ -35,7 +35,12 @@ __global__ __launch_bounds__(256) void k_kv_quant(
   const int ngroups = DH / group;
   float sg[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) sg[j] = (ROT && signs && signs[sub * 8 + j] < 0) ? -1.0f : 1.0f;
+  for (int j = 0; j < 8; ++j) sg[j] = 1.0f;
+  if (ROT && signs) {
+    const uint32_t w0 = *(const uint32_t*)(signs + sub * 8), w1 = *(const uint32_t*)(signs + sub * 8 + 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sg[j] = (((j < 4 ? w0 : w1) >> (8 * (j & 3) + 7)) & 1u) ? -1.0f : 1.0f;
+  }
 
   for (int64_t base = ((int64_t)blockIdx.x * 4 + wave) * RPW; base < rows;
        base += (int64_t)gridDim.x * 4 * RPW) {
@@ -177,7 +182,8 @@ extern "C" qr_status qr_kv_rotate_quant(const void* kv_f16, int32_t B, int32_t S
   if (S_new == 0) return QR_OK;
   if (!kv_f16 || !cache_q || !cache_meta) return QR_ERR_NULL;
   if (ld_token % 8 != 0 || !aligned(kv_f16, 16) || !aligned(cache_q, 4) ||
-      !aligned(cache_meta, 4) || (z_dbg && !aligned(z_dbg, 16)))
+      !aligned(cache_meta, 4) || (z_dbg && !aligned(z_dbg, 16)) ||
+      (rot == QR_ROT_HADAMARD && signs && !aligned(signs, 4)))
     return QR_ERR_ALIGN;
   const int64_t rows = (int64_t)B * S_new * H;
   const uint16_t* x = (const uint16_t*)kv_f16;

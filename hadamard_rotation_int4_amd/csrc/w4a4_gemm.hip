@@ -349,6 +349,9 @@ __global__ __launch_bounds__(256) void k_w4a4_decode(
     const uint8_t* __restrict__ A, const uint16_t* __restrict__ a_scale, int T,
     const uint8_t* __restrict__ W, const uint16_t* __restrict__ w_scale, int N, int K,
     uint16_t* __restrict__ Y, int32_t* __restrict__ acc_dbg) {
+  // Blocks per chunk: a wavefront keeps two chunks of loads in flight,
+  // 2 * CH * (1 + MT) 16-byte loads per lane.
+  constexpr int CH = 8 / MT;
   __shared__ v4i s_part[3][MT][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -365,32 +368,53 @@ __global__ __launch_bounds__(256) void k_w4a4_decode(
   const int per = (kblocks + 3) / 4;
   const int kb0 = wave * per, kb1 = min(kblocks, kb0 + per);
 
+  v4u wv[2][CH], av[2][CH][MT];
+  // Load chunk starting at block kb into buffer b; blocks past kb1 and the
+  // bytes of a final half block (K % 128 == 64) read as zero.
+  auto load = [&](auto bt, int kb) {
+    constexpr int b = decltype(bt)::value;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int byte = (kb + c) * 64 + 16 * g;
+      const bool ok = kb + c < kb1 && byte < rowbytes;
+      const int off = ok ? byte : 0;
+      wv[b][c] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_w, i * rowbytes + off, 0, 0));
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        av[b][c][m] = __builtin_bit_cast(
+            v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, (16 * m + i) * rowbytes + off, 0, 0));
+      if (!ok) {
+        wv[b][c] = v4u{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int m = 0; m < MT; ++m) av[b][c][m] = v4u{0u, 0u, 0u, 0u};
+      }
+    }
+  };
   v4i acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = v4i{0, 0, 0, 0};
-#pragma unroll 4
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const int byte = kb * 64 + 16 * g;  // this lane's 16 bytes of the block
-    const bool inside = byte < rowbytes;  // K % 128 == 64: the last block is half full
-    v4u wv = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_w, i * rowbytes + byte, 0, 0));
-    v4u av[MT];
+  auto compute = [&](auto bt) {
+    constexpr int b = decltype(bt)::value;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-      av[m] = __builtin_bit_cast(
-          v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, (16 * m + i) * rowbytes + byte, 0, 0));
-    if (!inside) {
-      wv = v4u{0u, 0u, 0u, 0u};
+    for (int c = 0; c < CH; ++c)
 #pragma unroll
-      for (int m = 0; m < MT; ++m) av[m] = v4u{0u, 0u, 0u, 0u};
-    }
+      for (int e = 0; e < 2; ++e) {
+        const v4i bw = unpack16(make_uint2(wv[b][c][2 * e], wv[b][c][2 * e + 1]));
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const v4i b = unpack16(make_uint2(wv[2 * e], wv[2 * e + 1]));
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        acc[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-            unpack16(make_uint2(av[m][2 * e], av[m][2 * e + 1])), b, acc[m], 0, 0, 0);
-    }
+        for (int m = 0; m < MT; ++m)
+          acc[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+              unpack16(make_uint2(av[b][c][m][2 * e], av[b][c][m][2 * e + 1])), bw, acc[m], 0, 0, 0);
+      }
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  if (kb0 < kb1) load(B0{}, kb0);
+  for (int kb = kb0; kb < kb1; kb += 2 * CH) {  // buffer indices stay compile-time
+    if (kb + CH < kb1) load(B1{}, kb + CH);
+    compute(B0{});
+    if (kb + CH >= kb1) break;
+    if (kb + 2 * CH < kb1) load(B0{}, kb + 2 * CH);
+    compute(B1{});
   }
   if (wave > 0) {
 #pragma unroll

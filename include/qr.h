@@ -99,7 +99,8 @@ qr_status qr_hadamard_factor(int32_t d, int32_t* log2_pow2, int32_t* m);
  * The order of the fp32 additions inside z is not specified.
  *
  * Requirements: T >= 0; d supported; ld_x >= d and ld_x % 8 == 0; x_f16
- * 16-byte aligned; q_u8 4-byte aligned; z_dbg 16-byte aligned if given.
+ * 16-byte aligned; q_u8 and signs 4-byte aligned; z_dbg 16-byte aligned if
+ * given.
  */
 qr_status qr_hadamard_quant(const void* x_f16, int64_t T, int32_t d, int64_t ld_x, qr_rot rot,
                             const int8_t* signs, float clip_ratio, void* q_u8, void* scale_f16,
@@ -111,7 +112,7 @@ qr_status qr_hadamard_quant(const void* x_f16, int64_t T, int32_t d, int64_t ld_
  * fp32(z * c) with z and c as in qr_hadamard_quant, written as fp32
  * (y_is_f32 != 0) or rounded to fp16.
  *   x_f16 [T, ld_x] fp16; signs [d] int8 or NULL; y [T, d] contiguous.
- * Requirements as qr_hadamard_quant (y 16-byte aligned).
+ * Requirements as qr_hadamard_quant (y 16-byte aligned, signs 4-byte aligned).
  */
 qr_status qr_hadamard(const void* x_f16, int64_t T, int32_t d, int64_t ld_x, const int8_t* signs,
                       void* y, int32_t y_is_f32, hipStream_t stream);
@@ -128,7 +129,7 @@ qr_status qr_hadamard(const void* x_f16, int64_t T, int32_t d, int64_t ld_x, con
  *   w_scale    [N] fp16 channel scales.
  *   y_f16      [T, N] fp16 output (contiguous).
  *   acc_dbg    NULL, or [T, N] int32 (output): the exact accumulators.
- * Requirements: T, N >= 0; K > 0, K % 64 == 0, K <= 131072; a_q and w_q
+ * Requirements: T, N >= 0; K > 0, K % 64 == 0, K <= 131008; a_q and w_q
  * 16-byte aligned; y_f16 and acc_dbg 4-byte aligned.
  */
 qr_status qr_w4a4_gemm(const void* a_q, const void* a_scale_f16, int64_t T, const void* w_q,
@@ -157,8 +158,8 @@ qr_status qr_w4a4_gemm(const void* a_q, const void* a_scale_f16, int64_t T, cons
  *   z_dbg       NULL, or [B, S_new, H, Dh] fp32: z before the 1/sqrt(Dh) factor.
  * Requirements: B, H >= 1, S_new >= 0; Dh a power of two, 8 <= Dh <= 256;
  * ld_token >= H * Dh, ld_token % 8 == 0; 0 <= start_pos and
- * start_pos + S_new <= S_max; kv_f16 16-byte aligned; cache_q 4-byte aligned;
- * cache_meta 4-byte aligned.
+ * start_pos + S_new <= S_max; kv_f16 16-byte aligned; cache_q, cache_meta and
+ * signs 4-byte aligned.
  */
 qr_status qr_kv_rotate_quant(const void* kv_f16, int32_t B, int32_t S_new, int32_t H, int32_t Dh,
                              int64_t ld_token, qr_rot rot, const int8_t* signs, int32_t group,
