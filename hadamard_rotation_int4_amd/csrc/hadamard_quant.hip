@@ -591,10 +591,48 @@ __global__ __launch_bounds__(256) void k_hq_lds(const uint16_t* __restrict__ x, 
 // DPP across lanes, two between registers, and a radix-4 stage across the
 // wavefronts through LDS (four rounds of 7 chunk positions).  After it each
 // wavefront owns column tile ct = w of all four w'' and so whole chunks; amax
-// is reduced through LDS, and the packed codes are staged in LDS (aliasing the
-// exchange buffer) for coalesced row stores.
-constexpr int K28_XROUND = 4 * 4 * 7 * 64;  // floats per exchange round: [w][ct][7][lane]
-constexpr int K28_AFRAG = 7 * 4 * 64;       // v8h A fragments: [mt][kb][lane]
+// is reduced through LDS, and each lane stores its chunks' 14 bytes of packed
+// codes directly (two-byte stores: measured faster than staging the row in
+// LDS for 16-byte stores, which costs two more barriers per row).
+#ifndef QR_K28_ROUNDS
+#define QR_K28_ROUNDS 4
+#endif
+#ifndef QR_K28_DIRECT
+#define QR_K28_DIRECT 1
+#endif
+constexpr int K28_RV = 28 / QR_K28_ROUNDS;             // chunk positions per exchange round
+constexpr int K28_XROUND = 4 * 4 * K28_RV * 64;       // floats per round: [w][ct][RV][lane]
+constexpr int K28_AFRAG = 7 * 4 * 64;                 // A fragments: [mt][kb][lane]
+
+// H_112 = H_4 (x) H_28 in MFMA A-fragment layout, built at compile time: tile
+// mt row i -> output 28 (i >> 2) + 4 mt + (i & 3), block kb lane (i, g) ->
+// columns 32 kb + 8 g .. + 7 (zero past 111); +-1 as fp16 bit patterns.
+struct H112Frags {
+  uint16_t v[K28_AFRAG][8];
+};
+constexpr H112Frags make_h112_frags() {
+  H112Frags f{};
+  const HTable<28> h = make_h28();
+  for (int idx = 0; idx < K28_AFRAG; ++idx) {
+    const int fl = idx & 63, mk = idx >> 6;
+    const int mt = mk >> 2, kb = mk & 3;
+    const int i = fl & 15, gg = fl >> 4;
+    const int o = 28 * (i >> 2) + 4 * mt + (i & 3);
+    for (int j = 0; j < 8; ++j) {
+      const int col = 32 * kb + 8 * gg + j;
+      uint16_t bits = 0;
+      if (col < 112) {
+        int par = 0;
+        for (int b = (o / 28) & (col / 28); b; b >>= 1) par ^= b & 1;
+        const bool neg = (h.v[o % 28][col % 28] < 0.0f) != (par == 1);
+        bits = neg ? 0xBC00u : 0x3C00u;
+      }
+      f.v[idx][j] = bits;
+    }
+  }
+  return f;
+}
+__device__ const H112Frags g_h112_frags = make_h112_frags();
 
 template <int MODE, bool CLAMP>
 __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uint16_t* __restrict__ x, int64_t T,
@@ -605,7 +643,7 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
                                                    void* __restrict__ yout) {
   constexpr int D = 28672;
   __shared__ v8h s_afrag[K28_AFRAG];           // 28 KB
-  __shared__ float s_x[K28_XROUND];            // 28 KB, also the packed-row stage
+  __shared__ float s_x[K28_XROUND];            // exchange rounds, also the packed-row stage
   __shared__ v4u s_sbits[4 * 4 * 64];         // 16 KB
   __shared__ float s_red[4];
   const int tid = threadIdx.x;
@@ -616,24 +654,10 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
 
   // A fragments of H_112 = H_4 (x) H_28: tile mt row i -> output 28 (i >> 2) + 4 mt + (i & 3),
   // block kb lane (i, g) holds columns 32 kb + 8 g + j (zero past 112).
-  for (int f = tid; f < K28_AFRAG; f += 256) {
-    const int fl = f & 63, mk = f >> 6;
-    const int mt = mk >> 2, kb = mk & 3;
-    const int i = fl & 15, gg = fl >> 4;
-    const int o = 28 * (i >> 2) + 4 * mt + (i & 3);
-    v8h a;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = 32 * kb + 8 * gg + j;
-      float v = 0.0f;
-      if (col < 112) {
-        const int h4 = (__builtin_popcount((o / 28) & (col / 28)) & 1) ? -1 : 1;
-        v = (float)h4 * g_h28.v[o % 28][col % 28];
-      }
-      a[j] = (_Float16)v;
-    }
-    s_afrag[f] = a;
-  }
+  // (reading them through the caches on every row instead was measured slower)
+  const v8h* afrag_g = (const v8h*)&g_h112_frags.v[0][0];
+  for (int f = tid; f < K28_AFRAG; f += 256) s_afrag[f] = afrag_g[f];
+  const v8h* afrag = s_afrag;
   // Signs of the lane's B fragments (the same for every row), one dword per
   // fragment: bit 15 - j holds the sign of element 2 j, bit 31 - j that of
   // element 2 j + 1, so (E << j) & 0x80008000 is the sign-bit mask of dword j.
@@ -686,7 +710,7 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
       for (int ct = 0; ct < 4; ++ct) accm[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const v8h a = s_afrag[(mt * 4 + kb) * 64 + lane];
+        const v8h a = afrag[(mt * 4 + kb) * 64 + lane];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           const v8h b = __builtin_bit_cast(v8h, braw[ct][kb]);
@@ -757,23 +781,24 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
     //      chunk 4 G + g, G = (4 w'' + w) 16 + gmap(n), position k ----
     float o[4][28];
 #pragma unroll
-    for (int rnd = 0; rnd < 4; ++rnd) {
+    for (int rnd = 0; rnd < QR_K28_ROUNDS; ++rnd) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int k = 0; k < 7; ++k) s_x[((w * 4 + ct) * 7 + k) * 64 + lane] = v[ct][7 * rnd + k];
+        for (int k = 0; k < K28_RV; ++k)
+          s_x[((w * 4 + ct) * K28_RV + k) * 64 + lane] = v[ct][K28_RV * rnd + k];
       __syncthreads();
 #pragma unroll
-      for (int k = 0; k < 7; ++k) {
-        const float a0 = s_x[((0 * 4 + w) * 7 + k) * 64 + lane];
-        const float a1 = s_x[((1 * 4 + w) * 7 + k) * 64 + lane];
-        const float a2 = s_x[((2 * 4 + w) * 7 + k) * 64 + lane];
-        const float a3 = s_x[((3 * 4 + w) * 7 + k) * 64 + lane];
+      for (int k = 0; k < K28_RV; ++k) {
+        const float a0 = s_x[((0 * 4 + w) * K28_RV + k) * 64 + lane];
+        const float a1 = s_x[((1 * 4 + w) * K28_RV + k) * 64 + lane];
+        const float a2 = s_x[((2 * 4 + w) * K28_RV + k) * 64 + lane];
+        const float a3 = s_x[((3 * 4 + w) * K28_RV + k) * 64 + lane];
         const float p01 = a0 + a1, m01 = a0 - a1, p23 = a2 + a3, m23 = a2 - a3;
-        o[0][7 * rnd + k] = p01 + p23;
-        o[1][7 * rnd + k] = m01 + m23;
-        o[2][7 * rnd + k] = p01 - p23;
-        o[3][7 * rnd + k] = m01 - m23;
+        o[0][K28_RV * rnd + k] = p01 + p23;
+        o[1][K28_RV * rnd + k] = m01 + m23;
+        o[2][K28_RV * rnd + k] = p01 - p23;
+        o[3][K28_RV * rnd + k] = m01 - m23;
       }
       __syncthreads();
     }
@@ -816,16 +841,26 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
                             : quant_pack8<false>(&o[w2][8 * k8], ml);
         float tail[8] = {o[w2][24], o[w2][25], o[w2][26], o[w2][27], 0.0f, 0.0f, 0.0f, 0.0f};
         words[3] = clamp ? quant_pack8<true>(tail, ml) : quant_pack8<false>(tail, ml);
+        if (QR_K28_DIRECT) {
+          uint16_t* qc = (uint16_t*)(q + row * (D / 2)) + cb;
 #pragma unroll
-        for (int k = 0; k < 7; ++k)
-          stage16[cb + k] = (uint16_t)((k & 1) ? (words[k >> 1] >> 16) : (words[k >> 1] & 0xffffu));
+          for (int k = 0; k < 7; ++k)
+            __builtin_nontemporal_store(
+                (uint16_t)((k & 1) ? (words[k >> 1] >> 16) : (words[k >> 1] & 0xffffu)), qc + k);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 7; ++k)
+            stage16[cb + k] = (uint16_t)((k & 1) ? (words[k >> 1] >> 16) : (words[k >> 1] & 0xffffu));
+        }
       }
-      __syncthreads();
-      const uint32_t* st32 = (const uint32_t*)s_x;
-      uint32_t* qr32 = (uint32_t*)(q + row * (D / 2));
-      for (int i = tid; i < D / 8; i += 256) st_stream(qr32 + i, st32[i]);
+      if (!QR_K28_DIRECT) {
+        __syncthreads();
+        const uint32_t* st32 = (const uint32_t*)s_x;
+        uint32_t* qr32 = (uint32_t*)(q + row * (D / 2));
+        for (int i = tid; i < D / 8; i += 256) st_stream(qr32 + i, st32[i]);
+      }
       if (tid == 0) scale[row] = sh;
-      __syncthreads();  // the stage aliases the next row's exchange buffer
+      if (!QR_K28_DIRECT) __syncthreads();  // the stage aliases the next row's exchange buffer
     } else {
       const float cs = c * sigma;
 #pragma unroll
