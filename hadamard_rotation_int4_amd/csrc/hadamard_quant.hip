@@ -7,23 +7,31 @@
 // y = z / sqrt(d), scale = fp16(clip * max|y| / 7), q = clamp(rne(y / scale), -8, 7),
 // two codes per byte.  The exact fp32 recipe is stated in include/qr.h.
 //
-// Three kernel families:
+// Kernel families:
 //  * k_hq_pow2   d = 512 .. 8192 (powers of two), one wavefront per row, no LDS
-//                traffic for data.  H_d = H_{d/32} (x) H_32: the H_32 factor runs
-//                on the matrix cores (v_mfma_f32_16x16x32_f16) directly on the
+//                traffic for data.  H_d = H_{d/(32K)} (x) H_K (x) H_32, K = min(4,
+//                d/512): the H_K (x) H_32 factor runs on the matrix cores
+//                (v_mfma_f32_16x16x32_f16, K chained products per output tile,
+//                the H_K signs carried by negated A fragments) directly on the
 //                fp16 input with the signs applied by flipping sign bits, which is
 //                exact (the products are +-x and the accumulation is fp32).  The
-//                remaining log2(d) - 5 butterfly stages run in fp32 VALU: 4 across
-//                lanes through DPP (one v_fmac_f32_dpp per element and stage, with
-//                a per-lane +-1 multiplier) and the rest between registers of a
-//                lane.  amax, scale, rounding and packing follow in registers; the
-//                row makes exactly one HBM round trip.
+//                remaining stages run in fp32 VALU: 4 across lanes through DPP
+//                (one v_fmac_f32_dpp per element and stage, with a per-lane +-1
+//                multiplier) and the rest between registers of a lane.  amax,
+//                scale, rounding and packing follow in registers; the row makes
+//                exactly one HBM round trip, and the next row's loads are in
+//                flight while the current row is transformed.
 //  * k_hq_small  d = 8 .. 256 (and the head-wise K/V path): d/8 lanes per row,
 //                three in-register stages and the rest through lane shuffles.
-//  * k_hq_lds    d = 2^n * m, m in {28, 172}, and quantization without rotation:
-//                one workgroup per row, the row staged in LDS as fp32, the dense
-//                +-1 H_m products on contiguous m-chunks followed by radix-32
-//                butterfly passes in LDS.
+//  * k_hq_k28    d = 1024 * 28: H_4 (x) H_28 on the matrix cores, H_256 in
+//                registers, DPP and one LDS exchange across the workgroup.
+//  * k_hq_k172   d = 64 * 172: H_172 on the matrix cores, H_64 in DPP/registers.
+//  * k_hq_lds    other d = 2^n * m, m in {28, 172}, and quantization without
+//                rotation: one workgroup per row, the row staged in LDS as fp32,
+//                the dense +-1 H_m products on contiguous m-chunks followed by
+//                radix-32 butterfly passes in LDS.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace qr {
@@ -140,14 +148,20 @@ __device__ __forceinline__ int gmap(int c) {
 #ifndef QR_POW2_WAVES_PER_SIMD
 #define QR_POW2_WAVES_PER_SIMD 2
 #endif
-#ifndef QR_POW2_PREFETCH
-#define QR_POW2_PREFETCH 1
+#ifndef QR_POW2_KM
+#define QR_POW2_KM 4
+#endif
+#ifndef QR_POW2_PF_EARLY
+#define QR_POW2_PF_EARLY 8
 #endif
 #ifndef QR_K28_WAVES_PER_SIMD
 #define QR_K28_WAVES_PER_SIMD 2
 #endif
 
-template <int NB, int MODE, bool CLAMP>
+// Buffer-resource cache policy of the streaming accesses (gfx9 "nt" bit).
+#define QR_BUF_POLICY (QR_NT ? 2 : 0)
+
+template <int NB, int MODE, bool CLAMP, bool DBG>
 __global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const uint16_t* __restrict__ x, int64_t T,
                                                  int64_t ld, const int8_t* __restrict__ signs,
                                                  float c, float clip, uint8_t* __restrict__ q,
@@ -155,6 +169,12 @@ __global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const u
                                                  float* __restrict__ zdbg,
                                                  void* __restrict__ yout) {
   constexpr int D = NB * 512;
+  // Blocks of the next row fetched right after the MFMAs; the others are
+  // fetched during quantization, as the registers of the current row free up
+  // (quantization-only kernels: there is no later point, all are early).
+  constexpr int PF_EARLY = (MODE == MODE_QUANT && NB == 16) ? QR_POW2_PF_EARLY : NB;
+  // Blocks combined on the matrix cores (the rest by butterflies in the lane).
+  constexpr int KM = NB < QR_POW2_KM ? NB : QR_POW2_KM;
   __shared__ v4u s_mask[NB * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -184,6 +204,7 @@ __global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const u
     a0[j] = (__builtin_popcount(o0 & k) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
     a1[j] = (__builtin_popcount(o1 & k) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
   }
+  const v8h a0n = -a0, a1n = -a1;
   // DPP stage multipliers: +1 on the lane holding the lower chunk of the pair.
   const float s0 = (gc & 1) ? -1.0f : 1.0f;
   const float s1 = (gc & 2) ? -1.0f : 1.0f;
@@ -192,42 +213,63 @@ __global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const u
   // After the four DPP stages the lane holds sigma * z.
   const float sigma = (__builtin_popcount(gc) & 1) ? -1.0f : 1.0f;
 
-  // The next row's input is fetched into the same registers as soon as the
-  // MFMAs have consumed the current one, so its latency overlaps this row's work.
+  // Rows are addressed through one buffer resource per row (a wave-uniform
+  // base in scalar registers) plus the lane's fixed byte offset, so no 64-bit
+  // per-lane pointers stay live.  Block b of a row sits at scalar offset
+  // 1024 b.  A resource with zero records returns zeros without a fetch.
+  const int voff = lane_off * 2;
+  auto row_rsrc = [&](int64_t r, bool valid) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(x + r * ld), 0, valid ? D * 2 : 0, 0x00020000);
+  };
+
+  // The next row's input is fetched into the same registers block by block as
+  // soon as the MFMAs have consumed the current one, so its latency overlaps
+  // this row's butterflies and quantization.
   const int64_t rstride = (int64_t)gridDim.x * 4;
   int64_t row = (int64_t)blockIdx.x * 4 + wave;
   v4u raw[NB];
-  if (QR_POW2_PREFETCH && row < T) {
+  {
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(row < T ? row : 0, row < T);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) raw[b] = ld_stream(x + row * ld + lane_off + b * 512);
+    for (int b = 0; b < NB; ++b)
+      raw[b] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, b * 1024, QR_BUF_POLICY));
   }
   for (; row < T; row += rstride) {
-    if (!QR_POW2_PREFETCH) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) raw[b] = ld_stream(x + row * ld + lane_off + b * 512);
-    }
+    const bool more = row + rstride < T;
+    const __amdgpu_buffer_rsrc_t rsn = row_rsrc(more ? row + rstride : row, more);
+    // Matrix-core stage over element bits 0..4 and the low log2(KM) block
+    // bits: H_KM (x) H_32 as KM chained MFMAs per output tile, the H_KM signs
+    // carried by the negated A fragments.
     float w[NB][8];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const v4u v = raw[b] ^ s_mask[b * 64 + lane];
-      const v8h bop = __builtin_bit_cast(v8h, v);
-      const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-      const v4f r0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bop, zero, 0, 0, 0);
-      const v4f r1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bop, zero, 0, 0, 0);
+    for (int grp = 0; grp < NB / KM; ++grp) {
+      v8h bop[KM];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w[b][j] = r0[j];
-        w[b][4 + j] = r1[j];
+      for (int kb = 0; kb < KM; ++kb) {
+        const int b = grp * KM + kb;
+        bop[kb] = __builtin_bit_cast(v8h, raw[b] ^ s_mask[b * 64 + lane]);
+        if (b < PF_EARLY)
+          raw[b] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsn, voff, b * 1024, QR_BUF_POLICY));
+      }
+#pragma unroll
+      for (int h = 0; h < KM; ++h) {
+        v4f r0 = {0.0f, 0.0f, 0.0f, 0.0f}, r1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < KM; ++kb) {
+          const bool neg = __builtin_popcount(h & kb) & 1;
+          r0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(neg ? a0n : a0, bop[kb], r0, 0, 0, 0);
+          r1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(neg ? a1n : a1, bop[kb], r1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          w[grp * KM + h][j] = r0[j];
+          w[grp * KM + h][4 + j] = r1[j];
+        }
       }
     }
-    if (QR_POW2_PREFETCH && row + rstride < T) {
-      const uint16_t* xn = x + (row + rstride) * ld + lane_off;
+    // Butterflies over the remaining block bits, inside the lane.
 #pragma unroll
-      for (int b = 0; b < NB; ++b) raw[b] = ld_stream(xn + b * 512);
-    }
-    // Butterflies over the block index (element bits 9 ..), inside the lane.
-#pragma unroll
-    for (int h = 1; h < NB; h <<= 1)
+    for (int h = KM; h < NB; h <<= 1)
 #pragma unroll
       for (int b = 0; b < NB; ++b)
         if (!(b & h))
@@ -237,7 +279,7 @@ __global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const u
             w[b][j] = u + v;
             w[b + h][j] = u - v;
           }
-    if (NB == 1) {
+    if (NB == KM) {
       // keep a compiler-visible VALU op between the MFMA results and the DPP asm
 #pragma unroll
       for (int j = 0; j < 8; ++j) w[0][j] = __fadd_rn(w[0][j], 0.0f);
@@ -252,7 +294,7 @@ __global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const u
 #pragma unroll
     for (int b = 0; b < NB; ++b) QR_DPP8("row_mirror", w[b], s3);
 
-    if (zdbg) {
+    if constexpr (DBG) {
       float* zr = zdbg + row * D + lane_off;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
@@ -263,7 +305,7 @@ __global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const u
       }
     }
 
-    if (MODE == MODE_QUANT) {
+    if constexpr (MODE == MODE_QUANT) {
       float am = 0.0f;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
@@ -273,17 +315,29 @@ __global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const u
       uint16_t sh;
       float m;
       sym_scale(am, c, clip, &sh, &m);
+      sh = (uint16_t)__builtin_amdgcn_readfirstlane(sh);  // the same on every lane
       const float ml = m * sigma;  // w * ml = z * m exactly
-      uint8_t* qr = q + row * (D / 2) + lane_off / 2;
+      const __amdgpu_buffer_rsrc_t rsq =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(q + row * (D / 2)), 0, D / 2, 0x00020000);
+      const int qoff = lane_off / 2;
       // Without clipping |z m| <= 7 (1 + 2^-10) < 7.5 whenever s_h is a normal
       // fp16, so the clamp can be skipped; a subnormal s_h carries a larger
       // relative rounding error and takes the clamped path (wave-uniform branch).
+      // The blocks not fetched early are fetched as their registers free up.
       if (CLAMP || (sh & 0x7fffu) < 0x0400u) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) st_stream((uint32_t*)(qr + b * 256), quant_pack8<true>(w[b], ml));
+        for (int b = 0; b < NB; ++b) {
+          __builtin_amdgcn_raw_buffer_store_b32(quant_pack8<true>(w[b], ml), rsq, qoff, b * 256, QR_BUF_POLICY);
+          if (b >= PF_EARLY)
+            raw[b] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsn, voff, b * 1024, QR_BUF_POLICY));
+        }
       } else {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) st_stream((uint32_t*)(qr + b * 256), quant_pack8<false>(w[b], ml));
+        for (int b = 0; b < NB; ++b) {
+          __builtin_amdgcn_raw_buffer_store_b32(quant_pack8<false>(w[b], ml), rsq, qoff, b * 256, QR_BUF_POLICY);
+          if (b >= PF_EARLY)
+            raw[b] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsn, voff, b * 1024, QR_BUF_POLICY));
+        }
       }
       if (lane == 0) scale[row] = sh;
     } else {
@@ -555,6 +609,7 @@ __global__ __launch_bounds__(256) void k_hq_lds(const uint16_t* __restrict__ x, 
       uint16_t sh;
       float m;
       sym_scale(am, c, clip, &sh, &m);
+      sh = (uint16_t)__builtin_amdgcn_readfirstlane(sh);  // the same on every lane
       // 5. quantize + pack, 8 elements per thread and step
       const bool clamp = CLAMP || (sh & 0x7fffu) < 0x0400u;  // block-uniform
       for (int i = tid * 8; i < d; i += 256 * 8) {
@@ -596,9 +651,6 @@ __global__ __launch_bounds__(256) void k_hq_lds(const uint16_t* __restrict__ x, 
 // LDS for 16-byte stores, which costs two more barriers per row).
 #ifndef QR_K28_ROUNDS
 #define QR_K28_ROUNDS 4
-#endif
-#ifndef QR_K28_DIRECT
-#define QR_K28_DIRECT 1
 #endif
 constexpr int K28_RV = 28 / QR_K28_ROUNDS;             // chunk positions per exchange round
 constexpr int K28_XROUND = 4 * 4 * K28_RV * 64;       // floats per round: [w][ct][RV][lane]
@@ -643,7 +695,7 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
                                                    void* __restrict__ yout) {
   constexpr int D = 28672;
   __shared__ v8h s_afrag[K28_AFRAG];           // 28 KB
-  __shared__ float s_x[K28_XROUND];            // exchange rounds, also the packed-row stage
+  __shared__ float s_x[K28_XROUND];            // exchange rounds
   __shared__ v4u s_sbits[4 * 4 * 64];         // 16 KB
   __shared__ float s_red[4];
   const int tid = threadIdx.x;
@@ -828,39 +880,32 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
       uint16_t sh;
       float m;
       sym_scale(am, c, clip, &sh, &m);
+      // The scale is the same on every lane: make that visible, so that the
+      // clamp decision below is one scalar branch and not a per-lane mask.
+      sh = (uint16_t)__builtin_amdgcn_readfirstlane(sh);
       const float ml = m * sigma;
-      const bool clamp = CLAMP || (sh & 0x7fffu) < 0x0400u;  // block-uniform
-      uint16_t* stage16 = (uint16_t*)s_x;  // packed row, 14 bytes per chunk
+      uint16_t* qrow = (uint16_t*)(q + row * (D / 2));
+      auto emit = [&](auto clamp_tag) {
+        constexpr bool CL = decltype(clamp_tag)::value;
 #pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const int cb = chunk_of(w2) * 7;  // 16-bit word offset of the chunk
-        uint32_t words[4];
+        for (int w2 = 0; w2 < 4; ++w2) {
+          uint32_t words[4];
 #pragma unroll
-        for (int k8 = 0; k8 < 3; ++k8)
-          words[k8] = clamp ? quant_pack8<true>(&o[w2][8 * k8], ml)
-                            : quant_pack8<false>(&o[w2][8 * k8], ml);
-        float tail[8] = {o[w2][24], o[w2][25], o[w2][26], o[w2][27], 0.0f, 0.0f, 0.0f, 0.0f};
-        words[3] = clamp ? quant_pack8<true>(tail, ml) : quant_pack8<false>(tail, ml);
-        if (QR_K28_DIRECT) {
-          uint16_t* qc = (uint16_t*)(q + row * (D / 2)) + cb;
+          for (int k8 = 0; k8 < 3; ++k8) words[k8] = quant_pack8<CL>(&o[w2][8 * k8], ml);
+          float tail[8] = {o[w2][24], o[w2][25], o[w2][26], o[w2][27], 0.0f, 0.0f, 0.0f, 0.0f};
+          words[3] = quant_pack8<CL>(tail, ml);
+          uint16_t* qc = qrow + chunk_of(w2) * 7;  // 14 bytes of packed codes per chunk
 #pragma unroll
           for (int k = 0; k < 7; ++k)
             __builtin_nontemporal_store(
                 (uint16_t)((k & 1) ? (words[k >> 1] >> 16) : (words[k >> 1] & 0xffffu)), qc + k);
-        } else {
-#pragma unroll
-          for (int k = 0; k < 7; ++k)
-            stage16[cb + k] = (uint16_t)((k & 1) ? (words[k >> 1] >> 16) : (words[k >> 1] & 0xffffu));
         }
-      }
-      if (!QR_K28_DIRECT) {
-        __syncthreads();
-        const uint32_t* st32 = (const uint32_t*)s_x;
-        uint32_t* qr32 = (uint32_t*)(q + row * (D / 2));
-        for (int i = tid; i < D / 8; i += 256) st_stream(qr32 + i, st32[i]);
-      }
+      };
+      if (CLAMP || (sh & 0x7fffu) < 0x0400u)
+        emit(std::true_type{});
+      else
+        emit(std::false_type{});
       if (tid == 0) scale[row] = sh;
-      if (!QR_K28_DIRECT) __syncthreads();  // the stage aliases the next row's exchange buffer
     } else {
       const float cs = c * sigma;
 #pragma unroll
@@ -1073,6 +1118,7 @@ __global__ __launch_bounds__(256, 2) void k_hq_k172(const uint16_t* __restrict__
       uint16_t sh;
       float m;
       sym_scale(am, c, clip, &sh, &m);
+      sh = (uint16_t)__builtin_amdgcn_readfirstlane(sh);  // the same on every lane
       const float ml = m * sigma;
       const bool clamp = CLAMP || (sh & 0x7fffu) < 0x0400u;  // block-uniform
 #pragma unroll
@@ -1136,14 +1182,18 @@ static qr_status launch_pow2(int nb, const uint16_t* x, int64_t T, int64_t ld, c
                              float c, float clip, uint8_t* q, uint16_t* sc, float* z, void* y,
                              hipStream_t st) {
 #ifndef QR_POW2_GRID
-#define QR_POW2_GRID 1024
+#define QR_POW2_GRID 512
 #endif
   const int grid = grid_for(T, 4, QR_POW2_GRID);
   switch (nb) {
 #define QR_CASE(NBV)                                                                   \
   case NBV:                                                                            \
-    hipLaunchKernelGGL((k_hq_pow2<NBV, MODE, CLAMP>), dim3(grid), dim3(256), 0, st, x, T, ld, s, \
-                       c, clip, q, sc, z, y);                                          \
+    if (z)                                                                             \
+      hipLaunchKernelGGL((k_hq_pow2<NBV, MODE, CLAMP, true>), dim3(grid), dim3(256), 0, st, x, T, \
+                         ld, s, c, clip, q, sc, z, y);                                 \
+    else                                                                               \
+      hipLaunchKernelGGL((k_hq_pow2<NBV, MODE, CLAMP, false>), dim3(grid), dim3(256), 0, st, x, \
+                         T, ld, s, c, clip, q, sc, z, y);                              \
     break;
     QR_CASE(1)
     QR_CASE(2)
