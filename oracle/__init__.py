@@ -25,6 +25,10 @@ LLMs Impossible"):
 * ``kv``: head-wise rotation of keys and queries and asymmetric group-wise
   4-bit KV quantization (QuaRot paper, keys/queries paragraph and the
   implementation paragraph on clipping ratios and group size 128).
+* ``attention``: the Decode routine, softmax attention of one query per
+  sequence over the dequantized 4-bit cache, with grouped-query heads (QuaRot
+  paper, attention paragraph and its attention routines: Init, Append,
+  Decode).
 
 Two modes exist where floating point is involved.  "Math" functions work in
 float64 throughout.  "Recipe" functions follow the fp32 step sequence that the
