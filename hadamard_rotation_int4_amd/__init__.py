@@ -17,6 +17,7 @@ Functions (same names as the C entry points without the ``qr_`` prefix):
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from pathlib import Path
 
@@ -53,6 +54,11 @@ def _load():
     lib.qr_kv_rotate_quant.restype = ctypes.c_int
     lib.qr_kv_rotate_quant.argtypes = [vp, i32, i32, i32, i32, i64, ctypes.c_int, vp, i32, f32,
                                        vp, vp, i32, i32, vp, vp]
+    lib.qr_kv_decode_workspace_bytes.restype = i64
+    lib.qr_kv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.qr_kv_decode_attention.restype = ctypes.c_int
+    lib.qr_kv_decode_attention.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32, i32,
+                                           f32, vp, vp, i64, vp]
     _lib = lib
     return lib
 
@@ -238,3 +244,48 @@ def kv_rotate_quant(kv, signs, group: int, clip_ratio: float, cache_q, cache_met
                                       _stream(stream))
     _check(code, "qr_kv_rotate_quant")
     return z
+
+
+def kv_decode_workspace_bytes(B: int, Hq: int, Hkv: int, Dh: int, L: int) -> int:
+    return int(_load().qr_kv_decode_workspace_bytes(B, Hq, Hkv, Dh, L))
+
+
+def kv_decode_attention(q, k_cache_q, k_cache_meta, v_cache_q, v_cache_meta, L: int,
+                        group: int = 128, softmax_scale: float | None = None, out=None,
+                        workspace=None, stream=None):
+    """Decode attention of q fp16 [B, Hq, Dh] over positions 0 .. L-1 of the 4-bit cache.
+
+    Caches as qr_kv_rotate_quant writes them: codes uint8 [B, Hkv, S_max, Dh/2],
+    meta fp16 [B, Hkv, S_max, Dh/group, 2].  Returns fp16 [B, Hq, Dh].
+    """
+    torch = _torch()
+    _need(q, torch.float16, "q", 3)
+    for t, nm in ((k_cache_q, "k_cache_q"), (v_cache_q, "v_cache_q")):
+        _need(t, torch.uint8, nm, 4)
+    for t, nm in ((k_cache_meta, "k_cache_meta"), (v_cache_meta, "v_cache_meta")):
+        _need(t, torch.float16, nm, 5)
+    B, Hq, Dh = q.shape
+    _, Hkv, S_max, _ = k_cache_q.shape
+    for t in (q, k_cache_q, v_cache_q, k_cache_meta, v_cache_meta):
+        if not t.is_contiguous():
+            raise ValueError("q and the cache tensors must be contiguous")
+    if tuple(k_cache_q.shape) != (B, Hkv, S_max, Dh // 2) or tuple(v_cache_q.shape) != tuple(k_cache_q.shape) \
+            or tuple(k_cache_meta.shape) != (B, Hkv, S_max, Dh // group, 2) \
+            or tuple(v_cache_meta.shape) != tuple(k_cache_meta.shape):
+        raise ValueError("cache tensors have the wrong shape")
+    scale = float(softmax_scale) if softmax_scale is not None else 1.0 / math.sqrt(Dh)
+    o = out if out is not None else torch.empty((B, Hq, Dh), dtype=torch.float16, device=q.device)
+    if out is not None:
+        _need(o, torch.float16, "out", 3)
+        if tuple(o.shape) != (B, Hq, Dh) or not o.is_contiguous():
+            raise ValueError("out must be a contiguous fp16 [B, Hq, Dh] tensor")
+    nbytes = kv_decode_workspace_bytes(B, Hq, Hkv, Dh, int(L)) if B > 0 else 0
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 4),), dtype=torch.uint8, device=q.device)
+    code = _load().qr_kv_decode_attention(_ptr(q), B, Hq, Hkv, Dh, _ptr(k_cache_q),
+                                          _ptr(k_cache_meta), _ptr(v_cache_q), _ptr(v_cache_meta),
+                                          S_max, int(L), int(group), scale, _ptr(o),
+                                          _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          _stream(stream))
+    _check(code, "qr_kv_decode_attention")
+    return o

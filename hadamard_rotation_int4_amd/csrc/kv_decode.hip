@@ -1,0 +1,352 @@
+// Decode routine: attention of one new query per sequence over the 4-bit
+// K/V cache (qr_kv_decode_attention), for gfx950.
+//
+// What is computed (QuaRot paper, attention paragraph and its attention
+// routines Init / Append / Decode): for batch b, query head hq and its KV head
+// h = hq / (Hq / Hkv), over cache positions j < L,
+//   k_j = code * scale + min, v_j likewise (asymmetric 4-bit, one group per head),
+//   s_j = softmax_scale * q . k_j,   o = sum_j softmax(s)_j v_j.
+// The query arrives in fp16 and rotated like the keys, so q . k is the score of
+// the unrotated model; the pages keep queries in FP16, dequantize each loaded
+// segment of the cache and use an online softmax (flash attention).
+//
+// Design (MI355X first):
+//  * Flash-decoding split: workgroup (split, h, b) streams `cpw` chunks of 256
+//    cached positions of one KV head for all Hq / Hkv <= 16 query heads that
+//    share it, with an online softmax across its chunks, and writes one
+//    partial record (running max, sum, unnormalised output) per query head;
+//    k_kv_decode_combine merges the records of a head.
+//  * Both products run on the matrix cores (v_mfma_f32_16x16x32_f16) on exact
+//    operands.  A 4-bit code c enters as the fp16 number 1024 + c (bit pattern
+//    0x6400 | c: one v_perm and one and-or per pair of codes); the constant
+//    and the scale / min of the position are applied around the product, in
+//    fp32:  q . k_j = scale_j (q . (1024 + c_j) - 1024 sum(q)) + min_j sum(q).
+//    The MFMA accumulator starts at -1024 sum(q), so it ends at q . c_j.
+//  * Scores: keys are the M index (16 per tile, lane-major), query heads the N
+//    index, head dimensions the contraction; lane (head n, g) ends with the
+//    scores of positions 4 g .. 4 g + 3 of each tile.
+//  * Values: the product P V contracts over positions, which the cache holds
+//    row-wise.  Each 16-position tile is transposed on the matrix cores by a
+//    0/1 selection matrix (T = V_tile x Sel - 1024 = the codes, exact), which
+//    leaves position 4 g + r in register r of lane (dim, g): exactly the
+//    B-operand layout of P V for the position order the scores already have.
+//  * P' = p * scale_v is split into fp16 hi + lo parts (two MFMAs), so the
+//    weights keep about 22 bits; sum_j p_j min_j is added in fp32.
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace qr {
+
+constexpr int KD_DH = 128;     // head dimension
+constexpr int KD_CHUNK = 256;  // positions per workgroup pass: 4 wavefronts x 4 tiles x 16
+constexpr int KD_TARGET_WG = 2048;
+
+struct KdPlan {
+  int chunks, cpw, splits;
+};
+static KdPlan kd_plan(int64_t B, int64_t Hkv, int64_t L) {
+  KdPlan p;
+  p.chunks = (int)((L + KD_CHUNK - 1) / KD_CHUNK);
+  const int64_t pairs = B * Hkv;
+  int64_t want = (KD_TARGET_WG + pairs - 1) / pairs;
+  if (want < 1) want = 1;
+  const int splits0 = (int)(want < p.chunks ? want : p.chunks);
+  p.cpw = (p.chunks + splits0 - 1) / splits0;
+  p.splits = (p.chunks + p.cpw - 1) / p.cpw;
+  return p;
+}
+
+// Packed 4-bit codes (8 per dword: code 2i in the low nibble of byte i) ->
+// 8 fp16 values 1024 + code in the element order (0, 2, 1, 3, 4, 6, 5, 7).
+__device__ __forceinline__ v8h codes8_f16(uint32_t x) {
+  const uint32_t t0 = __builtin_amdgcn_perm(0u, x, 0x0c010c00u);  // [b0, 0, b1, 0]
+  const uint32_t t1 = __builtin_amdgcn_perm(0u, x, 0x0c030c02u);  // [b2, 0, b3, 0]
+  v4u r;
+  r[0] = (t0 & 0x000F000Fu) | 0x64006400u;         // codes 0, 2
+  r[1] = ((t0 >> 4) & 0x000F000Fu) | 0x64006400u;  // codes 1, 3
+  r[2] = (t1 & 0x000F000Fu) | 0x64006400u;         // codes 4, 6
+  r[3] = ((t1 >> 4) & 0x000F000Fu) | 0x64006400u;  // codes 5, 7
+  return __builtin_bit_cast(v8h, r);
+}
+
+__device__ __forceinline__ float fp16_lo(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float fp16_hi(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
+
+// Head dimension held by lane n' of output tile (kb, hs) after the transpose.
+__device__ __forceinline__ int kd_dim(int kb, int hs, int np) {
+  const int e = np & 7;
+  const int sig = (e == 1 || e == 2 || e == 5 || e == 6) ? (e ^ 3) : e;  // 0 2 1 3 4 6 5 7
+  return 32 * (2 * hs + (np >> 3)) + 8 * kb + sig;
+}
+
+__global__ __launch_bounds__(256) void k_kv_decode(
+    const uint16_t* __restrict__ q, int Hq, int Hkv, int GQ, const uint8_t* __restrict__ kc,
+    const uint32_t* __restrict__ km, const uint8_t* __restrict__ vc,
+    const uint32_t* __restrict__ vm, int S_max, int L, float scale_log2e, int chunks, int cpw,
+    int splits, float* __restrict__ ws) {
+  __shared__ float s_wmax[2][4][16];
+  __shared__ __attribute__((aligned(16))) uint32_t s_meta[4][2][64];
+  __shared__ float s_o[4][16][KD_DH];
+  __shared__ float s_l[4][16], s_ms[4][16], s_mrun[16];
+
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+
+  // This (b, h)'s cache rows; positions >= L are outside the resources and read as zero.
+  const int64_t row0 = ((int64_t)b * Hkv + h) * S_max;
+  const __amdgpu_buffer_rsrc_t rs_kc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(kc + row0 * 64), 0, L * 64, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_vc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(vc + row0 * 64), 0, L * 64, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_km =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(km + row0), 0, L * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_vm =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(vm + row0), 0, L * 4, 0x00020000);
+
+  // ---- query fragments (B operand of the scores): lane (head n, g), block kb
+  //      holds dims 32 g + 8 kb + (0, 2, 1, 3, 4, 6, 5, 7); heads >= GQ are zero ----
+  v8h qf[4];
+  float qsum = 0.0f;
+  {
+    const bool real = n < GQ;
+    const uint16_t* qh = q + ((int64_t)b * Hq + (int64_t)h * GQ + (real ? n : 0)) * KD_DH + 32 * g;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      v4u raw = real ? *(const v4u*)(qh + 8 * kb) : v4u{0u, 0u, 0u, 0u};
+      v4u o;
+      o[0] = __builtin_amdgcn_perm(raw[1], raw[0], 0x05040100u);
+      o[1] = __builtin_amdgcn_perm(raw[1], raw[0], 0x07060302u);
+      o[2] = __builtin_amdgcn_perm(raw[3], raw[2], 0x05040100u);
+      o[3] = __builtin_amdgcn_perm(raw[3], raw[2], 0x07060302u);
+      qf[kb] = __builtin_bit_cast(v8h, o);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qsum += fp16_lo(raw[i]) + fp16_hi(raw[i]);
+    }
+    qsum += __shfl_xor(qsum, 16);
+    qsum += __shfl_xor(qsum, 32);
+  }
+  const float qc = -1024.0f * qsum;
+
+  // Selection matrices of the transpose: Sel_hs[k = 8 g + j][n'] = 1 iff
+  // g == 2 hs + (n' >> 3) and j == (n' & 7).
+  v8h sel[2];
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      sel[hs][j] = (g == 2 * hs + (n >> 3) && j == (n & 7)) ? (_Float16)1.0f : (_Float16)0.0f;
+
+  // Running state: max (log2 domain) for head n and for heads 4 g + r (the
+  // output rows this lane accumulates), lane-partial sums of p and p * min_v.
+  float m_n = -INFINITY, m_r[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float l_n = 0.0f, ms_n = 0.0f;
+  v4f O[4][2];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) O[kb][hs] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int c0 = split * cpw, c1 = min(chunks, c0 + cpw);
+  for (int c = c0; c < c1; ++c) {
+    const int par = c & 1;
+    const int kw = c * KD_CHUNK + 64 * w;  // first position of this wavefront's 64
+    // ---- loads: codes of tile t (lane m = position 16 t + n, 16 bytes = dims
+    //      32 g .. 32 g + 31), one metadata word per lane ----
+    v4u kraw[4], vraw[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int off = (kw + 16 * t + n) * 64 + 16 * g;
+      kraw[t] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs_kc, off, 0, 0));
+      vraw[t] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs_vc, off, 0, 0));
+    }
+    s_meta[w][0][lane] = __builtin_amdgcn_raw_buffer_load_b32(rs_km, (kw + lane) * 4, 0, 0);
+    s_meta[w][1][lane] = __builtin_amdgcn_raw_buffer_load_b32(rs_vm, (kw + lane) * 4, 0, 0);
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- scores of tile t: lane (head n, g) gets positions 16 t + 4 g + r ----
+    float sc[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      v4f acc = {qc, qc, qc, qc};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_f16(kraw[t][kb]), qf[kb], acc, 0, 0, 0);
+      const v4u kmeta = *(const v4u*)&s_meta[w][0][16 * t + 4 * g];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pos = kw + 16 * t + 4 * g + r;
+        const float s = fp16_lo(kmeta[r]), mn = fp16_hi(kmeta[r]);
+        sc[t][r] = pos < L ? scale_log2e * fmaf(s, acc[r], mn * qsum) : -INFINITY;
+        mx = fmaxf(mx, sc[t][r]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (g == 0) s_wmax[par][w][n] = mx;
+    __syncthreads();
+
+    // ---- online softmax update (the chunk's first position is < L, so the
+    //      new maxima are finite) ----
+    auto chunk_max = [&](int hd) {
+      return fmaxf(fmaxf(s_wmax[par][0][hd], s_wmax[par][1][hd]),
+                   fmaxf(s_wmax[par][2][hd], s_wmax[par][3][hd]));
+    };
+    const float mnew_n = fmaxf(m_n, chunk_max(n));
+    const float a_n = exp2f(m_n - mnew_n);
+    m_n = mnew_n;
+    l_n *= a_n;
+    ms_n *= a_n;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mnew = fmaxf(m_r[r], chunk_max(4 * g + r));
+      const float a = exp2f(m_r[r] - mnew);
+      m_r[r] = mnew;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) O[kb][hs][r] *= a;
+    }
+
+    // ---- weights P' = p * scale_v as fp16 hi + lo, A operands of P V: block
+    //      kp = tiles (2 kp, 2 kp + 1), element j -> position 4 g + (j & 3) of
+    //      tile 2 kp + (j >> 2) ----
+    v8h ph[2], pl[2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const v4u vmeta = *(const v4u*)&s_meta[w][1][16 * t + 4 * g];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = exp2f(sc[t][r] - m_n);
+        l_n += p;
+        ms_n = fmaf(p, fp16_hi(vmeta[r]), ms_n);
+        const float pp = p * fp16_lo(vmeta[r]);
+        const _Float16 hi = (_Float16)pp;
+        ph[t >> 1][4 * (t & 1) + r] = hi;
+        pl[t >> 1][4 * (t & 1) + r] = (_Float16)(pp - (float)hi);
+      }
+    }
+
+    // ---- P V: transpose each value tile on the matrix cores, then multiply ----
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const v8h va = codes8_f16(vraw[2 * kp][kb]);
+        const v8h vb = codes8_f16(vraw[2 * kp + 1][kb]);
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          const v4f cneg = {-1024.0f, -1024.0f, -1024.0f, -1024.0f};
+          const v4f ta = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, sel[hs], cneg, 0, 0, 0);
+          const v4f tb = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb, sel[hs], cneg, 0, 0, 0);
+          v8h bop;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            bop[r] = (_Float16)ta[r];
+            bop[4 + r] = (_Float16)tb[r];
+          }
+          O[kb][hs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[kp], bop, O[kb][hs], 0, 0, 0);
+          O[kb][hs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[kp], bop, O[kb][hs], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- combine the wavefronts (they share the running maxima) and write the
+  //      partial record of every query head: max, sum, unnormalised output ----
+  l_n += __shfl_xor(l_n, 16);
+  l_n += __shfl_xor(l_n, 32);
+  ms_n += __shfl_xor(ms_n, 16);
+  ms_n += __shfl_xor(ms_n, 32);
+  if (g == 0) {
+    s_l[w][n] = l_n;
+    s_ms[w][n] = ms_n;
+    if (w == 0) s_mrun[n] = m_n;
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_o[w][4 * g + r][kd_dim(kb, hs, n)] = O[kb][hs][r];
+  __syncthreads();
+  for (int i = tid; i < GQ * KD_DH; i += 256) {
+    const int hd = i / KD_DH, d = i % KD_DH;
+    const float ms = s_ms[0][hd] + s_ms[1][hd] + s_ms[2][hd] + s_ms[3][hd];
+    float* rec = ws + (((int64_t)b * Hq + (int64_t)h * GQ + hd) * splits + split) * (KD_DH + 2);
+    rec[2 + d] = s_o[0][hd][d] + s_o[1][hd][d] + s_o[2][hd][d] + s_o[3][hd][d] + ms;
+    if (d == 0) {
+      rec[0] = s_mrun[hd];
+      rec[1] = s_l[0][hd] + s_l[1][hd] + s_l[2][hd] + s_l[3][hd];
+    }
+  }
+}
+
+// Merge the split records of one query head: o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+__global__ __launch_bounds__(KD_DH) void k_kv_decode_combine(const float* __restrict__ ws,
+                                                             int splits,
+                                                             uint16_t* __restrict__ out) {
+  const int64_t head = blockIdx.x;  // b * Hq + hq
+  const int d = threadIdx.x;
+  const float* rec = ws + head * splits * (KD_DH + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, rec[s * (KD_DH + 2)]);
+  float l = 0.0f, o = 0.0f;
+  for (int s = 0; s < splits; ++s) {
+    const float* r = rec + s * (KD_DH + 2);
+    const float a = exp2f(r[0] - M);
+    l = fmaf(r[1], a, l);
+    o = fmaf(r[2 + d], a, o);
+  }
+  out[head * KD_DH + d] = f2h(o / l);
+}
+
+}  // namespace qr
+
+using namespace qr;
+
+extern "C" int64_t qr_kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dh,
+                                                int32_t L) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Dh < 1 || L < 1) return 0;
+  const KdPlan p = kd_plan(B, Hkv, L);
+  return (int64_t)B * Hq * p.splits * (Dh + 2) * (int64_t)sizeof(float);
+}
+
+extern "C" qr_status qr_kv_decode_attention(const void* q_f16, int32_t B, int32_t Hq,
+                                            int32_t Hkv, int32_t Dh, const void* k_cache_q,
+                                            const void* k_cache_meta, const void* v_cache_q,
+                                            const void* v_cache_meta, int32_t S_max, int32_t L,
+                                            int32_t group, float softmax_scale, void* out_f16,
+                                            void* workspace, int64_t workspace_bytes,
+                                            hipStream_t stream) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || S_max < 1 || L < 1 || L > S_max) return QR_ERR_SHAPE;
+  if (Hq % Hkv != 0) return QR_ERR_SHAPE;
+  if (Dh != KD_DH || group != KD_DH || Hq / Hkv > 16) return QR_ERR_UNSUPPORTED;
+  if (!(softmax_scale > 0.0f) || !(softmax_scale < 1e30f)) return QR_ERR_ARG;
+  if ((int64_t)S_max * 64 > INT32_MAX) return QR_ERR_SHAPE;
+  if (B == 0) return QR_OK;
+  if (!q_f16 || !k_cache_q || !k_cache_meta || !v_cache_q || !v_cache_meta || !out_f16 ||
+      !workspace)
+    return QR_ERR_NULL;
+  if (workspace_bytes < qr_kv_decode_workspace_bytes(B, Hq, Hkv, Dh, L)) return QR_ERR_SHAPE;
+  if (!aligned(q_f16, 16) || !aligned(k_cache_q, 16) || !aligned(v_cache_q, 16) ||
+      !aligned(k_cache_meta, 4) || !aligned(v_cache_meta, 4) || !aligned(out_f16, 2) ||
+      !aligned(workspace, 4))
+    return QR_ERR_ALIGN;
+  const KdPlan p = kd_plan(B, Hkv, L);
+  if ((int64_t)B * Hq > INT32_MAX || B > 65535 || Hkv > 65535) return QR_ERR_SHAPE;
+  const float scale_log2e = softmax_scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(k_kv_decode, dim3(p.splits, Hkv, B), dim3(256), 0, stream,
+                     (const uint16_t*)q_f16, Hq, Hkv, Hq / Hkv, (const uint8_t*)k_cache_q,
+                     (const uint32_t*)k_cache_meta, (const uint8_t*)v_cache_q,
+                     (const uint32_t*)v_cache_meta, S_max, L, scale_log2e, p.chunks, p.cpw,
+                     p.splits, (float*)workspace);
+  qr_status st = launch_status();
+  if (st != QR_OK) return st;
+  hipLaunchKernelGGL(k_kv_decode_combine, dim3((unsigned)(B * Hq)), dim3(KD_DH), 0, stream,
+                     (const float*)workspace, p.splits, (uint16_t*)out_f16);
+  return launch_status();
+}

@@ -15,7 +15,10 @@
  *     QuaRot paper, activation-quantization and performance paragraphs;
  *   - post-RoPE head-wise rotation of queries and keys, asymmetric group-128
  *     KV quantization with Init/Append routines: QuaRot paper, keys/queries
- *     paragraph, implementation paragraph, attention-routines paragraph.
+ *     paragraph, implementation paragraph, attention-routines paragraph;
+ *   - the Decode routine, flash-style attention of the FP16 query over the
+ *     dequantized cache: QuaRot paper, attention paragraph and attention
+ *     routines.
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
@@ -165,6 +168,42 @@ qr_status qr_kv_rotate_quant(const void* kv_f16, int32_t B, int32_t S_new, int32
                              int64_t ld_token, qr_rot rot, const int8_t* signs, int32_t group,
                              float clip_ratio, void* cache_q, void* cache_meta, int32_t S_max,
                              int32_t start_pos, float* z_dbg, hipStream_t stream);
+
+/*
+ * Decode routine (QuaRot paper, attention routines Init / Append / Decode):
+ * attention of one new query per sequence over the 4-bit K/V cache that
+ * qr_kv_rotate_quant wrote, for grouped-query heads.  For batch b, query head
+ * hq and its KV head h = hq / (Hq / Hkv), over cache positions j = 0 .. L-1:
+ *   k_j = code * scale + min, v_j likewise (the cache's (scale, min) pair),
+ *   s_j = softmax_scale * (q[b, hq] . k_j),   out[b, hq] = sum_j softmax(s)_j v_j.
+ * The query must carry the same head-wise rotation as the cached keys (for
+ * example qr_hadamard on the post-RoPE queries with the keys' signs); values
+ * are used as cached.
+ *   q_f16        [B, Hq, Dh] fp16, contiguous.
+ *   k_cache_q, v_cache_q        [B, Hkv, S_max, Dh/2] uint8 packed codes.
+ *   k_cache_meta, v_cache_meta  [B, Hkv, S_max, Dh/group, 2] fp16 (scale, min).
+ *   L            positions used, 1 <= L <= S_max (the same for every sequence).
+ *   out_f16      [B, Hq, Dh] fp16 (output, contiguous).
+ *   workspace    caller-owned device scratch of at least
+ *                qr_kv_decode_workspace_bytes(B, Hq, Hkv, Dh, L) bytes: fp32
+ *                partial results of the split over positions; its contents on
+ *                entry do not matter and are overwritten.  Calls that overlap on
+ *                one workspace race.
+ * Arithmetic: q . k_j and the weights are formed in fp32 from exact fp16
+ * operands (codes are exact; scale and min are applied in fp32), softmax in
+ * fp32 with exp2, weights * value scale carried as two fp16 parts; the output
+ * is rounded once to fp16.
+ * Requirements: Dh = 128, group = 128, Hq % Hkv == 0, Hq / Hkv <= 16,
+ * softmax_scale > 0; q_f16, k_cache_q and v_cache_q 16-byte aligned, the
+ * metadata and the workspace 4-byte aligned.  B == 0 returns QR_OK.
+ */
+int64_t qr_kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dh, int32_t L);
+
+qr_status qr_kv_decode_attention(const void* q_f16, int32_t B, int32_t Hq, int32_t Hkv, int32_t Dh,
+                                 const void* k_cache_q, const void* k_cache_meta,
+                                 const void* v_cache_q, const void* v_cache_meta, int32_t S_max,
+                                 int32_t L, int32_t group, float softmax_scale, void* out_f16,
+                                 void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -32,6 +32,7 @@ def lib():
 def test_header_declares_the_path():
     names = declared_functions()
     for must in ("qr_hadamard_quant", "qr_hadamard", "qr_w4a4_gemm", "qr_kv_rotate_quant",
+                 "qr_kv_decode_attention", "qr_kv_decode_workspace_bytes",
                  "qr_hadamard_factor", "qr_status_str", "qr_abi_version"):
         assert must in names
 
@@ -141,6 +142,32 @@ def test_kv_validation(lib):
     assert kvq(lib, kv=None) == QR_ERR_NULL
     assert kvq(lib, cq=A16 + 2) == QR_ERR_ALIGN
     assert kvq(lib, ld=1028) == QR_ERR_ALIGN
+
+
+def kvd(lib, q=A16, B=2, Hq=16, Hkv=2, Dh=128, kq=A16, km=A16, vq=A16, vm=A16, S_max=300, L=260,
+        group=128, scale=0.088, out=A16, ws=A16, wsb=1 << 30):
+    return lib.qr_kv_decode_attention(q, B, Hq, Hkv, Dh, kq, km, vq, vm, S_max, L, group, scale,
+                                      out, ws, wsb, None)
+
+
+def test_kv_decode_validation(lib):
+    assert lib.qr_kv_decode_workspace_bytes(2, 16, 2, 128, 260) > 0
+    assert lib.qr_kv_decode_workspace_bytes(0, 16, 2, 128, 260) == 0
+    assert kvd(lib, B=0) == QR_OK
+    assert kvd(lib, L=0) == QR_ERR_SHAPE
+    assert kvd(lib, L=301) == QR_ERR_SHAPE              # past the cache
+    assert kvd(lib, Hq=15) == QR_ERR_SHAPE              # not a multiple of Hkv
+    assert kvd(lib, Dh=64) == QR_ERR_UNSUPPORTED
+    assert kvd(lib, group=64) == QR_ERR_UNSUPPORTED
+    assert kvd(lib, Hq=64, Hkv=2) == QR_ERR_UNSUPPORTED  # 32 query heads per KV head
+    assert kvd(lib, scale=0.0) == QR_ERR_ARG
+    assert kvd(lib, scale=float("nan")) == QR_ERR_ARG
+    assert kvd(lib, q=None) == QR_ERR_NULL
+    assert kvd(lib, ws=None) == QR_ERR_NULL
+    need = lib.qr_kv_decode_workspace_bytes(2, 16, 2, 128, 260)
+    assert kvd(lib, wsb=need - 4) == QR_ERR_SHAPE
+    assert kvd(lib, kq=A16 + 4) == QR_ERR_ALIGN
+    assert kvd(lib, km=A16 + 2) == QR_ERR_ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

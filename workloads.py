@@ -161,6 +161,24 @@ def positive_scales(workload_id: int, tensor_id: int, n: int, lo: float = 1e-3,
     return np.exp(g.uniform(np.log(lo), np.log(hi), size=n)).astype(F16)
 
 
+def kv_cache_random(workload_id: int, tensor_id: int, b: int, h: int, s_max: int, dh: int,
+                    group: int, scale_lo: float = 0.01, scale_hi: float = 0.2,
+                    min_lo: float = -1.5, min_hi: float = 0.0):
+    """A filled 4-bit cache: uniformly random packed codes uint8 [b, h, s_max, dh/2] and
+    fp16 (scale, min) pairs [b, h, s_max, dh/group, 2] drawn uniformly in the given ranges."""
+    g = rng(workload_id, 600 + tensor_id)
+    codes = g.integers(0, 256, size=(b, h, s_max, dh // 2), dtype=np.uint8)
+    meta = np.stack([g.uniform(scale_lo, scale_hi, size=(b, h, s_max, dh // group)),
+                     g.uniform(min_lo, min_hi, size=(b, h, s_max, dh // group))], axis=-1)
+    return codes, meta.astype(F16)
+
+
+def queries(workload_id: int, tensor_id: int, b: int, h: int, dh: int, std: float = 1.0):
+    """fp16 [b, h, dh] ~ N(0, std^2): one decoding query per sequence."""
+    g = rng(workload_id, 700 + tensor_id)
+    return (g.standard_normal((b, h, dh)) * std).astype(F16)
+
+
 # ---------------------------------------------------------------------------
 # torch generators (large tensors, generated on the device)
 # ---------------------------------------------------------------------------
@@ -196,3 +214,15 @@ def kv_tensor_torch(torch, device, workload_id: int, tensor_id: int, b: int, s: 
     dims = rng(workload_id, 300 + tensor_id).integers(0, dh, size=h)
     x[:, :, torch.arange(h, device=device), torch.as_tensor(dims, device=device)] *= outlier
     return x.to(torch.float16)
+
+
+def kv_cache_random_torch(torch, device, workload_id: int, tensor_id: int, b: int, h: int,
+                          s_max: int, dh: int, group: int, scale_lo: float = 0.01,
+                          scale_hi: float = 0.2, min_lo: float = -1.5, min_hi: float = 0.0):
+    g = _torch_gen(torch, device, workload_id, 600 + tensor_id)
+    codes = torch.randint(0, 256, (b, h, s_max, dh // 2), generator=g, device=device,
+                          dtype=torch.uint8)
+    u = torch.rand((b, h, s_max, dh // group, 2), generator=g, device=device, dtype=torch.float32)
+    lo = torch.tensor([scale_lo, min_lo], device=device)
+    hi = torch.tensor([scale_hi, min_hi], device=device)
+    return codes, (lo + u * (hi - lo)).to(torch.float16)
