@@ -16,8 +16,9 @@ One step is one pass of the whole hot path over one batch of synthetic input
   the head-wise rotation of Q.
 * 7b_decode: the same four rotations and five GEMMs at T = 1, 8, 32 and 64.
 * 70b_kv: K/V Init of a 32 x 2048-token prompt (8 KV heads of 128), the
-  rotation of its queries (64 heads), then 50 decode steps of Append K, V and
-  rotate one query token.
+  rotation of its queries (64 heads), then 50 decode steps of Append K, V,
+  rotate one query token and the Decode attention of that query over the
+  4-bit cache (2049 .. 2098 positions).
 
 Prints one JSON line.  ``value`` is the step's GEMM int-ops per second (TOPS)
 for the prefill workloads and its algorithmic HBM bytes per second (GB/s) for
@@ -51,7 +52,8 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POP/s)
 METRIC = "fused Hadamard+INT4-quant HBM GB/s; W4A4 GEMM TOPS at Llama-2 shapes"
 CSRC = ROOT / "hadamard_rotation_int4_amd" / "csrc"
 KERNEL_SOURCE = {"w4a4_gemm": "w4a4_gemm.hip", "hadamard_quant": "hadamard_quant.hip",
-                 "kv_rotate_quant": "kv_quant.hip", "hadamard": "hadamard_quant.hip"}
+                 "kv_rotate_quant": "kv_quant.hip", "hadamard": "hadamard_quant.hip",
+                 "kv_decode_attention": "kv_decode.hip"}
 
 
 def parse():
@@ -94,6 +96,12 @@ def kv_bytes(rows, dh, group):
 def rot_bytes(rows, dh):
     """Rotation only, fp16 in and out."""
     return rows * 4 * dh
+
+
+def decode_bytes(b, hkv, hq, L, dh, group):
+    """Decode routine: the K and V caches of L positions (packed codes + fp16 (scale, min)
+    per group) read once, the fp16 queries in and the fp16 outputs out."""
+    return 2 * b * hkv * L * (dh // 2 + 4 * (dh // group)) + 2 * 2 * b * hq * dh
 
 
 # ---------------------------------------------------------------------------
@@ -177,6 +185,9 @@ def make_kv_decode(torch, qr, wl, W, dev):
          ("hadamard", "q:prompt", rot_bytes(B * P * Hq, Dh), 0,
           lambda: qr.hadamard(qp, s, torch.float16, out=qo_p), (qo_p,))]
     qo_d = [torch.empty((B * Hq, Dh), dtype=torch.float16, device=dev) for _ in range(Dn)]
+    att_o = [torch.empty((B, Hq, Dh), dtype=torch.float16, device=dev) for _ in range(Dn)]
+    ws = torch.empty((qr.kv_decode_workspace_bytes(B, Hq, H, Dh, S),), dtype=torch.uint8, device=dev)
+    scale = 1.0 / Dh ** 0.5
     for i in range(Dn):
         qd = q[:, P + i].reshape(-1, Dh)
         L.append(("kv_rotate_quant", f"k:append{i}", kv_bytes(B * H, Dh, G), 0,
@@ -187,9 +198,14 @@ def make_kv_decode(torch, qr, wl, W, dev):
                                                  P + i, rotate=False), cache["v"]))
         L.append(("hadamard", f"q:decode{i}", rot_bytes(B * Hq, Dh), 0,
                   lambda qd=qd, i=i: qr.hadamard(qd, s, torch.float16, out=qo_d[i]), (qo_d[i],)))
+        L.append(("kv_decode_attention", f"decode{i}", decode_bytes(B, H, Hq, P + i + 1, Dh, G), 0,
+                  lambda i=i: qr.kv_decode_attention(qo_d[i].view(B, Hq, Dh), *cache["k"], *cache["v"],
+                                                     P + i + 1, G, scale, out=att_o[i], workspace=ws),
+                  (att_o[i],)))
     desc = (f"Llama-2-70B KV path: batch {B}, {P}-token prompt + {Dn} decode steps, {H} KV heads "
             f"and {Hq} query heads of {Dh}; K/V Init + Append into the 4-bit cache (group {G}, "
-            f"clip 0.95), head-wise rotation of K and Q")
+            f"clip 0.95), head-wise rotation of K and Q, Decode attention of each step's query "
+            f"over the cache ({P + 1}..{S} positions)")
     return L, desc
 
 
@@ -374,7 +390,7 @@ def main():
     else:
         launches, desc = make_kv_decode(torch, qr, wl, W, dev)
         config.update({"workload": desc})
-        dominant, bound = "kv_rotate_quant", "hbm"
+        dominant, bound = "kv_decode_attention", "hbm"
     torch.cuda.synchronize()
 
     graphed = wname in ("7b_decode", "70b_kv")
@@ -414,6 +430,8 @@ def main():
     }
     if any(l[0] == "hadamard_quant" for l in launches):
         out["roofline_hadamard_quant"] = roofline("hadamard_quant", wname, launches, per, "hbm")
+    if dominant != "kv_rotate_quant" and any(l[0] == "kv_rotate_quant" for l in launches):
+        out["roofline_kv_rotate_quant"] = roofline("kv_rotate_quant", wname, launches, per, "hbm")
     out["kernels"] = kernels if len(kernels) <= 40 else {
         k: {"ms": round(sum(p for l, p in zip(launches, per) if l[0] == k), 4),
             "launches": sum(1 for l in launches if l[0] == k)}

@@ -49,9 +49,16 @@ def sources() -> list[Path]:
     return sorted(list(CSRC.glob("*.hip")) + list(CSRC.glob("*.cpp")))
 
 
+# Per-source extra flags.  The decode-attention kernel keeps its matrix-core
+# results in ordinary VGPRs: it has few accumulators and feeds most MFMA
+# results straight into VALU work, which AGPR results would first have to be
+# copied out of.
+EXTRA_FLAGS = {"kv_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: Path, verbose: bool) -> Path:
     obj = BUILD / (src.name + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", str(src), "-o", str(obj)]
+    cmd = [hipcc(), *COMMON_FLAGS, *EXTRA_FLAGS.get(src.name, []), "-c", str(src), "-o", str(obj)]
     if src.suffix == ".cpp":
         cmd = [hipcc(), *[f for f in COMMON_FLAGS if not f.startswith("--offload")], "-x", "hip",
                "--offload-arch=" + ARCH, "-c", str(src), "-o", str(obj)]

@@ -13,15 +13,18 @@
 // Design (MI355X first):
 //  * Flash-decoding split: workgroup (split, h, b) streams `cpw` chunks of 256
 //    cached positions of one KV head for all Hq / Hkv <= 16 query heads that
-//    share it, with an online softmax across its chunks, and writes one
-//    partial record (running max, sum, unnormalised output) per query head;
-//    k_kv_decode_combine merges the records of a head.
+//    share it.  Each of its 4 wavefronts keeps its own online softmax over its
+//    64 positions of every chunk (no barrier inside the loop) while the next
+//    chunk's codes are already in flight; the wavefronts meet once at the end
+//    and write one partial record (max, sum, unnormalised output) per query
+//    head; k_kv_decode_combine merges the records of a head.
 //  * Both products run on the matrix cores (v_mfma_f32_16x16x32_f16) on exact
 //    operands.  A 4-bit code c enters as the fp16 number 1024 + c (bit pattern
-//    0x6400 | c: one v_perm and one and-or per pair of codes); the constant
-//    and the scale / min of the position are applied around the product, in
-//    fp32:  q . k_j = scale_j (q . (1024 + c_j) - 1024 sum(q)) + min_j sum(q).
-//    The MFMA accumulator starts at -1024 sum(q), so it ends at q . c_j.
+//    0x6400 | c), or 1024 + 16 c for the high nibble of a byte, whose query
+//    operand is then divided by 16 (exact); the constant and the scale / min of
+//    the position are applied around the product, in fp32:
+//    q . k_j = scale_j (q . c_j) + min_j sum(q), the MFMA accumulator starting
+//    at -1024 times the sum of the query operands so that it ends at q . c_j.
 //  * Scores: keys are the M index (16 per tile, lane-major), query heads the N
 //    index, head dimensions the contraction; lane (head n, g) ends with the
 //    scores of positions 4 g .. 4 g + 3 of each tile.
@@ -32,6 +35,7 @@
 //    B-operand layout of P V for the position order the scores already have.
 //  * P' = p * scale_v is split into fp16 hi + lo parts (two MFMAs), so the
 //    weights keep about 22 bits; sum_j p_j min_j is added in fp32.
+#include <cfloat>
 #include <type_traits>
 
 #include "common.hpp"
@@ -40,7 +44,10 @@ namespace qr {
 
 constexpr int KD_DH = 128;     // head dimension
 constexpr int KD_CHUNK = 256;  // positions per workgroup pass: 4 wavefronts x 4 tiles x 16
-constexpr int KD_TARGET_WG = 2048;
+#ifndef QR_KD_TARGET_WG
+#define QR_KD_TARGET_WG 512
+#endif
+constexpr int KD_TARGET_WG = QR_KD_TARGET_WG;  // workgroups the split aims for
 
 struct KdPlan {
   int chunks, cpw, splits;
@@ -58,26 +65,29 @@ static KdPlan kd_plan(int64_t B, int64_t Hkv, int64_t L) {
 }
 
 // Packed 4-bit codes (8 per dword: code 2i in the low nibble of byte i) ->
-// 8 fp16 values 1024 + code in the element order (0, 2, 1, 3, 4, 6, 5, 7).
-__device__ __forceinline__ v8h codes8_f16(uint32_t x) {
-  const uint32_t t0 = __builtin_amdgcn_perm(0u, x, 0x0c010c00u);  // [b0, 0, b1, 0]
-  const uint32_t t1 = __builtin_amdgcn_perm(0u, x, 0x0c030c02u);  // [b2, 0, b3, 0]
+// 8 fp16 values in the element order (c0, c4, c1, c5, c2, c6, c3, c7): even
+// codes as 1024 + c, odd codes as 1024 + 16 c (their nibble left in place), so
+// five bit operations per dword.  mlo = 0x000F000F, mhi = 0x00F000F0 and
+// bias = 0x64006400 come in registers (three-operand and-or).
+__device__ __forceinline__ v8h codes8_f16(uint32_t x, uint32_t mlo, uint32_t mhi, uint32_t bias) {
+  const uint32_t x8 = x >> 8;
   v4u r;
-  r[0] = (t0 & 0x000F000Fu) | 0x64006400u;         // codes 0, 2
-  r[1] = ((t0 >> 4) & 0x000F000Fu) | 0x64006400u;  // codes 1, 3
-  r[2] = (t1 & 0x000F000Fu) | 0x64006400u;         // codes 4, 6
-  r[3] = ((t1 >> 4) & 0x000F000Fu) | 0x64006400u;  // codes 5, 7
+  r[0] = (x & mlo) | bias;   // c0, c4
+  r[1] = (x & mhi) | bias;   // 16 c1, 16 c5
+  r[2] = (x8 & mlo) | bias;  // c2, c6
+  r[3] = (x8 & mhi) | bias;  // 16 c3, 16 c7
   return __builtin_bit_cast(v8h, r);
 }
+// Code index of fragment element j, and whether it carries the factor 16.
+__device__ __forceinline__ constexpr int kd_pi(int j) { return (j >> 2) * 2 + (j & 1) * 4 + ((j >> 1) & 1); }
+__device__ __forceinline__ constexpr bool kd_odd(int j) { return (j >> 1) & 1; }
 
 __device__ __forceinline__ float fp16_lo(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float fp16_hi(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
 
 // Head dimension held by lane n' of output tile (kb, hs) after the transpose.
 __device__ __forceinline__ int kd_dim(int kb, int hs, int np) {
-  const int e = np & 7;
-  const int sig = (e == 1 || e == 2 || e == 5 || e == 6) ? (e ^ 3) : e;  // 0 2 1 3 4 6 5 7
-  return 32 * (2 * hs + (np >> 3)) + 8 * kb + sig;
+  return 32 * (2 * hs + (np >> 3)) + 8 * kb + kd_pi(np & 7);
 }
 
 __global__ __launch_bounds__(256) void k_kv_decode(
@@ -85,10 +95,9 @@ __global__ __launch_bounds__(256) void k_kv_decode(
     const uint32_t* __restrict__ km, const uint8_t* __restrict__ vc,
     const uint32_t* __restrict__ vm, int S_max, int L, float scale_log2e, int chunks, int cpw,
     int splits, float* __restrict__ ws) {
-  __shared__ float s_wmax[2][4][16];
-  __shared__ __attribute__((aligned(16))) uint32_t s_meta[4][2][64];
+  __shared__ __attribute__((aligned(16))) float s_meta[4][4][64];  // k scale, k min, v scale, v min
   __shared__ float s_o[4][16][KD_DH];
-  __shared__ float s_l[4][16], s_ms[4][16], s_mrun[16];
+  __shared__ float s_l[4][16], s_ms[4][16], s_mw[4][16];
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -106,42 +115,55 @@ __global__ __launch_bounds__(256) void k_kv_decode(
   const __amdgpu_buffer_rsrc_t rs_vm =
       __builtin_amdgcn_make_buffer_rsrc((void*)(vm + row0), 0, L * 4, 0x00020000);
 
-  // ---- query fragments (B operand of the scores): lane (head n, g), block kb
-  //      holds dims 32 g + 8 kb + (0, 2, 1, 3, 4, 6, 5, 7); heads >= GQ are zero ----
+  // Bit masks of the code unpacking, held in registers.
+  uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, bias = 0x64006400u;
+  asm volatile("" : "+v"(mlo), "+v"(mhi), "+v"(bias));
+
+  // ---- query fragments (B operand of the scores): lane (head n, g), block kb,
+  //      element j holds dim 32 g + 8 kb + pi(j), divided by 16 where the code
+  //      operand carries 16 c (exact: a power of two); heads >= GQ are zero.
+  //      qsum16 is the sum of these operands, qsum that of the query itself ----
   v8h qf[4];
-  float qsum = 0.0f;
+  float qsum = 0.0f, qsum16 = 0.0f;
   {
     const bool real = n < GQ;
     const uint16_t* qh = q + ((int64_t)b * Hq + (int64_t)h * GQ + (real ? n : 0)) * KD_DH + 32 * g;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      v4u raw = real ? *(const v4u*)(qh + 8 * kb) : v4u{0u, 0u, 0u, 0u};
-      v4u o;
-      o[0] = __builtin_amdgcn_perm(raw[1], raw[0], 0x05040100u);
-      o[1] = __builtin_amdgcn_perm(raw[1], raw[0], 0x07060302u);
-      o[2] = __builtin_amdgcn_perm(raw[3], raw[2], 0x05040100u);
-      o[3] = __builtin_amdgcn_perm(raw[3], raw[2], 0x07060302u);
-      qf[kb] = __builtin_bit_cast(v8h, o);
+      const v4u raw = real ? *(const v4u*)(qh + 8 * kb) : v4u{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qsum += fp16_lo(raw[i]) + fp16_hi(raw[i]);
+      for (int j = 0; j < 8; ++j) {
+        const int i = kd_pi(j);
+        const float v = (i & 1) ? fp16_hi(raw[i >> 1]) : fp16_lo(raw[i >> 1]);
+        const _Float16 o = (_Float16)(kd_odd(j) ? v * 0.0625f : v);
+        qf[kb][j] = o;
+        qsum += v;
+        qsum16 += (float)o;
+      }
     }
     qsum += __shfl_xor(qsum, 16);
     qsum += __shfl_xor(qsum, 32);
+    qsum16 += __shfl_xor(qsum16, 16);
+    qsum16 += __shfl_xor(qsum16, 32);
   }
-  const float qc = -1024.0f * qsum;
+  const float qc = -1024.0f * qsum16;
 
-  // Selection matrices of the transpose: Sel_hs[k = 8 g + j][n'] = 1 iff
-  // g == 2 hs + (n' >> 3) and j == (n' & 7).
+  // Selection matrices of the transpose: Sel_hs[k = 8 g + j][n'] = w_j iff
+  // g == 2 hs + (n' >> 3) and j == (n' & 7), with w_j = 1/16 on the elements
+  // that carry 16 c; the product then holds 1024 + c or 64 + c, and the
+  // accumulator's start value takes the constant off.
   v8h sel[2];
 #pragma unroll
   for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      sel[hs][j] = (g == 2 * hs + (n >> 3) && j == (n & 7)) ? (_Float16)1.0f : (_Float16)0.0f;
+      sel[hs][j] = (g == 2 * hs + (n >> 3) && j == (n & 7))
+                       ? (_Float16)(kd_odd(j) ? 0.0625f : 1.0f) : (_Float16)0.0f;
+  const float tneg = kd_odd(n & 7) ? -64.0f : -1024.0f;
 
   // Running state: max (log2 domain) for head n and for heads 4 g + r (the
   // output rows this lane accumulates), lane-partial sums of p and p * min_v.
-  float m_n = -INFINITY, m_r[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float m_n = -FLT_MAX, m_r[4] = {-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX};
   float l_n = 0.0f, ms_n = 0.0f;
   v4f O[4][2];
 #pragma unroll
@@ -149,21 +171,36 @@ __global__ __launch_bounds__(256) void k_kv_decode(
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs) O[kb][hs] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int c0 = split * cpw, c1 = min(chunks, c0 + cpw);
-  for (int c = c0; c < c1; ++c) {
-    const int par = c & 1;
-    const int kw = c * KD_CHUNK + 64 * w;  // first position of this wavefront's 64
-    // ---- loads: codes of tile t (lane m = position 16 t + n, 16 bytes = dims
-    //      32 g .. 32 g + 31), one metadata word per lane ----
-    v4u kraw[4], vraw[4];
+  // ---- loads of one chunk: codes of tile t (lane m = position 16 t + n, 16
+  //      bytes = dims 32 g .. 32 g + 31), one metadata word per lane.  The next
+  //      chunk's are issued once the current one's keys are consumed. ----
+  v4u kraw[4], vraw[4], vnext[4];
+  uint32_t kmeta_reg, vmeta_reg;
+  auto load_k = [&](int kw) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int off = (kw + 16 * t + n) * 64 + 16 * g;
-      kraw[t] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs_kc, off, 0, 0));
-      vraw[t] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs_vc, off, 0, 0));
-    }
-    s_meta[w][0][lane] = __builtin_amdgcn_raw_buffer_load_b32(rs_km, (kw + lane) * 4, 0, 0);
-    s_meta[w][1][lane] = __builtin_amdgcn_raw_buffer_load_b32(rs_vm, (kw + lane) * 4, 0, 0);
+    for (int t = 0; t < 4; ++t)
+      kraw[t] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs_kc, (kw + 16 * t + n) * 64 + 16 * g, 0, 0));
+    kmeta_reg = __builtin_amdgcn_raw_buffer_load_b32(rs_km, (kw + lane) * 4, 0, 0);
+    vmeta_reg = __builtin_amdgcn_raw_buffer_load_b32(rs_vm, (kw + lane) * 4, 0, 0);
+  };
+  auto load_v = [&](int kw, v4u* dst) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      dst[t] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs_vc, (kw + 16 * t + n) * 64 + 16 * g, 0, 0));
+  };
+
+  const int c0 = split * cpw, c1 = min(chunks, c0 + cpw);
+  // One chunk: values of this chunk in vcur, the next chunk's fetched into vnxt.
+  auto chunk = [&](const int c, v4u (&vcur)[4], v4u (&vnxt)[4]) {
+    const int kw = c * KD_CHUNK + 64 * w;  // first position of this wavefront's 64
+    // metadata of the wavefront's 64 positions, converted once per position
+    // (the key's already carrying the log2-domain softmax scale)
+    s_meta[w][0][lane] = scale_log2e * fp16_lo(kmeta_reg);
+    s_meta[w][1][lane] = scale_log2e * fp16_hi(kmeta_reg);
+    s_meta[w][2][lane] = fp16_lo(vmeta_reg);
+    s_meta[w][3][lane] = fp16_hi(vmeta_reg);
     __builtin_amdgcn_wave_barrier();
 
     // ---- scores of tile t: lane (head n, g) gets positions 16 t + 4 g + r ----
@@ -174,42 +211,64 @@ __global__ __launch_bounds__(256) void k_kv_decode(
       v4f acc = {qc, qc, qc, qc};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_f16(kraw[t][kb]), qf[kb], acc, 0, 0, 0);
-      const v4u kmeta = *(const v4u*)&s_meta[w][0][16 * t + 4 * g];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_f16(kraw[t][kb], mlo, mhi, bias), qf[kb],
+                                                     acc, 0, 0, 0);
+      const v4f ks = *(const v4f*)&s_meta[w][0][16 * t + 4 * g];
+      const v4f kmn = *(const v4f*)&s_meta[w][1][16 * t + 4 * g];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pos = kw + 16 * t + 4 * g + r;
-        const float s = fp16_lo(kmeta[r]), mn = fp16_hi(kmeta[r]);
-        sc[t][r] = pos < L ? scale_log2e * fmaf(s, acc[r], mn * qsum) : -INFINITY;
-        mx = fmaxf(mx, sc[t][r]);
-      }
+      for (int r = 0; r < 4; ++r) sc[t][r] = fmaf(ks[r], acc[r], kmn[r] * qsum);
+    }
+    if ((c + 1) * KD_CHUNK > L) {  // the last chunk: positions past L take no weight
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kw + 16 * t + 4 * g + r >= L) sc[t][r] = -INFINITY;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[t][r]);
+    const bool more = c + 1 < c1;
+    if (more) {
+      load_k(kw + KD_CHUNK);
+      load_v(kw + KD_CHUNK, vnxt);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (g == 0) s_wmax[par][w][n] = mx;
-    __syncthreads();
 
-    // ---- online softmax update (the chunk's first position is < L, so the
-    //      new maxima are finite) ----
-    auto chunk_max = [&](int hd) {
-      return fmaxf(fmaxf(s_wmax[par][0][hd], s_wmax[par][1][hd]),
-                   fmaxf(s_wmax[par][2][hd], s_wmax[par][3][hd]));
-    };
-    const float mnew_n = fmaxf(m_n, chunk_max(n));
-    const float a_n = exp2f(m_n - mnew_n);
-    m_n = mnew_n;
-    l_n *= a_n;
-    ms_n *= a_n;
+    // ---- online softmax update, per wavefront (no barrier: the wavefronts
+    //      meet once, at the end).  The maxima start at -FLT_MAX, not -inf, so
+    //      that a wavefront whose positions are all past L keeps weights 0 and
+    //      factors 1 instead of NaN. ----
+    auto chunk_max = [&](int hd) { return __shfl(mx, hd); };  // lane hd holds head hd's
+    const float mnew_n = fmaxf(m_n, mx);
+    if (c > c0) {
+      const float a_n = __builtin_amdgcn_exp2f(m_n - mnew_n);
+      l_n *= a_n;
+      ms_n *= a_n;
+      float a[4];
+      bool grew = false;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float mnew = fmaxf(m_r[r], chunk_max(4 * g + r));
-      const float a = exp2f(m_r[r] - mnew);
-      m_r[r] = mnew;
+      for (int r = 0; r < 4; ++r) {
+        const float mnew = fmaxf(m_r[r], chunk_max(4 * g + r));
+        grew |= mnew > m_r[r];
+        a[r] = __builtin_amdgcn_exp2f(m_r[r] - mnew);
+        m_r[r] = mnew;
+      }
+      if (__any(grew)) {  // rescale the output rows only when a maximum moved
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs) O[kb][hs][r] *= a;
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs) O[kb][hs][r] *= a[r];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m_r[r] = fmaxf(m_r[r], chunk_max(4 * g + r));
     }
+    m_n = mnew_n;
 
     // ---- weights P' = p * scale_v as fp16 hi + lo, A operands of P V: block
     //      kp = tiles (2 kp, 2 kp + 1), element j -> position 4 g + (j & 3) of
@@ -217,13 +276,14 @@ __global__ __launch_bounds__(256) void k_kv_decode(
     v8h ph[2], pl[2];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const v4u vmeta = *(const v4u*)&s_meta[w][1][16 * t + 4 * g];
+      const v4f vs = *(const v4f*)&s_meta[w][2][16 * t + 4 * g];
+      const v4f vmn = *(const v4f*)&s_meta[w][3][16 * t + 4 * g];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(sc[t][r] - m_n);
+        const float p = __builtin_amdgcn_exp2f(sc[t][r] - m_n);
         l_n += p;
-        ms_n = fmaf(p, fp16_hi(vmeta[r]), ms_n);
-        const float pp = p * fp16_lo(vmeta[r]);
+        ms_n = fmaf(p, vmn[r], ms_n);
+        const float pp = p * vs[r];
         const _Float16 hi = (_Float16)pp;
         ph[t >> 1][4 * (t & 1) + r] = hi;
         pl[t >> 1][4 * (t & 1) + r] = (_Float16)(pp - (float)hi);
@@ -231,15 +291,15 @@ __global__ __launch_bounds__(256) void k_kv_decode(
     }
 
     // ---- P V: transpose each value tile on the matrix cores, then multiply ----
+    const v4f cneg = {tneg, tneg, tneg, tneg};
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const v8h va = codes8_f16(vraw[2 * kp][kb]);
-        const v8h vb = codes8_f16(vraw[2 * kp + 1][kb]);
+        const v8h va = codes8_f16(vcur[2 * kp][kb], mlo, mhi, bias);
+        const v8h vb = codes8_f16(vcur[2 * kp + 1][kb], mlo, mhi, bias);
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-          const v4f cneg = {-1024.0f, -1024.0f, -1024.0f, -1024.0f};
           const v4f ta = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, sel[hs], cneg, 0, 0, 0);
           const v4f tb = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb, sel[hs], cneg, 0, 0, 0);
           v8h bop;
@@ -253,10 +313,16 @@ __global__ __launch_bounds__(256) void k_kv_decode(
         }
       }
     }
+  };
+  load_k(c0 * KD_CHUNK + 64 * w);
+  load_v(c0 * KD_CHUNK + 64 * w, vraw);
+  for (int c = c0; c < c1; c += 2) {  // two chunks per trip: the value buffers swap roles
+    chunk(c, vraw, vnext);
+    if (c + 1 < c1) chunk(c + 1, vnext, vraw);
   }
 
-  // ---- combine the wavefronts (they share the running maxima) and write the
-  //      partial record of every query head: max, sum, unnormalised output ----
+  // ---- combine the wavefronts (each with its own running maxima) and write
+  //      the partial record of every query head: max, sum, unnormalised output ----
   l_n += __shfl_xor(l_n, 16);
   l_n += __shfl_xor(l_n, 32);
   ms_n += __shfl_xor(ms_n, 16);
@@ -264,7 +330,7 @@ __global__ __launch_bounds__(256) void k_kv_decode(
   if (g == 0) {
     s_l[w][n] = l_n;
     s_ms[w][n] = ms_n;
-    if (w == 0) s_mrun[n] = m_n;
+    s_mw[w][n] = m_n;
   }
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
@@ -275,12 +341,19 @@ __global__ __launch_bounds__(256) void k_kv_decode(
   __syncthreads();
   for (int i = tid; i < GQ * KD_DH; i += 256) {
     const int hd = i / KD_DH, d = i % KD_DH;
-    const float ms = s_ms[0][hd] + s_ms[1][hd] + s_ms[2][hd] + s_ms[3][hd];
+    const float M = fmaxf(fmaxf(s_mw[0][hd], s_mw[1][hd]), fmaxf(s_mw[2][hd], s_mw[3][hd]));
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float f = __builtin_amdgcn_exp2f(s_mw[v][hd] - M);
+      o = fmaf(f, s_o[v][hd][d] + s_ms[v][hd], o);
+      l = fmaf(f, s_l[v][hd], l);
+    }
     float* rec = ws + (((int64_t)b * Hq + (int64_t)h * GQ + hd) * splits + split) * (KD_DH + 2);
-    rec[2 + d] = s_o[0][hd][d] + s_o[1][hd][d] + s_o[2][hd][d] + s_o[3][hd][d] + ms;
+    rec[2 + d] = o;
     if (d == 0) {
-      rec[0] = s_mrun[hd];
-      rec[1] = s_l[0][hd] + s_l[1][hd] + s_l[2][hd] + s_l[3][hd];
+      rec[0] = M;
+      rec[1] = l;
     }
   }
 }
