@@ -358,21 +358,25 @@ __global__ __launch_bounds__(256) void k_kv_decode(
   }
 }
 
-// Merge the split records of one query head: o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// Merge the split records of one query head in one pass (running max, the
+// loads of every record independent of the previous ones):
+// o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
 __global__ __launch_bounds__(KD_DH) void k_kv_decode_combine(const float* __restrict__ ws,
                                                              int splits,
                                                              uint16_t* __restrict__ out) {
   const int64_t head = blockIdx.x;  // b * Hq + hq
   const int d = threadIdx.x;
   const float* rec = ws + head * splits * (KD_DH + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, rec[s * (KD_DH + 2)]);
-  float l = 0.0f, o = 0.0f;
+  float M = -FLT_MAX, l = 0.0f, o = 0.0f;
+#pragma unroll 4
   for (int s = 0; s < splits; ++s) {
     const float* r = rec + s * (KD_DH + 2);
-    const float a = exp2f(r[0] - M);
-    l = fmaf(r[1], a, l);
-    o = fmaf(r[2 + d], a, o);
+    const float ms = r[0], ls = r[1], os = r[2 + d];
+    const float Mn = fmaxf(M, ms);
+    const float a = __builtin_amdgcn_exp2f(M - Mn), bs = __builtin_amdgcn_exp2f(ms - Mn);
+    l = fmaf(l, a, ls * bs);
+    o = fmaf(o, a, os * bs);
+    M = Mn;
   }
   out[head * KD_DH + d] = f2h(o / l);
 }
