@@ -33,8 +33,12 @@
 //    0/1 selection matrix (T = V_tile x Sel - 1024 = the codes, exact), which
 //    leaves position 4 g + r in register r of lane (dim, g): exactly the
 //    B-operand layout of P V for the position order the scores already have.
-//  * P' = p * scale_v is split into fp16 hi + lo parts (two MFMAs), so the
-//    weights keep about 22 bits; sum_j p_j min_j is added in fp32.
+//  * The weights P' = p * scale_v enter the product as fp16 (the pages' FP16
+//    dot product; QR_KD_SPLIT_WEIGHTS=1 carries them as hi + lo parts, about
+//    22 bits, at two MFMAs); sum_j p_j min_j is added in fp32.
+//  * When one workgroup per KV head already fills the machine (B * Hkv >= 256
+//    compute units) the split is a single chunk run and the workgroup writes
+//    the normalised fp16 output itself: no workspace, no merge kernel.
 #include <cfloat>
 #include <type_traits>
 
@@ -44,8 +48,11 @@ namespace qr {
 
 constexpr int KD_DH = 128;     // head dimension
 constexpr int KD_CHUNK = 256;  // positions per workgroup pass: 4 wavefronts x 4 tiles x 16
+#ifndef QR_KD_SPLIT_WEIGHTS
+#define QR_KD_SPLIT_WEIGHTS 0
+#endif
 #ifndef QR_KD_TARGET_WG
-#define QR_KD_TARGET_WG 512
+#define QR_KD_TARGET_WG 256
 #endif
 constexpr int KD_TARGET_WG = QR_KD_TARGET_WG;  // workgroups the split aims for
 
@@ -94,7 +101,7 @@ __global__ __launch_bounds__(256) void k_kv_decode(
     const uint16_t* __restrict__ q, int Hq, int Hkv, int GQ, const uint8_t* __restrict__ kc,
     const uint32_t* __restrict__ km, const uint8_t* __restrict__ vc,
     const uint32_t* __restrict__ vm, int S_max, int L, float scale_log2e, int chunks, int cpw,
-    int splits, float* __restrict__ ws) {
+    int splits, float* __restrict__ ws, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) float s_meta[4][4][64];  // k scale, k min, v scale, v min
   __shared__ float s_o[4][16][KD_DH];
   __shared__ float s_l[4][16], s_ms[4][16], s_mw[4][16];
@@ -286,7 +293,7 @@ __global__ __launch_bounds__(256) void k_kv_decode(
         const float pp = p * vs[r];
         const _Float16 hi = (_Float16)pp;
         ph[t >> 1][4 * (t & 1) + r] = hi;
-        pl[t >> 1][4 * (t & 1) + r] = (_Float16)(pp - (float)hi);
+        if (QR_KD_SPLIT_WEIGHTS) pl[t >> 1][4 * (t & 1) + r] = (_Float16)(pp - (float)hi);
       }
     }
 
@@ -309,7 +316,8 @@ __global__ __launch_bounds__(256) void k_kv_decode(
             bop[4 + r] = (_Float16)tb[r];
           }
           O[kb][hs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[kp], bop, O[kb][hs], 0, 0, 0);
-          O[kb][hs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[kp], bop, O[kb][hs], 0, 0, 0);
+          if (QR_KD_SPLIT_WEIGHTS)
+            O[kb][hs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[kp], bop, O[kb][hs], 0, 0, 0);
         }
       }
     }
@@ -349,11 +357,16 @@ __global__ __launch_bounds__(256) void k_kv_decode(
       o = fmaf(f, s_o[v][hd][d] + s_ms[v][hd], o);
       l = fmaf(f, s_l[v][hd], l);
     }
-    float* rec = ws + (((int64_t)b * Hq + (int64_t)h * GQ + hd) * splits + split) * (KD_DH + 2);
-    rec[2 + d] = o;
-    if (d == 0) {
-      rec[0] = M;
-      rec[1] = l;
+    const int64_t head = (int64_t)b * Hq + (int64_t)h * GQ + hd;
+    if (splits == 1) {  // the whole context in one workgroup: the final output
+      out[head * KD_DH + d] = f2h(o / l);
+    } else {
+      float* rec = ws + (head * splits + split) * (KD_DH + 2);
+      rec[2 + d] = o;
+      if (d == 0) {
+        rec[0] = M;
+        rec[1] = l;
+      }
     }
   }
 }
@@ -389,6 +402,7 @@ extern "C" int64_t qr_kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t H
                                                 int32_t L) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Dh < 1 || L < 1) return 0;
   const KdPlan p = kd_plan(B, Hkv, L);
+  if (p.splits == 1) return 0;  // one workgroup per KV head writes the output directly
   return (int64_t)B * Hq * p.splits * (Dh + 2) * (int64_t)sizeof(float);
 }
 
@@ -405,10 +419,11 @@ extern "C" qr_status qr_kv_decode_attention(const void* q_f16, int32_t B, int32_
   if (!(softmax_scale > 0.0f) || !(softmax_scale < 1e30f)) return QR_ERR_ARG;
   if ((int64_t)S_max * 64 > INT32_MAX) return QR_ERR_SHAPE;
   if (B == 0) return QR_OK;
+  const int64_t need = qr_kv_decode_workspace_bytes(B, Hq, Hkv, Dh, L);
   if (!q_f16 || !k_cache_q || !k_cache_meta || !v_cache_q || !v_cache_meta || !out_f16 ||
-      !workspace)
+      (need > 0 && !workspace))
     return QR_ERR_NULL;
-  if (workspace_bytes < qr_kv_decode_workspace_bytes(B, Hq, Hkv, Dh, L)) return QR_ERR_SHAPE;
+  if (workspace_bytes < need) return QR_ERR_SHAPE;
   if (!aligned(q_f16, 16) || !aligned(k_cache_q, 16) || !aligned(v_cache_q, 16) ||
       !aligned(k_cache_meta, 4) || !aligned(v_cache_meta, 4) || !aligned(out_f16, 2) ||
       !aligned(workspace, 4))
@@ -420,9 +435,9 @@ extern "C" qr_status qr_kv_decode_attention(const void* q_f16, int32_t B, int32_
                      (const uint16_t*)q_f16, Hq, Hkv, Hq / Hkv, (const uint8_t*)k_cache_q,
                      (const uint32_t*)k_cache_meta, (const uint8_t*)v_cache_q,
                      (const uint32_t*)v_cache_meta, S_max, L, scale_log2e, p.chunks, p.cpw,
-                     p.splits, (float*)workspace);
+                     p.splits, (float*)workspace, (uint16_t*)out_f16);
   qr_status st = launch_status();
-  if (st != QR_OK) return st;
+  if (st != QR_OK || p.splits == 1) return st;
   hipLaunchKernelGGL(k_kv_decode_combine, dim3((unsigned)(B * Hq)), dim3(KD_DH), 0, stream,
                      (const float*)workspace, p.splits, (uint16_t*)out_f16);
   return launch_status();

@@ -188,11 +188,13 @@ qr_status qr_kv_rotate_quant(const void* kv_f16, int32_t B, int32_t S_new, int32
  *                qr_kv_decode_workspace_bytes(B, Hq, Hkv, Dh, L) bytes: fp32
  *                partial results of the split over positions; its contents on
  *                entry do not matter and are overwritten.  Calls that overlap on
- *                one workspace race.
- * Arithmetic: q . k_j and the weights are formed in fp32 from exact fp16
- * operands (codes are exact; scale and min are applied in fp32), softmax in
- * fp32 with exp2, weights * value scale carried as two fp16 parts; the output
- * is rounded once to fp16.
+ *                one workspace race.  When that size is 0 (B * Hkv large enough
+ *                that one workgroup per KV head fills the GPU) workspace may be
+ *                NULL.
+ * Arithmetic: q . k_j is formed in fp32 from exact fp16 operands (codes are
+ * exact; scale and min are applied in fp32), softmax in fp32 with exp2; the
+ * weights times the value scale enter the value product as fp16 (the pages'
+ * FP16 dot product), min terms in fp32; the output is rounded once to fp16.
  * Requirements: Dh = 128, group = 128, Hq % Hkv == 0, Hq / Hkv <= 16,
  * softmax_scale > 0; q_f16, k_cache_q and v_cache_q 16-byte aligned, the
  * metadata and the workspace 4-byte aligned.  B == 0 returns QR_OK.

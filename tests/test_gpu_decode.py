@@ -1,13 +1,14 @@
 """GPU parity: qr_kv_decode_attention (the Decode routine over the 4-bit cache)
 against the float64 oracle.
 
-Tolerance (derived from the kernel's arithmetic, see include/qr.h): the scores
-and weights are formed in fp32 from exact operands and the weights keep about
-22 bits, so the result before its final fp16 rounding is within ~1e-5 of the
-exact value relative to the values' magnitude; the output is then rounded once
-to fp16.  Bound per element:
+Tolerance (derived from the kernel's arithmetic, see include/qr.h): scores and
+softmax are fp32 on exact operands (relative error ~1e-6); each weight p_j s_j
+enters the value product rounded to fp16 (relative 2^-11), and since
+|s_j c_j| <= |v_j| + |min_j| <= 2 max|v| those roundings move the normalised
+output by at most 2^-11 * 2 max|v|; the output is then rounded once to fp16.
+Bound per element:
 
-    |out - ref| <= 1e-3 * max|v_j| + 2^-11 * |ref|
+    |out - ref| <= 2e-3 * max|v_j| + 2^-11 * |ref|
 
 with max|v_j| over the dequantized values of that KV head and positions < L.
 
@@ -47,7 +48,7 @@ def check(got, ref, v_cache_q, v_cache_meta, L, group, hq_per_kv):
     vmax = np.abs(vdeq).max(axis=(2, 3))                                 # [B, Hkv]
     vmax = np.repeat(vmax, hq_per_kv, axis=1)[..., None]                 # [B, Hq, 1]
     err = np.abs(got.astype(np.float64) - ref)
-    bound = 1e-3 * vmax + 2.0 ** -11 * np.abs(ref)
+    bound = 2e-3 * vmax + 2.0 ** -11 * np.abs(ref)
     worst = float((err / bound).max())
     assert worst <= 1.0, f"max error / bound = {worst:.3f}"
     return worst
