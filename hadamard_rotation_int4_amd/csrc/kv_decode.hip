@@ -13,11 +13,13 @@
 // Design (MI355X first):
 //  * Flash-decoding split: workgroup (split, h, b) streams `cpw` chunks of 256
 //    cached positions of one KV head for all Hq / Hkv <= 16 query heads that
-//    share it.  Each of its 4 wavefronts keeps its own online softmax over its
-//    64 positions of every chunk (no barrier inside the loop) while the next
-//    chunk's codes are already in flight; the wavefronts meet once at the end
-//    and write one partial record (max, sum, unnormalised output) per query
-//    head; k_kv_decode_combine merges the records of a head.
+//    share it.  Its 8 wavefronts form two streams over alternate chunks, each
+//    wavefront taking 64 positions of every chunk of its stream (two
+//    wavefronts per SIMD); each keeps its own online softmax (no barrier inside
+//    the loop) while its next chunk's codes are already in flight.  The
+//    wavefronts meet once at the end and write one partial record (max, sum,
+//    unnormalised output) per query head; k_kv_decode_combine merges the
+//    records of a head.
 //  * Both products run on the matrix cores (v_mfma_f32_16x16x32_f16) on exact
 //    operands.  A 4-bit code c enters as the fp16 number 1024 + c (bit pattern
 //    0x6400 | c), or 1024 + 16 c for the high nibble of a byte, whose query
@@ -97,18 +99,25 @@ __device__ __forceinline__ int kd_dim(int kb, int hs, int np) {
   return 32 * (2 * hs + (np >> 3)) + 8 * kb + kd_pi(np & 7);
 }
 
-__global__ __launch_bounds__(256) void k_kv_decode(
+// Wavefronts per workgroup: 4 position blocks x KD_SETS chunk streams.
+constexpr int KD_SETS = 2;
+constexpr int KD_WAVES = 4 * KD_SETS;
+
+__global__ __launch_bounds__(64 * KD_WAVES) void k_kv_decode(
     const uint16_t* __restrict__ q, int Hq, int Hkv, int GQ, const uint8_t* __restrict__ kc,
     const uint32_t* __restrict__ km, const uint8_t* __restrict__ vc,
     const uint32_t* __restrict__ vm, int S_max, int L, float scale_log2e, int chunks, int cpw,
     int splits, float* __restrict__ ws, uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) float s_meta[4][4][64];  // k scale, k min, v scale, v min
-  __shared__ float s_o[4][16][KD_DH];
-  __shared__ float s_l[4][16], s_ms[4][16], s_mw[4][16];
+  __shared__ __attribute__((aligned(16))) float s_meta[KD_WAVES][4][64];  // k scale, k min, v scale, v min
+  __shared__ float s_o[KD_WAVES][16][KD_DH];
+  __shared__ float s_l[KD_WAVES][16], s_ms[KD_WAVES][16], s_mw[KD_WAVES][16];
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // wavefront w takes positions 64 (w % 4) .. + 63 of every KD_SETS-th chunk,
+  // starting at chunk c0 + w / 4: two wavefronts per SIMD stream the same KV head.
+  const int wq = w & 3, ws0 = w >> 2;
   const int n = lane & 15, g = lane >> 4;
 
   // This (b, h)'s cache rows; positions >= L are outside the resources and read as zero.
@@ -201,7 +210,7 @@ __global__ __launch_bounds__(256) void k_kv_decode(
   const int c0 = split * cpw, c1 = min(chunks, c0 + cpw);
   // One chunk: values of this chunk in vcur, the next chunk's fetched into vnxt.
   auto chunk = [&](const int c, v4u (&vcur)[4], v4u (&vnxt)[4]) {
-    const int kw = c * KD_CHUNK + 64 * w;  // first position of this wavefront's 64
+    const int kw = c * KD_CHUNK + 64 * wq;  // first position of this wavefront's 64
     // metadata of the wavefront's 64 positions, converted once per position
     // (the key's already carrying the log2-domain softmax scale)
     s_meta[w][0][lane] = scale_log2e * fp16_lo(kmeta_reg);
@@ -236,10 +245,10 @@ __global__ __launch_bounds__(256) void k_kv_decode(
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[t][r]);
-    const bool more = c + 1 < c1;
+    const bool more = c + KD_SETS < c1;
     if (more) {
-      load_k(kw + KD_CHUNK);
-      load_v(kw + KD_CHUNK, vnxt);
+      load_k(kw + KD_SETS * KD_CHUNK);
+      load_v(kw + KD_SETS * KD_CHUNK, vnxt);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -250,7 +259,7 @@ __global__ __launch_bounds__(256) void k_kv_decode(
     //      factors 1 instead of NaN. ----
     auto chunk_max = [&](int hd) { return __shfl(mx, hd); };  // lane hd holds head hd's
     const float mnew_n = fmaxf(m_n, mx);
-    if (c > c0) {
+    if (c > c0 + ws0) {
       const float a_n = __builtin_amdgcn_exp2f(m_n - mnew_n);
       l_n *= a_n;
       ms_n *= a_n;
@@ -322,11 +331,14 @@ __global__ __launch_bounds__(256) void k_kv_decode(
       }
     }
   };
-  load_k(c0 * KD_CHUNK + 64 * w);
-  load_v(c0 * KD_CHUNK + 64 * w, vraw);
-  for (int c = c0; c < c1; c += 2) {  // two chunks per trip: the value buffers swap roles
+  const int cs = c0 + ws0;  // this wavefront's first chunk (it may have none)
+  if (cs < c1) {
+    load_k(cs * KD_CHUNK + 64 * wq);
+    load_v(cs * KD_CHUNK + 64 * wq, vraw);
+  }
+  for (int c = cs; c < c1; c += 2 * KD_SETS) {  // two chunks per trip: the value buffers swap roles
     chunk(c, vraw, vnext);
-    if (c + 1 < c1) chunk(c + 1, vnext, vraw);
+    if (c + KD_SETS < c1) chunk(c + KD_SETS, vnext, vraw);
   }
 
   // ---- combine the wavefronts (each with its own running maxima) and write
@@ -347,12 +359,14 @@ __global__ __launch_bounds__(256) void k_kv_decode(
 #pragma unroll
       for (int r = 0; r < 4; ++r) s_o[w][4 * g + r][kd_dim(kb, hs, n)] = O[kb][hs][r];
   __syncthreads();
-  for (int i = tid; i < GQ * KD_DH; i += 256) {
+  for (int i = tid; i < GQ * KD_DH; i += 64 * KD_WAVES) {
     const int hd = i / KD_DH, d = i % KD_DH;
-    const float M = fmaxf(fmaxf(s_mw[0][hd], s_mw[1][hd]), fmaxf(s_mw[2][hd], s_mw[3][hd]));
+    float M = s_mw[0][hd];
+#pragma unroll
+    for (int v = 1; v < KD_WAVES; ++v) M = fmaxf(M, s_mw[v][hd]);
     float o = 0.0f, l = 0.0f;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < KD_WAVES; ++v) {
       const float f = __builtin_amdgcn_exp2f(s_mw[v][hd] - M);
       o = fmaf(f, s_o[v][hd][d] + s_ms[v][hd], o);
       l = fmaf(f, s_l[v][hd], l);
@@ -431,7 +445,7 @@ extern "C" qr_status qr_kv_decode_attention(const void* q_f16, int32_t B, int32_
   const KdPlan p = kd_plan(B, Hkv, L);
   if ((int64_t)B * Hq > INT32_MAX || B > 65535 || Hkv > 65535) return QR_ERR_SHAPE;
   const float scale_log2e = softmax_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(k_kv_decode, dim3(p.splits, Hkv, B), dim3(256), 0, stream,
+  hipLaunchKernelGGL(k_kv_decode, dim3(p.splits, Hkv, B), dim3(64 * KD_WAVES), 0, stream,
                      (const uint16_t*)q_f16, Hq, Hkv, Hq / Hkv, (const uint8_t*)k_cache_q,
                      (const uint32_t*)k_cache_meta, (const uint8_t*)v_cache_q,
                      (const uint32_t*)v_cache_meta, S_max, L, scale_log2e, p.chunks, p.cpw,
