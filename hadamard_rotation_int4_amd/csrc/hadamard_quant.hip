@@ -148,6 +148,9 @@ __device__ __forceinline__ int gmap(int c) {
 #ifndef QR_POW2_WAVES_PER_SIMD
 #define QR_POW2_WAVES_PER_SIMD 2
 #endif
+#ifndef QR_SMALL_UNROLL
+#define QR_SMALL_UNROLL 1
+#endif
 #ifndef QR_POW2_KM
 #define QR_POW2_KM 4
 #endif
@@ -387,30 +390,45 @@ __global__ __launch_bounds__(256) void k_hq_small(const uint16_t* __restrict__ x
   const int wave = tid >> 6;
   const int sub = lane % LPR;  // lane within the row
   const int rw = lane / LPR;   // row within the wavefront
+  // With 16 lanes per row (one DPP row), the lane holds chunk gmap(sub) and
+  // the cross-lane stages run through DPP as in k_hq_pow2; the lane then ends
+  // with sigma * z.  Otherwise chunk sub and lane shuffles.
+  constexpr bool DPP = LPR == 16;
+  const int gc = DPP ? gmap(sub) : sub;
+  const int coff = gc * 8;     // first element of the lane's chunk
+  const float sigma = (DPP && (__builtin_popcount(gc) & 1)) ? -1.0f : 1.0f;
   float sg[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) sg[j] = 1.0f;
   if (rot && signs) {
-    const uint32_t w0 = *(const uint32_t*)(signs + sub * 8), w1 = *(const uint32_t*)(signs + sub * 8 + 4);
+    const uint32_t w0 = *(const uint32_t*)(signs + coff), w1 = *(const uint32_t*)(signs + coff + 4);
 #pragma unroll
     for (int j = 0; j < 8; ++j) sg[j] = (((j < 4 ? w0 : w1) >> (8 * (j & 3) + 7)) & 1u) ? -1.0f : 1.0f;
   }
 
-  for (int64_t base = ((int64_t)blockIdx.x * 4 + wave) * RPW; base < T;
-       base += (int64_t)gridDim.x * 4 * RPW) {
-    const int64_t row = base + rw;
+  // Grid-stride over groups of RPW rows per wavefront; QR_SMALL_UNROLL groups
+  // are loaded before any is processed, so that many loads are in flight.
+  constexpr int U = QR_SMALL_UNROLL;
+  const int64_t gstride = (int64_t)gridDim.x * 4 * RPW;
+  for (int64_t base0 = ((int64_t)blockIdx.x * 4 + wave) * RPW; base0 < T; base0 += U * gstride) {
+  v4u raws[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t r = base0 + u * gstride + rw;
+    raws[u] = r < T ? ld_stream(x + r * ld + coff) : v4u{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t row = base0 + u * gstride + rw;
     const bool valid = row < T;
     float v[8];
-    if (valid) {
-      const v4u raw = *(const v4u*)(x + row * ld + sub * 8);
+    {
+      const v4u raw = raws[u];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         v[2 * j] = h2f((uint16_t)(raw[j] & 0xffffu)) * sg[2 * j];
         v[2 * j + 1] = h2f((uint16_t)(raw[j] >> 16)) * sg[2 * j + 1];
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
     }
     if (rot) {
 #pragma unroll
@@ -422,20 +440,29 @@ __global__ __launch_bounds__(256) void k_hq_small(const uint16_t* __restrict__ x
             v[j] = a + b;
             v[j + h] = a - b;
           }
+      if constexpr (DPP) {
+        const float s0 = (gc & 1) ? -1.0f : 1.0f, s1 = (gc & 2) ? -1.0f : 1.0f;
+        const float s2 = (gc & 4) ? -1.0f : 1.0f, s3 = (gc & 8) ? -1.0f : 1.0f;
+        QR_DPP8("quad_perm:[1,0,3,2]", v, s0);
+        QR_DPP8("quad_perm:[2,3,0,1]", v, s1);
+        QR_DPP8("row_half_mirror", v, s2);
+        QR_DPP8("row_mirror", v, s3);
+      } else {
 #pragma unroll
-      for (int h = 1; h < LPR; h <<= 1) {
-        const float s = (sub & h) ? -1.0f : 1.0f;
+        for (int h = 1; h < LPR; h <<= 1) {
+          const float s = (sub & h) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = __shfl_xor(v[j], h);
-          v[j] = fmaf(v[j], s, p);  // low lane: mine + partner; high lane: partner - mine
+          for (int j = 0; j < 8; ++j) {
+            const float p = __shfl_xor(v[j], h);
+            v[j] = fmaf(v[j], s, p);  // low lane: mine + partner; high lane: partner - mine
+          }
         }
       }
     }
     if (valid && zdbg) {
-      float* zr = zdbg + row * D + sub * 8;
-      *(v4f*)zr = v4f{v[0], v[1], v[2], v[3]};
-      *(v4f*)(zr + 4) = v4f{v[4], v[5], v[6], v[7]};
+      float* zr = zdbg + row * D + coff;
+      *(v4f*)zr = v4f{v[0] * sigma, v[1] * sigma, v[2] * sigma, v[3] * sigma};
+      *(v4f*)(zr + 4) = v4f{v[4] * sigma, v[5] * sigma, v[6] * sigma, v[7] * sigma};
     }
     if (MODE == MODE_QUANT) {
       float am = 0.0f;
@@ -446,28 +473,31 @@ __global__ __launch_bounds__(256) void k_hq_small(const uint16_t* __restrict__ x
       uint16_t sh;
       float m;
       sym_scale(am, c, clip, &sh, &m);
+      const float ml = m * sigma;  // v * ml = z * m exactly
       if (valid) {
-        *(uint32_t*)(q + row * (D / 2) + sub * 4) = (CLAMP || (sh & 0x7fffu) < 0x0400u)
-                                                        ? quant_pack8<true>(v, m)
-                                                        : quant_pack8<false>(v, m);
+        *(uint32_t*)(q + row * (D / 2) + coff / 2) = (CLAMP || (sh & 0x7fffu) < 0x0400u)
+                                                         ? quant_pack8<true>(v, ml)
+                                                         : quant_pack8<false>(v, ml);
         if (sub == 0) scale[row] = sh;
       }
     } else if (valid) {
+      const float cs = c * sigma;
       if (MODE == MODE_ROT_F32) {
-        float* yr = (float*)yout + row * D + sub * 8;
-        *(v4f*)yr = v4f{__fmul_rn(v[0], c), __fmul_rn(v[1], c), __fmul_rn(v[2], c),
-                        __fmul_rn(v[3], c)};
-        *(v4f*)(yr + 4) = v4f{__fmul_rn(v[4], c), __fmul_rn(v[5], c), __fmul_rn(v[6], c),
-                              __fmul_rn(v[7], c)};
+        float* yr = (float*)yout + row * D + coff;
+        *(v4f*)yr = v4f{__fmul_rn(v[0], cs), __fmul_rn(v[1], cs), __fmul_rn(v[2], cs),
+                        __fmul_rn(v[3], cs)};
+        *(v4f*)(yr + 4) = v4f{__fmul_rn(v[4], cs), __fmul_rn(v[5], cs), __fmul_rn(v[6], cs),
+                              __fmul_rn(v[7], cs)};
       } else {
         v4u o;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          o[j] = (uint32_t)f2h(__fmul_rn(v[2 * j], c)) |
-                 ((uint32_t)f2h(__fmul_rn(v[2 * j + 1], c)) << 16);
-        *(v4u*)((uint16_t*)yout + row * D + sub * 8) = o;
+          o[j] = (uint32_t)f2h(__fmul_rn(v[2 * j], cs)) |
+                 ((uint32_t)f2h(__fmul_rn(v[2 * j + 1], cs)) << 16);
+        *(v4u*)((uint16_t*)yout + row * D + coff) = o;
       }
     }
+  }
   }
 }
 
@@ -1213,7 +1243,10 @@ static qr_status launch_small(int d, int rot, const uint16_t* x, int64_t T, int6
                               float* z, void* y, hipStream_t st) {
   const int lpr = d / 8;
   const int rows_per_block = 4 * (64 / lpr);
-  const int grid = grid_for(T, rows_per_block, 4096);
+#ifndef QR_SMALL_GRID
+#define QR_SMALL_GRID 2048
+#endif
+  const int grid = grid_for(T, rows_per_block, QR_SMALL_GRID);
   switch (lpr) {
 #define QR_CASE(L)                                                                     \
   case L:                                                                              \

@@ -19,11 +19,69 @@
 
 namespace qr {
 
+// n / d for 0 <= n < 2^31 with a host-computed multiplier:
+// q = (umulhi(n, m) + n) >> s with s = ceil(log2 d), m = floor(2^32 (2^s - d) / d) + 1.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+static FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  f.s = 0;
+  while ((1ull << f.s) < d) ++f.s;
+  f.m = (uint32_t)((((1ull << 32) * ((1ull << f.s) - d)) / d + 1) & 0xffffffffull);
+  return f;
+}
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+// One butterfly stage across lanes for eight registers: r += dpp(r) * s (the
+// leading s_nop covers the VALU-write -> DPP-read hazard).
+#define QR_KV_DPP8(CTRL, r, s)                                                         \
+  asm volatile(                                                                        \
+      "s_nop 1\n\t"                                                                    \
+      "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"                  \
+      : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), \
+        "+v"(r[7])                                                                     \
+      : "v"(s))
+
+// Lane-in-row c (0..15) -> 8-element chunk, linear over GF(2) with
+// kv_gmap(1) = 1, kv_gmap(2) = 2, kv_gmap(7) = 4, kv_gmap(15) = 8: the DPP
+// patterns xor 1, xor 2 (quad_perm), xor 7 (row_half_mirror) and xor 15
+// (row_mirror) then each flip exactly one chunk bit.
+__device__ __forceinline__ int kv_gmap(int c) {
+  const int c0 = c & 1, c1 = (c >> 1) & 1, c2 = (c >> 2) & 1, c3 = (c >> 3) & 1;
+  return (c0 ^ c2) | ((c1 ^ c2) << 1) | ((c2 ^ c3) << 2) | (c3 << 3);
+}
+// Max / min over the 16 lanes of a DPP row (quad_perm [1,0,3,2] and [2,3,0,1],
+// row_half_mirror, row_mirror).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                            0xF, 0xF, false));
+}
+#define QR_ROW16(OP, v)                   \
+  do {                                    \
+    v = OP(v, dpp_f<0xB1>(v));            \
+    v = OP(v, dpp_f<0x4E>(v));            \
+    v = OP(v, dpp_f<0x141>(v));           \
+    v = OP(v, dpp_f<0x140>(v));           \
+  } while (0)
+
 template <int LPR, bool ROT>
 __global__ __launch_bounds__(256) void k_kv_quant(
     const uint16_t* __restrict__ x, int64_t rows, int S_new, int H, int64_t ld_token,
     const int8_t* __restrict__ signs, int group, float c, float clip, uint8_t* __restrict__ cq,
-    uint16_t* __restrict__ meta, int S_max, int start_pos, float* __restrict__ zdbg) {
+    uint16_t* __restrict__ meta, int S_max, int start_pos, float* __restrict__ zdbg, FastDiv fdH,
+    FastDiv fdS) {
   constexpr int DH = LPR * 8;
   constexpr int RPW = 64 / LPR;
   const int tid = threadIdx.x;
@@ -33,11 +91,19 @@ __global__ __launch_bounds__(256) void k_kv_quant(
   const int rw = lane / LPR;
   const int lpg = group / 8;  // lanes per group
   const int ngroups = DH / group;
+  // With 16 lanes per row and one group per row the lane holds chunk
+  // kv_gmap(sub) and both the butterflies and the min / max run through DPP
+  // inside the 16-lane row; the lane then holds sigma * z.  Otherwise chunk
+  // sub and lane shuffles.
+  const bool dpp = LPR == 16 && group == DH;
+  const int gc = dpp ? kv_gmap(sub) : sub;
+  const int coff = gc * 8;
+  const float sigma = (ROT && dpp && (__builtin_popcount(gc) & 1)) ? -1.0f : 1.0f;
   float sg[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) sg[j] = 1.0f;
   if (ROT && signs) {
-    const uint32_t w0 = *(const uint32_t*)(signs + sub * 8), w1 = *(const uint32_t*)(signs + sub * 8 + 4);
+    const uint32_t w0 = *(const uint32_t*)(signs + coff), w1 = *(const uint32_t*)(signs + coff + 4);
 #pragma unroll
     for (int j = 0; j < 8; ++j) sg[j] = (((j < 4 ? w0 : w1) >> (8 * (j & 3) + 7)) & 1u) ? -1.0f : 1.0f;
   }
@@ -46,11 +112,11 @@ __global__ __launch_bounds__(256) void k_kv_quant(
        base += (int64_t)gridDim.x * 4 * RPW) {
     const int64_t row = base + rw;  // row = (b * S_new + s) * H + h
     const bool valid = row < rows;
-    const int64_t tok = row / H;
-    const int h = (int)(row - tok * H);
+    const uint32_t tok = fast_div((uint32_t)row, fdH);
+    const int h = (int)((uint32_t)row - tok * (uint32_t)H);
     float v[8];
     if (valid) {
-      const v4u raw = *(const v4u*)(x + tok * ld_token + (int64_t)h * DH + sub * 8);
+      const v4u raw = *(const v4u*)(x + (int64_t)tok * ld_token + (int64_t)h * DH + coff);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         v[2 * j] = h2f((uint16_t)(raw[j] & 0xffffu)) * sg[2 * j];
@@ -70,34 +136,49 @@ __global__ __launch_bounds__(256) void k_kv_quant(
             v[j] = a + b;
             v[j + hh] = a - b;
           }
+      if (LPR == 16 && dpp) {
+        const float s0 = (gc & 1) ? -1.0f : 1.0f, s1 = (gc & 2) ? -1.0f : 1.0f;
+        const float s2 = (gc & 4) ? -1.0f : 1.0f, s3 = (gc & 8) ? -1.0f : 1.0f;
+        QR_KV_DPP8("quad_perm:[1,0,3,2]", v, s0);
+        QR_KV_DPP8("quad_perm:[2,3,0,1]", v, s1);
+        QR_KV_DPP8("row_half_mirror", v, s2);
+        QR_KV_DPP8("row_mirror", v, s3);
+      } else {
 #pragma unroll
-      for (int hh = 1; hh < LPR; hh <<= 1) {
-        const float s = (sub & hh) ? -1.0f : 1.0f;
+        for (int hh = 1; hh < LPR; hh <<= 1) {
+          const float s = (sub & hh) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = __shfl_xor(v[j], hh);
-          v[j] = fmaf(v[j], s, p);
+          for (int j = 0; j < 8; ++j) {
+            const float p = __shfl_xor(v[j], hh);
+            v[j] = fmaf(v[j], s, p);
+          }
         }
       }
     }
     if (valid && zdbg) {
-      float* zr = zdbg + row * DH + sub * 8;
-      *(v4f*)zr = v4f{v[0], v[1], v[2], v[3]};
-      *(v4f*)(zr + 4) = v4f{v[4], v[5], v[6], v[7]};
+      float* zr = zdbg + row * DH + coff;
+      *(v4f*)zr = v4f{v[0] * sigma, v[1] * sigma, v[2] * sigma, v[3] * sigma};
+      *(v4f*)(zr + 4) = v4f{v[4] * sigma, v[5] * sigma, v[6] * sigma, v[7] * sigma};
     }
-    // y = fp32(z * c)
+    // y = fp32(z * c) (= sigma * fp32(v * c) exactly)
+    const float cs = c * sigma;
     float y[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) y[j] = ROT ? __fmul_rn(v[j], c) : v[j];
+    for (int j = 0; j < 8; ++j) y[j] = ROT ? __fmul_rn(v[j], cs) : v[j];
     float mx = y[0], mn = y[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) {
       mx = fmaxf(mx, y[j]);
       mn = fminf(mn, y[j]);
     }
-    for (int hh = 1; hh < lpg; hh <<= 1) {
-      mx = fmaxf(mx, __shfl_xor(mx, hh));
-      mn = fminf(mn, __shfl_xor(mn, hh));
+    if (LPR == 16 && dpp) {
+      QR_ROW16(fmaxf, mx);
+      QR_ROW16(fminf, mn);
+    } else {
+      for (int hh = 1; hh < lpg; hh <<= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, hh));
+        mn = fminf(mn, __shfl_xor(mn, hh));
+      }
     }
     const float mxc = __fmul_rn(clip, mx);
     const float mnc = __fmul_rn(clip, mn);
@@ -122,12 +203,12 @@ __global__ __launch_bounds__(256) void k_kv_quant(
     const uint32_t word = __builtin_amdgcn_perm(p1, p0, 0x0c0c0400u) |
                           __builtin_amdgcn_perm(p3, p2, 0x04000c0cu);
     if (valid) {
-      const int64_t b = tok / S_new;
-      const int s = (int)(tok - b * S_new);
+      const int64_t b = fast_div(tok, fdS);
+      const int s = (int)(tok - (uint32_t)b * (uint32_t)S_new);
       const int64_t crow = (b * H + h) * (int64_t)S_max + start_pos + s;
-      *(uint32_t*)(cq + crow * (DH / 2) + sub * 4) = word;
-      if ((sub % lpg) == 0) {
-        const int gi = sub / lpg;
+      *(uint32_t*)(cq + crow * (DH / 2) + coff / 2) = word;
+      if ((gc % lpg) == 0) {
+        const int gi = gc / lpg;
         *(uint32_t*)(meta + (crow * ngroups + gi) * 2) = (uint32_t)sh | ((uint32_t)mh << 16);
       }
     }
@@ -148,7 +229,7 @@ static qr_status launch_kv(int dh, const uint16_t* x, int64_t rows, int S_new, i
   case L:                                                                                       \
     hipLaunchKernelGGL((k_kv_quant<L, ROT>), dim3((int)grid), dim3(256), 0, st, x, rows, \
                        S_new, H, ld_token, signs, group, c, clip, cq, meta, S_max, start_pos,   \
-                       zdbg);                                                                   \
+                       zdbg, make_fastdiv((uint32_t)H), make_fastdiv((uint32_t)S_new));         \
     break;
     QR_CASE(1)
     QR_CASE(2)
@@ -186,6 +267,7 @@ extern "C" qr_status qr_kv_rotate_quant(const void* kv_f16, int32_t B, int32_t S
       (rot == QR_ROT_HADAMARD && signs && !aligned(signs, 4)))
     return QR_ERR_ALIGN;
   const int64_t rows = (int64_t)B * S_new * H;
+  if (rows > INT32_MAX) return QR_ERR_SHAPE;
   const uint16_t* x = (const uint16_t*)kv_f16;
   uint8_t* cq = (uint8_t*)cache_q;
   uint16_t* meta = (uint16_t*)cache_meta;
