@@ -37,6 +37,7 @@
 //  * Tile order: workgroup ids are remapped so that the ids the hardware places
 //    on one XCD (id % 8) are consecutive, then grouped 8 tile-rows at a time, so
 //    the tiles running together on an XCD share A and W panels in its L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -334,76 +335,98 @@ static double tile_score(int64_t T, int64_t N, int bm, int bn, double eff, int s
 // Decode (T <= 64): weight-streaming GEMM
 // ===========================================================================
 // With a handful of tokens the product is bound by reading W once.  A
-// workgroup owns 16 output channels (one MFMA column block) and all T <= 64
-// tokens (up to 4 MFMA row blocks); its 4 wavefronts split K in 128-element
-// blocks and each streams its part of the 16 weight rows exactly once with
-// v_mfma_i32_16x16x64_i8.  Lane (row i, group g) of a block holds packed
-// bytes 16 g .. 16 g + 15 (k = 32 g .. 32 g + 31) and feeds two MFMAs, one per
-// 8-byte half, identically for A and W.  The four partial accumulators are
-// summed through LDS and wavefront 0 applies the fp32 epilogue.  N / 16
-// workgroups: 256 to 768 for the Llama-2 projections.
+// workgroup owns S strips of 16 output channels (16 S consecutive rows of W)
+// and all T <= 64 tokens (MT MFMA row blocks of 16); its 4 wavefronts split K
+// in 128-element blocks and each streams its part of the 16 S weight rows
+// exactly once with v_mfma_i32_16x16x64_i8.  Lane (row i, group g) of a block
+// holds packed bytes 16 g .. 16 g + 15 (k = 32 g .. 32 g + 31) and feeds two
+// MFMAs, one per 8-byte half, identically for A and W.  The activation
+// fragments of a block are loaded and unpacked once and used for all S
+// strips, so the unpacking of A, which dominates the vector work at T = 64,
+// is shared S ways.  Loads run CH blocks ahead in a second register buffer;
+// blocks past the wavefront's range or past K read as zero through the
+// buffer range check (their offsets point past the resource).  The four
+// partial accumulators are summed through LDS; wavefront 0 applies the fp32
+// epilogue into an LDS tile [token][channel] that the whole workgroup then
+// stores row by row (whole 4-byte words from consecutive lanes, instead of
+// one 2-byte store per accumulator element).
 constexpr int DEC_BN = 16;
 
-template <int MT, bool DBG>
-__global__ __launch_bounds__(256) void k_w4a4_decode(
+#ifndef QR_DEC_WAVES
+#define QR_DEC_WAVES 4
+#endif
+// Cache policy of the weight stream (2 = non-temporal measured no faster).
+#ifndef QR_DEC_WPOL
+#define QR_DEC_WPOL 0
+#endif
+#ifndef QR_DEC_LOADS
+#define QR_DEC_LOADS 16
+#endif
+constexpr int DEC_WAVES = QR_DEC_WAVES;
+
+template <int MT, int S, int CH, bool DBG>
+__global__ __launch_bounds__(64 * DEC_WAVES, 1) void k_w4a4_decode(
     const uint8_t* __restrict__ A, const uint16_t* __restrict__ a_scale, int T,
     const uint8_t* __restrict__ W, const uint16_t* __restrict__ w_scale, int N, int K,
     uint16_t* __restrict__ Y, int32_t* __restrict__ acc_dbg) {
-  // Blocks per chunk: a wavefront keeps two chunks of loads in flight,
-  // 2 * CH * (1 + MT) 16-byte loads per lane.
-  constexpr int CH = 8 / MT;
-  __shared__ v4i s_part[3][MT][64];
+  __shared__ v4i s_part[DEC_WAVES - 1][S][MT][64];
+  __shared__ uint32_t s_y[64][DEC_BN * S / 2 + 1];  // fp16 outputs, [token][channel pair]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * DEC_BN;
+  const int n0 = blockIdx.x * (DEC_BN * S);
   const int rowbytes = K / 2;
   // Rows past T (tokens) or N (channels) are outside the buffers' ranges and read as zero.
   const __amdgpu_buffer_rsrc_t rsrc_a =
       __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, T * rowbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsrc_w = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (int64_t)n0 * rowbytes), 0, min(N - n0, DEC_BN) * rowbytes, 0x00020000);
+      (void*)(W + (int64_t)n0 * rowbytes), 0, min(N - n0, DEC_BN * S) * rowbytes, 0x00020000);
   const int kblocks = (K + 127) / 128;
-  const int per = (kblocks + 3) / 4;
+  const int per = (kblocks + DEC_WAVES - 1) / DEC_WAVES;
   const int kb0 = wave * per, kb1 = min(kblocks, kb0 + per);
 
-  v4u wv[2][CH], av[2][CH][MT];
-  // Load chunk starting at block kb into buffer b; blocks past kb1 and the
-  // bytes of a final half block (K % 128 == 64) read as zero.
+  v4u wv[2][CH][S], av[2][CH][MT];
   auto load = [&](auto bt, int kb) {
     constexpr int b = decltype(bt)::value;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int byte = (kb + c) * 64 + 16 * g;
       const bool ok = kb + c < kb1 && byte < rowbytes;
-      const int off = ok ? byte : 0;
-      wv[b][c] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_w, i * rowbytes + off, 0, 0));
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        wv[b][c][s] = __builtin_bit_cast(
+            v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                     rsrc_w, ok ? (16 * s + i) * rowbytes + byte : INT32_MIN, 0, QR_DEC_WPOL));
 #pragma unroll
       for (int m = 0; m < MT; ++m)
         av[b][c][m] = __builtin_bit_cast(
-            v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, (16 * m + i) * rowbytes + off, 0, 0));
-      if (!ok) {
-        wv[b][c] = v4u{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int m = 0; m < MT; ++m) av[b][c][m] = v4u{0u, 0u, 0u, 0u};
-      }
+            v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                     rsrc_a, ok ? (16 * m + i) * rowbytes + byte : INT32_MIN, 0, 0));
     }
   };
-  v4i acc[MT];
+  v4i acc[S][MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = v4i{0, 0, 0, 0};
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[s][m] = v4i{0, 0, 0, 0};
   auto compute = [&](auto bt) {
     constexpr int b = decltype(bt)::value;
 #pragma unroll
     for (int c = 0; c < CH; ++c)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const v4i bw = unpack16(make_uint2(wv[b][c][2 * e], wv[b][c][2 * e + 1]));
+        v4i ua[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          acc[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-              unpack16(make_uint2(av[b][c][m][2 * e], av[b][c][m][2 * e + 1])), bw, acc[m], 0, 0, 0);
+          ua[m] = unpack16(make_uint2(av[b][c][m][2 * e], av[b][c][m][2 * e + 1]));
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const v4i bw = unpack16(make_uint2(wv[b][c][s][2 * e], wv[b][c][s][2 * e + 1]));
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            acc[s][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua[m], bw, acc[s][m], 0, 0, 0);
+        }
       }
   };
   using B0 = std::integral_constant<int, 0>;
@@ -418,45 +441,102 @@ __global__ __launch_bounds__(256) void k_w4a4_decode(
   }
   if (wave > 0) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) s_part[wave - 1][m][lane] = acc[m];
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) s_part[wave - 1][s][m][lane] = acc[s][m];
   }
   __syncthreads();
-  if (wave != 0) return;
+  // Wavefront 0 sums the partial accumulators and applies the epilogue into
+  // LDS ([token][channel], fp16); the 16x16 accumulator layout is lane (col i,
+  // group g), register r -> row 4 g + r.
+  if (wave == 0) {
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+    for (int s = 0; s < S; ++s) {
+      const int n = n0 + 16 * s + i;
+      const float ws = n < N ? h2f(w_scale[n]) : 0.0f;
 #pragma unroll
-    for (int w2 = 0; w2 < 3; ++w2) acc[m] += s_part[w2][m][lane];
-  // 16x16 accumulator layout: lane (col i, group g), register r -> row 4 g + r
-  const int n = n0 + i;
-  if (n >= N) return;
-  const float ws = h2f(w_scale[n]);
+      for (int m = 0; m < MT; ++m) {
+        v4i a4 = acc[s][m];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+        for (int w2 = 0; w2 < DEC_WAVES - 1; ++w2) a4 += s_part[w2][s][m][lane];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * m + 4 * g + r;
-      if (t < T) {
-        const int32_t a = acc[m][r] >> 8;  // exact: the accumulator is 256 * acc
-        Y[(int64_t)t * N + n] = f2h(__fmul_rn(__fmul_rn((float)a, h2f(a_scale[t])), ws));
-        if (DBG) acc_dbg[(int64_t)t * N + n] = a;
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * m + 4 * g + r;
+          if (t < T) {
+            const int32_t a = a4[r] >> 8;  // exact: the accumulator is 256 * acc
+            ((uint16_t*)&s_y[t][0])[16 * s + i] =
+                f2h(__fmul_rn(__fmul_rn((float)a, h2f(a_scale[t])), ws));
+            if (DBG && n < N) acc_dbg[(int64_t)t * N + n] = a;
+          }
+        }
       }
     }
+  }
+  __syncthreads();
+  // Every thread stores channel pairs: consecutive lanes write consecutive
+  // 4-byte words of a token's row (2-byte stores when N is odd).
+  constexpr int P = DEC_BN * S / 2;
+  const int nloc = min(N - n0, DEC_BN * S);
+  for (int idx = tid; idx < T * P; idx += 64 * DEC_WAVES) {
+    const int t = idx / P, nl = 2 * (idx - t * P);
+    if (nl >= nloc) continue;
+    const uint32_t v = s_y[t][nl / 2];
+    uint16_t* yp = Y + (int64_t)t * N + n0 + nl;
+    if ((N & 1) == 0 && nl + 1 < nloc) {
+      *(uint32_t*)yp = v;  // n0 + nl and t N are even, Y is 4-byte aligned
+    } else {
+      yp[0] = (uint16_t)(v & 0xffffu);
+      if (nl + 1 < nloc) yp[1] = (uint16_t)(v >> 16);
+    }
+  }
 }
 
+template <int MT, int S>
+static qr_status launch_decode_s(const void* a_q, const void* a_scale, int64_t T, const void* w_q,
+                                 const void* w_scale, int64_t N, int64_t K, void* y, int32_t* acc,
+                                 hipStream_t stream) {
+  // Blocks per load chunk: two chunks of (S + MT) 16-byte loads per lane in flight.
+  constexpr int CH = (QR_DEC_LOADS / (S + MT)) > 0 ? QR_DEC_LOADS / (S + MT) : 1;
+  const int64_t blocks = (N + DEC_BN * S - 1) / (DEC_BN * S);
+  if (acc)
+    hipLaunchKernelGGL((k_w4a4_decode<MT, S, CH, true>), dim3((unsigned)blocks), dim3(64 * DEC_WAVES),
+                       0, stream, (const uint8_t*)a_q, (const uint16_t*)a_scale, (int)T,
+                       (const uint8_t*)w_q, (const uint16_t*)w_scale, (int)N, (int)K,
+                       (uint16_t*)y, acc);
+  else
+    hipLaunchKernelGGL((k_w4a4_decode<MT, S, CH, false>), dim3((unsigned)blocks), dim3(64 * DEC_WAVES),
+                       0, stream, (const uint8_t*)a_q, (const uint16_t*)a_scale, (int)T,
+                       (const uint8_t*)w_q, (const uint16_t*)w_scale, (int)N, (int)K,
+                       (uint16_t*)y, (int32_t*)nullptr);
+  return launch_status();
+}
+
+// Strips per workgroup.  With one row block of tokens (T <= 16) the weight
+// stream is all that matters and one strip per workgroup gives the most
+// workgroups; with more tokens every workgroup re-reads all of A through the
+// L2, so strips are grouped until one workgroup per compute unit covers N
+// (at most 4), which divides that traffic and the unpacking of A.
 template <int MT>
 static qr_status launch_decode(const void* a_q, const void* a_scale, int64_t T, const void* w_q,
                                const void* w_scale, int64_t N, int64_t K, void* y, int32_t* acc,
                                hipStream_t stream) {
-  const int64_t blocks = (N + DEC_BN - 1) / DEC_BN;
-  if (acc)
-    hipLaunchKernelGGL((k_w4a4_decode<MT, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const uint8_t*)a_q, (const uint16_t*)a_scale, (int)T, (const uint8_t*)w_q,
-                       (const uint16_t*)w_scale, (int)N, (int)K, (uint16_t*)y, acc);
-  else
-    hipLaunchKernelGGL((k_w4a4_decode<MT, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const uint8_t*)a_q, (const uint16_t*)a_scale, (int)T, (const uint8_t*)w_q,
-                       (const uint16_t*)w_scale, (int)N, (int)K, (uint16_t*)y, (int32_t*)nullptr);
-  return launch_status();
+#ifndef QR_DEC_SLOTS
+#define QR_DEC_SLOTS 256
+#endif
+#ifndef QR_DEC_SMAX
+#define QR_DEC_SMAX 4
+#endif
+  const int64_t strips = (N + DEC_BN - 1) / DEC_BN;
+  const int64_t s =
+      MT == 1 ? 1
+              : std::min<int64_t>(QR_DEC_SMAX,
+                                  std::max<int64_t>(1, (strips + QR_DEC_SLOTS - 1) / QR_DEC_SLOTS));
+  switch (s) {
+    case 1: return launch_decode_s<MT, 1>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
+    case 2: return launch_decode_s<MT, 2>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
+    case 3: return launch_decode_s<MT, 3>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
+    default: return launch_decode_s<MT, 4>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
+  }
 }
 
 }  // namespace qr
