@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--workload 70b_prefill|7b_prefill|7b_decode|70b_kv]
-                    [--no-cpu-baseline] [--copy-calibration]
+                    [--no-cpu-baseline] [--copy-calibration] [--fp16-hadamard]
 
 One step is one pass of the whole hot path over one batch of synthetic input
 (inputs resident in HBM; weights prepared offline and not timed):
@@ -13,7 +13,9 @@ One step is one pass of the whole hot path over one batch of synthetic input
   the down-projection input, d = K of its GEMM); the five W4A4 GEMMs (QKV, O,
   gate, up, down) with the scale epilogue; head-wise Hadamard + asymmetric
   4-bit group-128 quantization of K and V into the cache (Init of the prompt);
-  the head-wise rotation of Q.
+  the head-wise rotation of Q.  With --fp16-hadamard the down-projection
+  rotation (d = 28672) runs the fp16 variant of the transform
+  (QR_ROT_HADAMARD_F16) instead of the default fp32 one.
 * 7b_decode: the same four rotations and five GEMMs at T = 1, 8, 32 and 64.
 * 70b_kv: K/V Init of a 32 x 2048-token prompt (8 KV heads of 128), the
   rotation of its queries (64 heads), then 50 decode steps of Append K, V,
@@ -66,6 +68,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--fp16-hadamard", action="store_true",
+                    help="70B down-projection rotation with the fp16 transform")
     return ap.parse_args()
 
 
@@ -108,7 +112,7 @@ def decode_bytes(b, hkv, hq, L, dh, group):
 # Workload construction: a list of launches (kernel, label, bytes, ops, fn)
 # ---------------------------------------------------------------------------
 
-def make_block(torch, qr, wl, W, T, dev, with_kv):
+def make_block(torch, qr, wl, W, T, dev, with_kv, f16_down=False):
     lin = {l.name: l for l in W.linears}
     H, ffn, wid = W.hidden, lin["down"].k, W.wid
     inputs = {}
@@ -130,9 +134,10 @@ def make_block(torch, qr, wl, W, T, dev, with_kv):
     L = []
     tag = f"T{T}:" if not with_kv else ""
     for name, x in inputs.items():
-        L.append(("hadamard_quant", tag + name, hq_bytes(T, x.shape[1]), 0,
-                  (lambda x=x, name=name: qr.hadamard_quant(x, signs[x.shape[1]], 1.0,
-                                                            out=qbuf[name])), qbuf[name]))
+        f16 = f16_down and name == "down_in" and x.shape[1] == 28672
+        L.append(("hadamard_quant", tag + name + (":fp16" if f16 else ""), hq_bytes(T, x.shape[1]), 0,
+                  (lambda x=x, name=name, f16=f16: qr.hadamard_quant(
+                      x, signs[x.shape[1]], 1.0, out=qbuf[name], fp16_transform=f16)), qbuf[name]))
     for name, l in lin.items():
         L.append(("w4a4_gemm", tag + name, gemm_bytes(T, l.n, l.k), gemm_ops(T, l.n, l.k),
                   (lambda name=name, l=l: qr.w4a4_gemm(*qbuf[l.input], *wq[name],
@@ -371,11 +376,13 @@ def main():
     config = {"workload": None}
     if wname in ("70b_prefill", "7b_prefill"):
         T = W.tokens[0]
-        launches, lin, kvdesc = make_block(torch, qr, wl, W, T, dev, True)
+        launches, lin, kvdesc = make_block(torch, qr, wl, W, T, dev, True, args.fp16_hadamard)
         config.update({
             "workload": f"{W.name}: T={T} tokens, hidden {W.hidden}, FFN {lin['down'].k}, QKV "
                         f"{lin['qkv'].n}; 4 fused rotate+quant, 5 W4A4 GEMMs, {kvdesc}",
-            "tokens": T, "hidden": W.hidden, "ffn": lin["down"].k})
+            "tokens": T, "hidden": W.hidden, "ffn": lin["down"].k,
+            "hadamard_arithmetic": ("fp16 for d = 28672, fp32 otherwise"
+                                    if args.fp16_hadamard and lin["down"].k == 28672 else "fp32")})
         dominant, bound = "w4a4_gemm", "mfma"
     elif wname == "7b_decode":
         launches = []

@@ -7,7 +7,8 @@ still succeeds, but the first call raises, naming the build command; nothing
 falls back to a CPU or PyTorch implementation.
 
 Functions (same names as the C entry points without the ``qr_`` prefix):
-  hadamard_quant(x, signs, clip_ratio, rotate=True, z_dbg=False) -> (q_u8, scale_f16[, z])
+  hadamard_quant(x, signs, clip_ratio, rotate=True, z_dbg=False, fp16_transform=False)
+      -> (q_u8, scale_f16[, z])
   hadamard(x, signs, out_dtype=torch.float32, out=None) -> y
   w4a4_gemm(a_q, a_scale, w_q, w_scale, acc_dbg=False) -> y_f16[, acc_i32]
   kv_rotate_quant(kv, signs, group, clip_ratio, cache_q, cache_meta, start_pos,
@@ -25,6 +26,7 @@ LIB_PATH = Path(__file__).resolve().parent / "lib" / "libquarot_hip.so"
 
 QR_ROT_NONE = 0
 QR_ROT_HADAMARD = 1
+QR_ROT_HADAMARD_F16 = 2
 
 _lib = None
 
@@ -132,11 +134,12 @@ def _signs(signs, d, device):
 
 
 def hadamard_quant(x, signs=None, clip_ratio: float = 1.0, rotate: bool = True,
-                   z_dbg: bool = False, out=None, stream=None):
+                   z_dbg: bool = False, out=None, stream=None, fp16_transform: bool = False):
     """Rotate (optionally) and quantize the rows of x [T, d] (fp16, row stride % 8 == 0).
 
     Returns (q uint8 [T, d/2], scale fp16 [T]) and, with z_dbg, z fp32 [T, d].
-    ``out`` may pass preallocated (q, scale) tensors.
+    ``out`` may pass preallocated (q, scale) tensors.  ``fp16_transform`` selects
+    QR_ROT_HADAMARD_F16 (the transform's additions in fp16; d = 28672 only).
     """
     torch = _torch()
     _need(x, torch.float16, "x", 2)
@@ -155,7 +158,8 @@ def hadamard_quant(x, signs=None, clip_ratio: float = 1.0, rotate: bool = True,
             raise ValueError("out tensors have the wrong size or layout")
     z = torch.empty((T, d), dtype=torch.float32, device=x.device) if z_dbg else None
     code = _load().qr_hadamard_quant(_ptr(x), T, d, x.stride(0) if T > 0 else d,
-                                     QR_ROT_HADAMARD if rotate else QR_ROT_NONE, _ptr(s),
+                                     (QR_ROT_HADAMARD_F16 if fp16_transform else QR_ROT_HADAMARD)
+                                     if rotate else QR_ROT_NONE, _ptr(s),
                                      float(clip_ratio), _ptr(q), _ptr(sc), _ptr(z), _stream(stream))
     _check(code, "qr_hadamard_quant")
     return (q, sc, z) if z_dbg else (q, sc)

@@ -716,7 +716,180 @@ constexpr H112Frags make_h112_frags() {
 }
 __device__ const H112Frags g_h112_frags = make_h112_frags();
 
-template <int MODE, bool CLAMP>
+// ---- fp16 variant of the transform after the matrix-core stage ----
+// QuaRot paper, appendix on the FP16 Hadamard transformation (Table 10): the
+// online transform may run in fp16 without changing accuracy.  Here every
+// stage after the exact H_112 products rounds to fp16 (round to nearest
+// even), two values per register: v_pk_add_f16 between registers and
+// v_pk_fmac_f16 with DPP across lanes (one instruction per two values where
+// the fp32 path needs one per value).  The stages carry z / 128 (the A
+// fragments are +-2^-7), and z_dbg reports 128 times the fp16 values.
+
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+// One fp16 butterfly stage across lanes for eight packed registers: r += dpp(r) * s.
+#define QR_DPP8H(CTRL, r, s)                                                           \
+  asm volatile(                                                                        \
+      "s_nop 1\n\t"                                                                    \
+      "v_pk_fmac_f16_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_pk_fmac_f16_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_pk_fmac_f16_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_pk_fmac_f16_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_pk_fmac_f16_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_pk_fmac_f16_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_pk_fmac_f16_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_pk_fmac_f16_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"               \
+      : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), \
+        "+v"(r[7])                                                                     \
+      : "v"(s))
+
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {  // v_cvt_pk_f16_f32 (RNE)
+  return __builtin_bit_cast(uint32_t, h2v{(_Float16)a, (_Float16)b});
+}
+__device__ __forceinline__ uint32_t hadd2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2v, a) + __builtin_bit_cast(h2v, b));
+}
+__device__ __forceinline__ uint32_t hsub2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2v, a) - __builtin_bit_cast(h2v, b));
+}
+// max(acc, |h.lo|, |h.hi|) on the low half of acc (fp16)
+__device__ __forceinline__ uint32_t hmax3abs(uint32_t acc, uint32_t h) {
+  asm("v_max3_f16 %0, |%1|, |%1|, %0 op_sel:[0,1,0,0]" : "+v"(acc) : "v"(h));
+  return acc;
+}
+__device__ __forceinline__ float hlo(uint32_t h) { return (float)__builtin_bit_cast(h2v, h)[0]; }
+__device__ __forceinline__ float hhi(uint32_t h) { return (float)__builtin_bit_cast(h2v, h)[1]; }
+// Eight fp16 values (four packed words) times m -> packed nibbles, as quant_pack8.
+template <bool CLAMP>
+__device__ __forceinline__ uint32_t quant_pack8h(const uint32_t* h, float m) {
+  float f[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = hlo(h[j]);
+    f[2 * j + 1] = hhi(h[j]);
+  }
+  return quant_pack8<CLAMP>(f, m);
+}
+
+// Rest of a k_hq_k28 row in fp16 (quantizer only): v holds the fp32 products
+// of H_112 (scaled by 2^-7) for the lane's four column tiles.
+template <bool CLAMP>
+__device__ __forceinline__ void k28_finish_f16(const float (&v)[4][28], int64_t row, int tid,
+                                               int lane, int w, int gc, float s0, float s1,
+                                               float s2, float s3, float sigma, float c,
+                                               float clip, float* s_x, float* s_red,
+                                               uint8_t* __restrict__ q,
+                                               uint16_t* __restrict__ scale,
+                                               float* __restrict__ zdbg) {
+  constexpr int D = 28672;
+  uint32_t hv[4][14];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int k = 0; k < 14; ++k) hv[ct][k] = pk_f16(v[ct][2 * k], v[ct][2 * k + 1]);
+  // H_4 over ct between registers
+#pragma unroll
+  for (int hb = 1; hb < 4; hb <<= 1)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      if (!(ct & hb))
+#pragma unroll
+        for (int k = 0; k < 14; ++k) {
+          const uint32_t a = hv[ct][k], b = hv[ct + hb][k];
+          hv[ct][k] = hadd2(a, b);
+          hv[ct + hb][k] = hsub2(a, b);
+        }
+  // H_16 over gmap(n) through DPP: 56 packed registers in 7 blocks of 8
+  auto pk_sign = [](float sv) { return sv < 0.0f ? 0xBC00BC00u : 0x3C003C00u; };
+  const uint32_t h0 = pk_sign(s0), h1 = pk_sign(s1), h2s = pk_sign(s2), h3 = pk_sign(s3);
+  uint32_t* hf = &hv[0][0];
+#pragma unroll
+  for (int b = 0; b < 56; b += 8) QR_DPP8H("quad_perm:[1,0,3,2]", (hf + b), h0);
+#pragma unroll
+  for (int b = 0; b < 56; b += 8) QR_DPP8H("quad_perm:[2,3,0,1]", (hf + b), h1);
+#pragma unroll
+  for (int b = 0; b < 56; b += 8) QR_DPP8H("row_half_mirror", (hf + b), h2s);
+#pragma unroll
+  for (int b = 0; b < 56; b += 8) QR_DPP8H("row_mirror", (hf + b), h3);
+  // H_4 over the wavefront index through LDS, two rounds of 7 packed positions
+  uint32_t* s_xu = (uint32_t*)s_x;
+  uint32_t o[4][14];
+#pragma unroll
+  for (int rnd = 0; rnd < 2; ++rnd) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int k = 0; k < 7; ++k) s_xu[((w * 4 + ct) * 7 + k) * 64 + lane] = hv[ct][7 * rnd + k];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 7; ++k) {
+      const uint32_t a0 = s_xu[((0 * 4 + w) * 7 + k) * 64 + lane];
+      const uint32_t a1 = s_xu[((1 * 4 + w) * 7 + k) * 64 + lane];
+      const uint32_t a2 = s_xu[((2 * 4 + w) * 7 + k) * 64 + lane];
+      const uint32_t a3 = s_xu[((3 * 4 + w) * 7 + k) * 64 + lane];
+      const uint32_t p01 = hadd2(a0, a1), m01 = hsub2(a0, a1);
+      const uint32_t p23 = hadd2(a2, a3), m23 = hsub2(a2, a3);
+      o[0][7 * rnd + k] = hadd2(p01, p23);
+      o[1][7 * rnd + k] = hadd2(m01, m23);
+      o[2][7 * rnd + k] = hsub2(p01, p23);
+      o[3][7 * rnd + k] = hsub2(m01, m23);
+    }
+    __syncthreads();
+  }
+  // o[w2][k] = sigma * z / 128 (fp16 pair) at chunk 4 ((4 w2 + w) 16 + gc) + g, positions 2k, 2k + 1
+  const int g = lane >> 4;
+  auto chunk_of = [&](int w2) { return 4 * ((4 * w2 + w) * 16 + gc) + g; };
+  if (zdbg) {
+    const float zs = 128.0f * sigma;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      float* zr = zdbg + row * D + chunk_of(w2) * 28;
+#pragma unroll
+      for (int k = 0; k < 14; k += 2)
+        *(v4f*)(zr + 2 * k) = v4f{hlo(o[w2][k]) * zs, hhi(o[w2][k]) * zs,
+                                  hlo(o[w2][k + 1]) * zs, hhi(o[w2][k + 1]) * zs};
+    }
+  }
+  uint32_t amh = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < 4; ++w2)
+#pragma unroll
+    for (int k = 0; k < 14; ++k) amh = hmax3abs(amh, o[w2][k]);
+  float am = wave_max(hlo(amh));
+  if (lane == 0) s_red[w] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  uint16_t sh;
+  float m;
+  // the fp16 stages carry z / 128: the same recipe with c * 128 (exact scaling)
+  sym_scale(am, c * 128.0f, clip, &sh, &m);
+  sh = (uint16_t)__builtin_amdgcn_readfirstlane(sh);
+  const float ml = m * sigma;
+  uint16_t* qrow = (uint16_t*)(q + row * (D / 2));
+  auto emit = [&](auto clamp_tag) {
+    constexpr bool CL = decltype(clamp_tag)::value;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      uint32_t words[4];
+#pragma unroll
+      for (int k8 = 0; k8 < 3; ++k8) words[k8] = quant_pack8h<CL>(&o[w2][4 * k8], ml);
+      const uint32_t tail[4] = {o[w2][12], o[w2][13], 0u, 0u};
+      words[3] = quant_pack8h<CL>(tail, ml);
+      uint16_t* qc = qrow + chunk_of(w2) * 7;  // 14 bytes of packed codes per chunk
+#pragma unroll
+      for (int k = 0; k < 7; ++k)
+        __builtin_nontemporal_store(
+            (uint16_t)((k & 1) ? (words[k >> 1] >> 16) : (words[k >> 1] & 0xffffu)), qc + k);
+    }
+  };
+  if (CLAMP || (sh & 0x7fffu) < 0x0400u)
+    emit(std::true_type{});
+  else
+    emit(std::false_type{});
+  if (tid == 0) scale[row] = sh;
+}
+
+template <int MODE, bool CLAMP, bool F16>
 __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uint16_t* __restrict__ x, int64_t T,
                                                    int64_t ld, const int8_t* __restrict__ signs,
                                                    float c, float clip, uint8_t* __restrict__ q,
@@ -737,8 +910,16 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
   // A fragments of H_112 = H_4 (x) H_28: tile mt row i -> output 28 (i >> 2) + 4 mt + (i & 3),
   // block kb lane (i, g) holds columns 32 kb + 8 g + j (zero past 112).
   // (reading them through the caches on every row instead was measured slower)
+  static_assert(!F16 || MODE == MODE_QUANT, "the fp16 transform is a quantizer variant");
   const v8h* afrag_g = (const v8h*)&g_h112_frags.v[0][0];
-  for (int f = tid; f < K28_AFRAG; f += 256) s_afrag[f] = afrag_g[f];
+  for (int f = tid; f < K28_AFRAG; f += 256) {
+    v4u a = __builtin_bit_cast(v4u, afrag_g[f]);
+    // fp16 transform: +-1 (0x3C00, 0xBC00) -> +-2^-7 (0x2000, 0xA000) by masking;
+    // the fp16 stages then carry z / 128, which keeps the first stage's sums
+    // of 112 fp16 inputs inside the fp16 range
+    if (F16) a &= 0xA000A000u;
+    s_afrag[f] = __builtin_bit_cast(v8h, a);
+  }
   const v8h* afrag = s_afrag;
   // Signs of the lane's B fragments (the same for every row), one dword per
   // fragment: bit 15 - j holds the sign of element 2 j, bit 31 - j that of
@@ -763,10 +944,10 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
   const float sigma = (__builtin_popcount(gc) & 1) ? -1.0f : 1.0f;  // lane holds sigma * z
   __syncthreads();
 
-  for (int64_t row = blockIdx.x; row < T; row += gridDim.x) {
-    const uint16_t* xr = x + row * ld;
-    // ---- B fragments: group G, elements 32 kb + 8 g .. + 7 (16 bytes) ----
-    v4u braw[4][4];
+  // ---- B fragments: group G, elements 32 kb + 8 g .. + 7 (16 bytes) ----
+  v4u braw[4][4];
+  auto load_b = [&](int64_t r) {
+    const uint16_t* xr = x + r * ld;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       const int G = (w * 4 + ct) * 16 + gc;
@@ -775,6 +956,9 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
         braw[ct][kb] = (kb < 3 || g < 2) ? ld_stream(xr + G * 112 + 32 * kb + 8 * g)
                                          : v4u{0u, 0u, 0u, 0u};
     }
+  };
+  for (int64_t row = blockIdx.x; row < T; row += gridDim.x) {
+    load_b(row);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       const v4u ev = s_sbits[(w * 4 + ct) * 64 + lane];
@@ -803,6 +987,11 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[ct][4 * mt + r] = accm[ct][r];
+    }
+    if constexpr (F16) {
+      k28_finish_f16<CLAMP>(v, row, tid, lane, w, gc, s0, s1, s2, s3, sigma, c, clip, s_x, s_red,
+                            q, scale, zdbg);
+      continue;
     }
     // ---- H_4 over ct: butterflies between registers (first, so that plain VALU
     //      ops and not the DPP asm consume the MFMA results) ----
@@ -1284,6 +1473,19 @@ static qr_status launch_lds_t(int d, int n, const uint16_t* x, int64_t T, int64_
   return launch_status();
 }
 
+#ifndef QR_K28_GRID
+#define QR_K28_GRID 512
+#endif
+template <int MODE, bool CLAMP, bool F16>
+static qr_status launch_k28(const uint16_t* x, int64_t T, int64_t ld, const int8_t* signs, float c,
+                            float clip, uint8_t* qq, uint16_t* ss, float* z, void* y,
+                            hipStream_t st) {
+  const int grid = grid_for(T, 1, QR_K28_GRID);
+  hipLaunchKernelGGL((k_hq_k28<MODE, CLAMP, F16>), dim3(grid), dim3(256), 0, st, x, T, ld, signs,
+                     c, clip, qq, ss, z, y);
+  return launch_status();
+}
+
 template <int MODE, bool CLAMP>
 static qr_status dispatch(const void* x_f16, int64_t T, int32_t d, int64_t ld, int rot,
                           const int8_t* signs, float clip, void* q, void* sc, float* z, void* y,
@@ -1301,15 +1503,7 @@ static qr_status dispatch(const void* x_f16, int64_t T, int32_t d, int64_t ld, i
       return launch_pow2<MODE, CLAMP>(d / 512, x, T, ld, signs, c, clip, qq, ss, z, y, st);
     return launch_small<MODE, CLAMP>(d, 1, x, T, ld, signs, c, clip, qq, ss, z, y, st);
   }
-  if (m == 28 && n == 10) {
-#ifndef QR_K28_GRID
-#define QR_K28_GRID 512
-#endif
-    const int grid = grid_for(T, 1, QR_K28_GRID);
-    hipLaunchKernelGGL((k_hq_k28<MODE, CLAMP>), dim3(grid), dim3(256), 0, st, x, T, ld, signs, c,
-                       clip, qq, ss, z, y);
-    return launch_status();
-  }
+  if (m == 28 && n == 10) return launch_k28<MODE, CLAMP, false>(x, T, ld, signs, c, clip, qq, ss, z, y, st);
   if (m == 28)
     return launch_lds_t<28, MODE, CLAMP, true>(d, n, x, T, ld, signs, c, clip, qq, ss, z, y, st);
   if (n == 6) {
@@ -1330,11 +1524,13 @@ extern "C" qr_status qr_hadamard_quant(const void* x_f16, int64_t T, int32_t d, 
                                        void* q_u8, void* scale_f16, float* z_dbg,
                                        hipStream_t stream) {
   if (T < 0 || d <= 0 || ld_x < d) return QR_ERR_SHAPE;
-  if (rot != QR_ROT_NONE && rot != QR_ROT_HADAMARD) return QR_ERR_ARG;
+  if (rot != QR_ROT_NONE && rot != QR_ROT_HADAMARD && rot != QR_ROT_HADAMARD_F16) return QR_ERR_ARG;
   if (!valid_clip(clip_ratio)) return QR_ERR_ARG;
   int n = 0, m = 0;
-  if (rot == QR_ROT_HADAMARD) {
+  if (rot != QR_ROT_NONE) {
     if (!factor_width(d, &n, &m)) return QR_ERR_UNSUPPORTED;
+    // the fp16 transform exists for the width of the 70B down projection
+    if (rot == QR_ROT_HADAMARD_F16 && !(m == 28 && n == 10)) return QR_ERR_UNSUPPORTED;
   } else if (d % 8 != 0 || d > 32768) {
     return QR_ERR_UNSUPPORTED;
   }
@@ -1343,6 +1539,15 @@ extern "C" qr_status qr_hadamard_quant(const void* x_f16, int64_t T, int32_t d, 
   if (ld_x % 8 != 0 || !aligned(x_f16, 16) || !aligned(q_u8, 4) || !aligned(scale_f16, 2) ||
       (z_dbg && !aligned(z_dbg, 16)) || (signs && !aligned(signs, 4)))
     return QR_ERR_ALIGN;
+  if (rot == QR_ROT_HADAMARD_F16) {
+    const float c = norm_constant(d);
+    const uint16_t* xx = (const uint16_t*)x_f16;
+    if (clip_ratio < 1.0f)
+      return launch_k28<MODE_QUANT, true, true>(xx, T, ld_x, signs, c, clip_ratio, (uint8_t*)q_u8,
+                                                (uint16_t*)scale_f16, z_dbg, nullptr, stream);
+    return launch_k28<MODE_QUANT, false, true>(xx, T, ld_x, signs, c, clip_ratio, (uint8_t*)q_u8,
+                                               (uint16_t*)scale_f16, z_dbg, nullptr, stream);
+  }
   const int r = rot == QR_ROT_HADAMARD ? 1 : 0;
   if (clip_ratio < 1.0f)
     return dispatch<MODE_QUANT, true>(x_f16, T, d, ld_x, r, signs, clip_ratio, q_u8, scale_f16,

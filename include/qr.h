@@ -63,8 +63,10 @@ typedef enum {
 } qr_status;
 
 typedef enum {
-  QR_ROT_NONE = 0,     /* quantize only */
-  QR_ROT_HADAMARD = 1  /* rotate by H_d diag(s) / sqrt(d), then quantize */
+  QR_ROT_NONE = 0,         /* quantize only */
+  QR_ROT_HADAMARD = 1,     /* rotate by H_d diag(s) / sqrt(d), then quantize */
+  QR_ROT_HADAMARD_F16 = 2  /* the same rotation with the transform's additions in fp16
+                              (qr_hadamard_quant only; d = 28672) */
 } qr_rot;
 
 /* Library ABI version (QR_ABI_VERSION of the build). */
@@ -100,6 +102,24 @@ qr_status qr_hadamard_factor(int32_t d, int32_t* log2_pow2, int32_t* m);
  *   m = c * (1 / s_h)  (m = 0 if s_h == 0);
  *   q_i = clamp(round_half_even(exact z_i * m), -8, 7).
  * The order of the fp32 additions inside z is not specified.
+ *
+ * QR_ROT_HADAMARD_F16 (QuaRot paper, appendix on the FP16 Hadamard
+ * transformation, Table 10: running the online transform in fp16 leaves
+ * accuracy unchanged).  Supported for d = 28672 = 1024 * 28 (the Llama-2-70B
+ * down projection); other widths return QR_ERR_UNSUPPORTED.  The dense
+ * H_4 (x) H_28 products of the fp16 inputs accumulate in fp32 as before; their
+ * conversion to fp16 and each of the 8 remaining butterfly stages round to
+ * fp16 (nearest even), on values scaled by 2^-7.  z_dbg returns that fp16
+ * result times 128, and the quantization is the recipe above applied to it,
+ * bit for bit.  Per row the 9 roundings bound the error as
+ *   ||z_dbg - z||_2 <= 9 * 2^-11 * ||z||_2 + 53 * 2^-18 * sqrt(d)
+ * (each rounding is relative 2^-11 of a vector whose norm the remaining
+ * stages, sqrt(2) times orthogonal each, carry to ||z||; the second term covers
+ * fp16 subnormals, whose absolute error of 2^-25 before the factor 128 the
+ * remaining stages grow by sqrt(2) each: sum over j = 0..8 of 2^(j/2) < 53).
+ * Rows whose |z| / 128
+ * exceeds the fp16 range (65504) overflow to an infinite scale: the mean |x|
+ * of a row must stay below about 290.
  *
  * Requirements: T >= 0; d supported; ld_x >= d and ld_x % 8 == 0; x_f16
  * 16-byte aligned; q_u8 and signs 4-byte aligned; z_dbg 16-byte aligned if

@@ -151,3 +151,60 @@ def test_determinism():
     b = run(x, s)
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
+
+
+# ---- QR_ROT_HADAMARD_F16 (the transform's additions in fp16, d = 28672) ----
+# Bound from the arithmetic (include/qr.h): 9 fp16 roundings, each relative
+# 2^-11 of a vector that the remaining scaled-orthogonal stages carry to ||z||,
+# plus the fp16 subnormal term (absolute 2^-25 before the factor 128, grown by
+# sqrt(2) per remaining stage); the quantization of the returned values is the
+# fp32 recipe, bit for bit.
+F16_D = 28672
+
+
+def f16_bound(z64):
+    return 9 * 2.0 ** -11 * np.linalg.norm(z64, axis=-1) + 53 * 2.0 ** -18 * np.sqrt(F16_D)
+
+
+def run_f16(x, s, clip=1.0):
+    q, sc, z = qr.hadamard_quant(dev(x), dev(s) if s is not None else None, clip, z_dbg=True,
+                                 fp16_transform=True)
+    return host(q), host(sc), host(z)
+
+
+@pytest.mark.parametrize("clip", [1.0, 0.9])
+def test_fp16_transform_bound_and_recipe(clip):
+    T = 37
+    x = wl.activations(11, 0, T, F16_D, n_outliers=4, lo=50, hi=50)
+    s = wl.signs(11, F16_D)
+    q, sc, z = run_f16(x, s, clip)
+    # the quantizer input is 128 times fp16 values
+    assert np.array_equal((z / 128).astype(np.float16).astype(np.float32) * 128, z)
+    z64 = oh.rotate_unnormalised(x.astype(np.float64), s)
+    err = np.linalg.norm(z.astype(np.float64) - z64, axis=-1)
+    assert (err <= f16_bound(z64)).all(), f"max err/bound {(err / f16_bound(z64)).max():.3f}"
+    check_sym_exact(q, sc, z.astype(np.float64), F16_D, True, clip)
+    # the codes agree with the fp32 transform's except near rounding ties
+    q32, sc32, z32 = run(x, s, clip)
+    assert (oq.unpack_int4(q).astype(np.int64) != oq.unpack_int4(q32)).mean() < 0.05
+
+
+def test_fp16_transform_edge_rows():
+    s = wl.signs(12, F16_D)
+    x = np.zeros((5, F16_D), dtype=np.float16)
+    x[1] = 1.0                                   # constant row
+    x[2, F16_D // 3] = 3.0                       # one spike
+    x[3] = wl.activations(12, 1, 1, F16_D)[0]
+    x[4] = (wl.activations(12, 2, 1, F16_D)[0].astype(np.float64) * 2.0 ** -12).astype(np.float16)
+    q, sc, z = run_f16(x, None)
+    z64 = oh.rotate_unnormalised(x.astype(np.float64), None)
+    err = np.linalg.norm(z.astype(np.float64) - z64, axis=-1)
+    assert (err <= f16_bound(z64)).all()
+    check_sym_exact(q, sc, z.astype(np.float64), F16_D, True, 1.0)
+    assert sc[0] == 0 and not q[0].any()
+
+
+def test_fp16_transform_other_widths_unsupported():
+    x = dev(wl.activations(13, 0, 2, 4096))
+    with pytest.raises(RuntimeError):
+        qr.hadamard_quant(x, None, 1.0, fp16_transform=True)
