@@ -14,8 +14,8 @@ One step is one pass of the whole hot path over one batch of synthetic input
   gate, up, down) with the scale epilogue; head-wise Hadamard + asymmetric
   4-bit group-128 quantization of K and V into the cache (Init of the prompt);
   the head-wise rotation of Q.  With --fp16-hadamard the down-projection
-  rotation (d = 28672) runs the fp16 variant of the transform
-  (QR_ROT_HADAMARD_F16) instead of the default fp32 one.
+  rotation (d = 28672, or 11008 for 7b_prefill) runs the fp16 variant of the
+  transform (QR_ROT_HADAMARD_F16) instead of the default fp32 one.
 * 7b_decode: the same four rotations and five GEMMs at T = 1, 8, 32 and 64.
 * 70b_kv: K/V Init of a 32 x 2048-token prompt (8 KV heads of 128), the
   rotation of its queries (64 heads), then 50 decode steps of Append K, V,
@@ -69,7 +69,7 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--fp16-hadamard", action="store_true",
-                    help="70B down-projection rotation with the fp16 transform")
+                    help="down-projection rotation with the fp16 transform")
     return ap.parse_args()
 
 
@@ -134,7 +134,7 @@ def make_block(torch, qr, wl, W, T, dev, with_kv, f16_down=False):
     L = []
     tag = f"T{T}:" if not with_kv else ""
     for name, x in inputs.items():
-        f16 = f16_down and name == "down_in" and x.shape[1] == 28672
+        f16 = f16_down and name == "down_in" and x.shape[1] in (28672, 11008)
         L.append(("hadamard_quant", tag + name + (":fp16" if f16 else ""), hq_bytes(T, x.shape[1]), 0,
                   (lambda x=x, name=name, f16=f16: qr.hadamard_quant(
                       x, signs[x.shape[1]], 1.0, out=qbuf[name], fp16_transform=f16)), qbuf[name]))
@@ -381,8 +381,8 @@ def main():
             "workload": f"{W.name}: T={T} tokens, hidden {W.hidden}, FFN {lin['down'].k}, QKV "
                         f"{lin['qkv'].n}; 4 fused rotate+quant, 5 W4A4 GEMMs, {kvdesc}",
             "tokens": T, "hidden": W.hidden, "ffn": lin["down"].k,
-            "hadamard_arithmetic": ("fp16 for d = 28672, fp32 otherwise"
-                                    if args.fp16_hadamard and lin["down"].k == 28672 else "fp32")})
+            "hadamard_arithmetic": (f"fp16 for d = {lin['down'].k}, fp32 otherwise"
+                                    if args.fp16_hadamard else "fp32")})
         dominant, bound = "w4a4_gemm", "mfma"
     elif wname == "7b_decode":
         launches = []

@@ -139,7 +139,7 @@ def hadamard_quant(x, signs=None, clip_ratio: float = 1.0, rotate: bool = True,
 
     Returns (q uint8 [T, d/2], scale fp16 [T]) and, with z_dbg, z fp32 [T, d].
     ``out`` may pass preallocated (q, scale) tensors.  ``fp16_transform`` selects
-    QR_ROT_HADAMARD_F16 (the transform's additions in fp16; d = 28672 only).
+    QR_ROT_HADAMARD_F16 (the transform's additions in fp16; d = 28672 and 11008).
     """
     torch = _torch()
     _need(x, torch.float16, "x", 2)

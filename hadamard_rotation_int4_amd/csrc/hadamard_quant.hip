@@ -1169,7 +1169,7 @@ constexpr int K172_AFRAG = 11 * 6 * 64;  // A fragments [mt][kb][lane], 8 fp16 e
 struct H172Frags {
   uint16_t v[K172_AFRAG][8];
 };
-constexpr H172Frags make_h172_frags() {
+constexpr H172Frags make_h172_frags(uint16_t one, uint16_t minus_one) {
   H172Frags f{};
   const HTable<172> h = make_h172();
   for (int idx = 0; idx < K172_AFRAG; ++idx) {
@@ -1179,15 +1179,18 @@ constexpr H172Frags make_h172_frags() {
     for (int j = 0; j < 8; ++j) {
       const int col = 32 * kb + 8 * gg + j;
       uint16_t bits = 0;
-      if (o < 172 && col < 172) bits = h.v[o][col] > 0.0f ? 0x3C00u : 0xBC00u;
+      if (o < 172 && col < 172) bits = h.v[o][col] > 0.0f ? one : minus_one;
       f.v[idx][j] = bits;
     }
   }
   return f;
 }
-__device__ const H172Frags g_h172_frags = make_h172_frags();
+__device__ const H172Frags g_h172_frags = make_h172_frags(0x3C00u, 0xBC00u);
+// +-2^-8 for the fp16 transform: the fp16 stages carry z / 256, which keeps
+// the first stage's sums of 172 fp16 inputs inside the fp16 range
+__device__ const H172Frags g_h172_frags16 = make_h172_frags(0x1C00u, 0x9C00u);
 
-template <int MODE, bool CLAMP>
+template <int MODE, bool CLAMP, bool F16>
 __global__ __launch_bounds__(256, 2) void k_hq_k172(const uint16_t* __restrict__ x, int64_t T,
                                                     int64_t ld, const int8_t* __restrict__ signs,
                                                     float c, float clip, uint8_t* __restrict__ q,
@@ -1203,7 +1206,9 @@ __global__ __launch_bounds__(256, 2) void k_hq_k172(const uint16_t* __restrict__
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int gc = gmap(n);
-  const v8h* afrag = (const v8h*)&g_h172_frags.v[0][0];  // read through the caches each row
+  static_assert(!F16 || MODE == MODE_QUANT, "the fp16 transform is a quantizer variant");
+  // read through the caches each row
+  const v8h* afrag = (const v8h*)&(F16 ? g_h172_frags16 : g_h172_frags).v[0][0];
 
   // Sign words of the B fragments, as in k_hq_k28: bit 15 - j / 31 - j hold the
   // signs of elements 2 j / 2 j + 1 of the fragment.
@@ -1274,6 +1279,89 @@ __global__ __launch_bounds__(256, 2) void k_hq_k172(const uint16_t* __restrict__
           for (int r = 0; r < 4; ++r) v[t][ct][r] = 0.0f;
       }
     }
+    // element index of v[t][ct][0]: chunk 16 ct + gc, position 16 (w + 4 t) + 4 g
+    auto elem_of = [&](int t, int ct) { return (16 * ct + gc) * 172 + 16 * (w + 4 * t) + 4 * g; };
+    auto valid = [&](int t) { return t < nmt && 16 * (w + 4 * t) + 4 * g < 172; };
+    if constexpr (F16) {
+      // fp16 transform (QR_ROT_HADAMARD_F16): the remaining six stages on
+      // packed fp16 pairs, as in k28_finish_f16
+      uint32_t hv[3][4][2];
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          hv[t][ct][0] = pk_f16(v[t][ct][0], v[t][ct][1]);
+          hv[t][ct][1] = pk_f16(v[t][ct][2], v[t][ct][3]);
+        }
+#pragma unroll
+      for (int hb = 1; hb < 4; hb <<= 1)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          if (!(ct & hb))
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+#pragma unroll
+              for (int j = 0; j < 2; ++j) {
+                const uint32_t p = hv[t][ct][j], m = hv[t][ct + hb][j];
+                hv[t][ct][j] = hadd2(p, m);
+                hv[t][ct + hb][j] = hsub2(p, m);
+              }
+      auto pk_sign = [](float sv) { return sv < 0.0f ? 0xBC00BC00u : 0x3C003C00u; };
+      const uint32_t h0 = pk_sign(s0), h1 = pk_sign(s1), h2s = pk_sign(s2), h3 = pk_sign(s3);
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        uint32_t* r8 = &hv[t][0][0];
+        QR_DPP8H("quad_perm:[1,0,3,2]", r8, h0);
+        QR_DPP8H("quad_perm:[2,3,0,1]", r8, h1);
+        QR_DPP8H("row_half_mirror", r8, h2s);
+        QR_DPP8H("row_mirror", r8, h3);
+      }
+      if (zdbg) {
+        const float zs = 256.0f * sigma;
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+          if (valid(t))
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+              *(v4f*)(zdbg + row * D + elem_of(t, ct)) =
+                  v4f{hlo(hv[t][ct][0]) * zs, hhi(hv[t][ct][0]) * zs, hlo(hv[t][ct][1]) * zs,
+                      hhi(hv[t][ct][1]) * zs};
+      }
+      uint32_t amh = 0;
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) amh = hmax3abs(amh, hv[t][ct][j]);
+      float am = wave_max(hlo(amh));
+      if (lane == 0) s_red[w] = am;
+      __syncthreads();
+      am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+      uint16_t sh;
+      float m;
+      sym_scale(am, c * 256.0f, clip, &sh, &m);  // the stages carry z / 256
+      sh = (uint16_t)__builtin_amdgcn_readfirstlane(sh);
+      const float ml = m * sigma;
+      const bool clamp = CLAMP || (sh & 0x7fffu) < 0x0400u;  // block-uniform
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        if (valid(t))
+#pragma unroll
+          for (int ct = 0; ct < 4; ct += 2) {
+            const uint32_t h4[4] = {hv[t][ct][0], hv[t][ct][1], hv[t][ct + 1][0], hv[t][ct + 1][1]};
+            const uint32_t word = clamp ? quant_pack8h<true>(h4, ml) : quant_pack8h<false>(h4, ml);
+            s_stage[elem_of(t, ct) / 4] = (uint16_t)(word & 0xffffu);
+            s_stage[elem_of(t, ct + 1) / 4] = (uint16_t)(word >> 16);
+          }
+      __syncthreads();
+      const uint32_t* st32 = (const uint32_t*)s_stage;
+      uint32_t* qr32 = (uint32_t*)(q + row * (D / 2));
+      for (int i = tid; i < D / 8; i += 256) st_stream(qr32 + i, st32[i]);
+      if (tid == 0) scale[row] = sh;
+      __syncthreads();  // stage and s_red are reused by the next row
+      continue;
+    }
     // ---- H_4 over ct between registers (plain VALU consumes the MFMA results) ----
 #pragma unroll
     for (int hb = 1; hb < 4; hb <<= 1)
@@ -1309,10 +1397,6 @@ __global__ __launch_bounds__(256, 2) void k_hq_k172(const uint16_t* __restrict__
           v[t][c2 + 1][r] = r8[4 + r];
         }
       }
-    // element index of v[t][ct][0]: chunk 16 ct + gc, position 16 (w + 4 t) + 4 g
-    auto elem_of = [&](int t, int ct) { return (16 * ct + gc) * 172 + 16 * (w + 4 * t) + 4 * g; };
-    auto valid = [&](int t) { return t < nmt && 16 * (w + 4 * t) + 4 * g < 172; };
-
     if (zdbg) {
 #pragma unroll
       for (int t = 0; t < 3; ++t)
@@ -1486,6 +1570,16 @@ static qr_status launch_k28(const uint16_t* x, int64_t T, int64_t ld, const int8
   return launch_status();
 }
 
+template <int MODE, bool CLAMP, bool F16>
+static qr_status launch_k172(const uint16_t* x, int64_t T, int64_t ld, const int8_t* signs,
+                             float c, float clip, uint8_t* qq, uint16_t* ss, float* z, void* y,
+                             hipStream_t st) {
+  const int grid = grid_for(T, 1, 512);
+  hipLaunchKernelGGL((k_hq_k172<MODE, CLAMP, F16>), dim3(grid), dim3(256), 0, st, x, T, ld,
+                     signs, c, clip, qq, ss, z, y);
+  return launch_status();
+}
+
 template <int MODE, bool CLAMP>
 static qr_status dispatch(const void* x_f16, int64_t T, int32_t d, int64_t ld, int rot,
                           const int8_t* signs, float clip, void* q, void* sc, float* z, void* y,
@@ -1506,12 +1600,7 @@ static qr_status dispatch(const void* x_f16, int64_t T, int32_t d, int64_t ld, i
   if (m == 28 && n == 10) return launch_k28<MODE, CLAMP, false>(x, T, ld, signs, c, clip, qq, ss, z, y, st);
   if (m == 28)
     return launch_lds_t<28, MODE, CLAMP, true>(d, n, x, T, ld, signs, c, clip, qq, ss, z, y, st);
-  if (n == 6) {
-    auto kern = k_hq_k172<MODE, CLAMP>;
-    const int grid = grid_for(T, 1, 512);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, x, T, ld, signs, c, clip, qq, ss, z, y);
-    return launch_status();
-  }
+  if (n == 6) return launch_k172<MODE, CLAMP, false>(x, T, ld, signs, c, clip, qq, ss, z, y, st);
   return launch_lds_t<172, MODE, CLAMP, true>(d, n, x, T, ld, signs, c, clip, qq, ss, z, y, st);
 }
 
@@ -1529,8 +1618,9 @@ extern "C" qr_status qr_hadamard_quant(const void* x_f16, int64_t T, int32_t d, 
   int n = 0, m = 0;
   if (rot != QR_ROT_NONE) {
     if (!factor_width(d, &n, &m)) return QR_ERR_UNSUPPORTED;
-    // the fp16 transform exists for the width of the 70B down projection
-    if (rot == QR_ROT_HADAMARD_F16 && !(m == 28 && n == 10)) return QR_ERR_UNSUPPORTED;
+    // the fp16 transform exists for the down-projection widths of the configurations
+    if (rot == QR_ROT_HADAMARD_F16 && !((m == 28 && n == 10) || (m == 172 && n == 6)))
+      return QR_ERR_UNSUPPORTED;
   } else if (d % 8 != 0 || d > 32768) {
     return QR_ERR_UNSUPPORTED;
   }
@@ -1542,11 +1632,19 @@ extern "C" qr_status qr_hadamard_quant(const void* x_f16, int64_t T, int32_t d, 
   if (rot == QR_ROT_HADAMARD_F16) {
     const float c = norm_constant(d);
     const uint16_t* xx = (const uint16_t*)x_f16;
-    if (clip_ratio < 1.0f)
-      return launch_k28<MODE_QUANT, true, true>(xx, T, ld_x, signs, c, clip_ratio, (uint8_t*)q_u8,
-                                                (uint16_t*)scale_f16, z_dbg, nullptr, stream);
-    return launch_k28<MODE_QUANT, false, true>(xx, T, ld_x, signs, c, clip_ratio, (uint8_t*)q_u8,
-                                               (uint16_t*)scale_f16, z_dbg, nullptr, stream);
+    uint8_t* qq = (uint8_t*)q_u8;
+    uint16_t* ss = (uint16_t*)scale_f16;
+    if (m == 28)
+      return clip_ratio < 1.0f
+                 ? launch_k28<MODE_QUANT, true, true>(xx, T, ld_x, signs, c, clip_ratio, qq, ss,
+                                                      z_dbg, nullptr, stream)
+                 : launch_k28<MODE_QUANT, false, true>(xx, T, ld_x, signs, c, clip_ratio, qq, ss,
+                                                       z_dbg, nullptr, stream);
+    return clip_ratio < 1.0f
+               ? launch_k172<MODE_QUANT, true, true>(xx, T, ld_x, signs, c, clip_ratio, qq, ss,
+                                                     z_dbg, nullptr, stream)
+               : launch_k172<MODE_QUANT, false, true>(xx, T, ld_x, signs, c, clip_ratio, qq, ss,
+                                                      z_dbg, nullptr, stream);
   }
   const int r = rot == QR_ROT_HADAMARD ? 1 : 0;
   if (clip_ratio < 1.0f)

@@ -66,7 +66,7 @@ typedef enum {
   QR_ROT_NONE = 0,         /* quantize only */
   QR_ROT_HADAMARD = 1,     /* rotate by H_d diag(s) / sqrt(d), then quantize */
   QR_ROT_HADAMARD_F16 = 2  /* the same rotation with the transform's additions in fp16
-                              (qr_hadamard_quant only; d = 28672) */
+                              (qr_hadamard_quant only; d = 28672 and 11008) */
 } qr_rot;
 
 /* Library ABI version (QR_ABI_VERSION of the build). */
@@ -105,21 +105,24 @@ qr_status qr_hadamard_factor(int32_t d, int32_t* log2_pow2, int32_t* m);
  *
  * QR_ROT_HADAMARD_F16 (QuaRot paper, appendix on the FP16 Hadamard
  * transformation, Table 10: running the online transform in fp16 leaves
- * accuracy unchanged).  Supported for d = 28672 = 1024 * 28 (the Llama-2-70B
- * down projection); other widths return QR_ERR_UNSUPPORTED.  The dense
- * H_4 (x) H_28 products of the fp16 inputs accumulate in fp32 as before; their
- * conversion to fp16 and each of the 8 remaining butterfly stages round to
- * fp16 (nearest even), on values scaled by 2^-7.  z_dbg returns that fp16
- * result times 128, and the quantization is the recipe above applied to it,
- * bit for bit.  Per row the 9 roundings bound the error as
- *   ||z_dbg - z||_2 <= 9 * 2^-11 * ||z||_2 + 53 * 2^-18 * sqrt(d)
- * (each rounding is relative 2^-11 of a vector whose norm the remaining
- * stages, sqrt(2) times orthogonal each, carry to ||z||; the second term covers
- * fp16 subnormals, whose absolute error of 2^-25 before the factor 128 the
- * remaining stages grow by sqrt(2) each: sum over j = 0..8 of 2^(j/2) < 53).
- * Rows whose |z| / 128
- * exceeds the fp16 range (65504) overflow to an infinite scale: the mean |x|
- * of a row must stay below about 290.
+ * accuracy unchanged).  Supported for the down-projection widths
+ * d = 28672 = 1024 * 28 (Llama-2-70B) and d = 11008 = 64 * 172 (Llama-2-7B);
+ * other widths return QR_ERR_UNSUPPORTED.  The dense H_m products (H_4 (x)
+ * H_28 for 28672, H_172 for 11008) of the fp16 inputs accumulate in fp32 as
+ * before; their conversion to fp16 and each remaining butterfly stage (8 for
+ * 28672, 6 for 11008) round to fp16 (nearest even), on values scaled by 2^-e
+ * (e = 7 for 28672, 8 for 11008, so that the dense stage's sums stay in the
+ * fp16 range).  z_dbg returns that fp16 result times 2^e, and the
+ * quantization is the recipe above applied to it, bit for bit.  With R
+ * roundings (9 for 28672, 7 for 11008) the error per row obeys
+ *   ||z_dbg - z||_2 <= R * 2^-11 * ||z||_2 + 2^(e-25) * S * sqrt(d),
+ *   S = sum over j = 0 .. R-1 of 2^(j/2)  (S < 53 for R = 9, < 25 for R = 7):
+ * each rounding is relative 2^-11 of a vector whose norm the remaining
+ * stages, sqrt(2) times orthogonal each, carry to ||z||; the second term
+ * covers fp16 subnormals (absolute error 2^-25 before the factor 2^e, grown
+ * by sqrt(2) per remaining stage).  Rows whose |z| / 2^e exceeds the fp16
+ * range (65504) overflow to an infinite scale: the mean |x| of a row must
+ * stay below about 290 (28672) or 1500 (11008).
  *
  * Requirements: T >= 0; d supported; ld_x >= d and ld_x % 8 == 0; x_f16
  * 16-byte aligned; q_u8 and signs 4-byte aligned; z_dbg 16-byte aligned if

@@ -84,9 +84,10 @@ def test_hadamard_quant_validation(lib):
     assert hq(lib, d=43, ld=48) == QR_ERR_UNSUPPORTED
     assert hq(lib, rot=7) == QR_ERR_ARG
     assert hq(lib, rot=3) == QR_ERR_ARG
-    assert hq(lib, rot=2) == QR_ERR_UNSUPPORTED        # fp16 transform: d = 28672 only
+    assert hq(lib, rot=2) == QR_ERR_UNSUPPORTED        # fp16 transform: d = 28672, 11008
     assert hq(lib, T=0, d=28672, ld=28672, rot=2) == QR_OK
-    assert hq(lib, T=0, d=11008, ld=11008, rot=2) == QR_ERR_UNSUPPORTED
+    assert hq(lib, T=0, d=11008, ld=11008, rot=2) == QR_OK
+    assert hq(lib, T=0, d=5504, ld=5504, rot=2) == QR_ERR_UNSUPPORTED
     assert hq(lib, clip=0.0) == QR_ERR_ARG
     assert hq(lib, clip=1.5) == QR_ERR_ARG
     assert hq(lib, clip=1e-4) == QR_ERR_ARG

@@ -153,17 +153,19 @@ def test_determinism():
         assert np.array_equal(u, v)
 
 
-# ---- QR_ROT_HADAMARD_F16 (the transform's additions in fp16, d = 28672) ----
-# Bound from the arithmetic (include/qr.h): 9 fp16 roundings, each relative
+# ---- QR_ROT_HADAMARD_F16 (the transform's additions in fp16, d = 28672, 11008) ----
+# Bound from the arithmetic (include/qr.h): R fp16 roundings, each relative
 # 2^-11 of a vector that the remaining scaled-orthogonal stages carry to ||z||,
-# plus the fp16 subnormal term (absolute 2^-25 before the factor 128, grown by
+# plus the fp16 subnormal term (absolute 2^-25 before the factor 2^e, grown by
 # sqrt(2) per remaining stage); the quantization of the returned values is the
 # fp32 recipe, bit for bit.
-F16_D = 28672
+F16_WIDTHS = {28672: (9, 7), 11008: (7, 8)}   # d -> (roundings R, scaling exponent e)
 
 
-def f16_bound(z64):
-    return 9 * 2.0 ** -11 * np.linalg.norm(z64, axis=-1) + 53 * 2.0 ** -18 * np.sqrt(F16_D)
+def f16_bound(z64, d):
+    R, e = F16_WIDTHS[d]
+    S = sum(2.0 ** (j / 2) for j in range(R))
+    return R * 2.0 ** -11 * np.linalg.norm(z64, axis=-1) + 2.0 ** (e - 25) * S * np.sqrt(d)
 
 
 def run_f16(x, s, clip=1.0):
@@ -172,35 +174,38 @@ def run_f16(x, s, clip=1.0):
     return host(q), host(sc), host(z)
 
 
+@pytest.mark.parametrize("d", sorted(F16_WIDTHS))
 @pytest.mark.parametrize("clip", [1.0, 0.9])
-def test_fp16_transform_bound_and_recipe(clip):
+def test_fp16_transform_bound_and_recipe(d, clip):
     T = 37
-    x = wl.activations(11, 0, T, F16_D, n_outliers=4, lo=50, hi=50)
-    s = wl.signs(11, F16_D)
+    x = wl.activations(11, 0, T, d, n_outliers=4, lo=50, hi=50)
+    s = wl.signs(11, d)
     q, sc, z = run_f16(x, s, clip)
-    # the quantizer input is 128 times fp16 values
-    assert np.array_equal((z / 128).astype(np.float16).astype(np.float32) * 128, z)
+    # the quantizer input is 2^e times fp16 values
+    f = 2.0 ** F16_WIDTHS[d][1]
+    assert np.array_equal((z / f).astype(np.float16).astype(np.float32) * f, z)
     z64 = oh.rotate_unnormalised(x.astype(np.float64), s)
     err = np.linalg.norm(z.astype(np.float64) - z64, axis=-1)
-    assert (err <= f16_bound(z64)).all(), f"max err/bound {(err / f16_bound(z64)).max():.3f}"
-    check_sym_exact(q, sc, z.astype(np.float64), F16_D, True, clip)
+    bound = f16_bound(z64, d)
+    assert (err <= bound).all(), f"max err/bound {(err / bound).max():.3f}"
+    check_sym_exact(q, sc, z.astype(np.float64), d, True, clip)
     # the codes agree with the fp32 transform's except near rounding ties
     q32, sc32, z32 = run(x, s, clip)
     assert (oq.unpack_int4(q).astype(np.int64) != oq.unpack_int4(q32)).mean() < 0.05
 
 
-def test_fp16_transform_edge_rows():
-    s = wl.signs(12, F16_D)
-    x = np.zeros((5, F16_D), dtype=np.float16)
+@pytest.mark.parametrize("d", sorted(F16_WIDTHS))
+def test_fp16_transform_edge_rows(d):
+    x = np.zeros((5, d), dtype=np.float16)
     x[1] = 1.0                                   # constant row
-    x[2, F16_D // 3] = 3.0                       # one spike
-    x[3] = wl.activations(12, 1, 1, F16_D)[0]
-    x[4] = (wl.activations(12, 2, 1, F16_D)[0].astype(np.float64) * 2.0 ** -12).astype(np.float16)
+    x[2, d // 3] = 3.0                           # one spike
+    x[3] = wl.activations(12, 1, 1, d)[0]
+    x[4] = (wl.activations(12, 2, 1, d)[0].astype(np.float64) * 2.0 ** -12).astype(np.float16)
     q, sc, z = run_f16(x, None)
     z64 = oh.rotate_unnormalised(x.astype(np.float64), None)
     err = np.linalg.norm(z.astype(np.float64) - z64, axis=-1)
-    assert (err <= f16_bound(z64)).all()
-    check_sym_exact(q, sc, z.astype(np.float64), F16_D, True, 1.0)
+    assert (err <= f16_bound(z64, d)).all()
+    check_sym_exact(q, sc, z.astype(np.float64), d, True, 1.0)
     assert sc[0] == 0 and not q[0].any()
 
 
