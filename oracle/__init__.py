@@ -29,6 +29,10 @@ LLMs Impossible"):
   sequence over the dequantized 4-bit cache, with grouped-query heads (QuaRot
   paper, attention paragraph and its attention routines: Init, Append,
   Decode).
+* ``block``: the block's other online steps: RMSNorm without its scale in
+  front of the QKV/gate/up quantizer, and the Hadamard-heads transform
+  Z (H_{n_h} (x) I) in front of the O projection's quantizer (QuaRot paper,
+  method section and the attention-block paragraph with Figure 6).
 
 Two modes exist where floating point is involved.  "Math" functions work in
 float64 throughout.  "Recipe" functions follow the fp32 step sequence that the

@@ -109,7 +109,17 @@ def sym_quant_recipe(z: np.ndarray, d: int, rotated: bool, clip: float = 1.0
             to an integer directly from its exact value.
     """
     z32 = np.asarray(z, dtype=F32)
-    c = norm_constant(d, rotated)
+    c = np.full(z32.shape[:-1], norm_constant(d, rotated), dtype=F32)
+    return sym_quant_recipe_rows(z32, c, clip)
+
+
+def sym_quant_recipe_rows(z: np.ndarray, c: np.ndarray, clip: float = 1.0
+                          ) -> tuple[np.ndarray, np.ndarray]:
+    """The recipe of sym_quant_recipe() with one fp32 constant c per row: the
+    quantizer input is y = z * c, with z the exact fp32 row (the transform
+    output, or the input itself) and c its normalisation."""
+    z32 = np.asarray(z, dtype=F32)
+    c = np.asarray(c, dtype=F32)
     clip32 = F32(clip)
     az = np.abs(z32).max(axis=-1)
     a = (az * c).astype(F32)
