@@ -13,6 +13,8 @@ Functions (same names as the C entry points without the ``qr_`` prefix):
   w4a4_gemm(a_q, a_scale, w_q, w_scale, acc_dbg=False) -> y_f16[, acc_i32]
   kv_rotate_quant(kv, signs, group, clip_ratio, cache_q, cache_meta, start_pos,
                   rotate=True, z_dbg=False) -> None[, z]
+  rmsnorm_quant(x, eps, clip_ratio, r_dbg=False) -> (q_u8, scale_f16[, r])
+  hadamard_heads_quant(x, n_heads, clip_ratio, z_dbg=False) -> (q_u8, scale_f16[, z])
   hadamard_factor(d) -> (n, m);  abi_version();  status_str(code)
 """
 from __future__ import annotations
@@ -56,6 +58,10 @@ def _load():
     lib.qr_kv_rotate_quant.restype = ctypes.c_int
     lib.qr_kv_rotate_quant.argtypes = [vp, i32, i32, i32, i32, i64, ctypes.c_int, vp, i32, f32,
                                        vp, vp, i32, i32, vp, vp]
+    lib.qr_rmsnorm_quant.restype = ctypes.c_int
+    lib.qr_rmsnorm_quant.argtypes = [vp, i64, i32, i64, f32, f32, vp, vp, vp, vp]
+    lib.qr_hadamard_heads_quant.restype = ctypes.c_int
+    lib.qr_hadamard_heads_quant.argtypes = [vp, i64, i32, i32, i64, f32, vp, vp, vp, vp]
     lib.qr_kv_decode_workspace_bytes.restype = i64
     lib.qr_kv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.qr_kv_decode_attention.restype = ctypes.c_int
@@ -162,6 +168,60 @@ def hadamard_quant(x, signs=None, clip_ratio: float = 1.0, rotate: bool = True,
                                      if rotate else QR_ROT_NONE, _ptr(s),
                                      float(clip_ratio), _ptr(q), _ptr(sc), _ptr(z), _stream(stream))
     _check(code, "qr_hadamard_quant")
+    return (q, sc, z) if z_dbg else (q, sc)
+
+
+def _quant_out(out, T, d, device):
+    torch = _torch()
+    if out is None:
+        return (torch.empty((T, d // 2), dtype=torch.uint8, device=device),
+                torch.empty((T,), dtype=torch.float16, device=device))
+    q, sc = out
+    _need(q, torch.uint8, "q")
+    _need(sc, torch.float16, "scale")
+    if q.numel() != T * (d // 2) or not q.is_contiguous() or sc.numel() != T:
+        raise ValueError("out tensors have the wrong size or layout")
+    return q, sc
+
+
+def rmsnorm_quant(x, eps: float = 1e-5, clip_ratio: float = 1.0, r_dbg: bool = False,
+                  out=None, stream=None):
+    """RMSNorm without scale (fp32) + per-token INT4 of the rows of x [T, d] (fp16).
+
+    Returns (q uint8 [T, d/2], scale fp16 [T]) and, with r_dbg, the fp32
+    multiplier r = 1/sqrt(mean(x^2) + eps) per row."""
+    torch = _torch()
+    _need(x, torch.float16, "x", 2)
+    if x.numel() and x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous (stride(1) == 1)")
+    T, d = x.shape
+    q, sc = _quant_out(out, T, d, x.device)
+    r = torch.empty((T,), dtype=torch.float32, device=x.device) if r_dbg else None
+    code = _load().qr_rmsnorm_quant(_ptr(x), T, d, x.stride(0) if T > 0 else d, float(eps),
+                                    float(clip_ratio), _ptr(q), _ptr(sc), _ptr(r), _stream(stream))
+    _check(code, "qr_rmsnorm_quant")
+    return (q, sc, r) if r_dbg else (q, sc)
+
+
+def hadamard_heads_quant(x, n_heads: int, clip_ratio: float = 1.0, z_dbg: bool = False,
+                         out=None, stream=None):
+    """Hadamard heads (H_nh (x) I) / sqrt(nh) + per-token INT4 of the rows of x [T, nh*dh].
+
+    Returns (q uint8 [T, d/2], scale fp16 [T]) and, with z_dbg, z fp32 [T, d]
+    (the transform before 1/sqrt(nh))."""
+    torch = _torch()
+    _need(x, torch.float16, "x", 2)
+    if x.numel() and x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous (stride(1) == 1)")
+    T, d = x.shape
+    if n_heads <= 0 or d % n_heads:
+        raise ValueError(f"row width {d} is not a multiple of n_heads={n_heads}")
+    q, sc = _quant_out(out, T, d, x.device)
+    z = torch.empty((T, d), dtype=torch.float32, device=x.device) if z_dbg else None
+    code = _load().qr_hadamard_heads_quant(_ptr(x), T, int(n_heads), d // int(n_heads),
+                                           x.stride(0) if T > 0 else d, float(clip_ratio),
+                                           _ptr(q), _ptr(sc), _ptr(z), _stream(stream))
+    _check(code, "qr_hadamard_heads_quant")
     return (q, sc, z) if z_dbg else (q, sc)
 
 

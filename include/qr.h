@@ -18,7 +18,11 @@
  *     paragraph, implementation paragraph, attention-routines paragraph;
  *   - the Decode routine, flash-style attention of the FP16 query over the
  *     dequantized cache: QuaRot paper, attention paragraph and attention
- *     routines.
+ *     routines;
+ *   - RMSNorm without scale in fp32 before the QKV/gate/up quantizer, and the
+ *     Hadamard-heads block before the O projection's quantizer: QuaRot paper,
+ *     method section, activation-quantization paragraph, attention-block
+ *     paragraph (Figure 6).
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
@@ -142,6 +146,53 @@ qr_status qr_hadamard_quant(const void* x_f16, int64_t T, int32_t d, int64_t ld_
  */
 qr_status qr_hadamard(const void* x_f16, int64_t T, int32_t d, int64_t ld_x, const int8_t* signs,
                       void* y, int32_t y_is_f32, hipStream_t stream);
+
+/*
+ * RMSNorm without its scale, in fp32, fused with per-token symmetric INT4
+ * quantization: the input quantizer of the QKV, gate and up projections
+ * (QuaRot paper, method section: the RMSNorm scale diag(alpha) is absorbed
+ * into the next weights; activation-quantization paragraph: RMSNorm without
+ * scaling stays in FP32 and its output is quantized per token).
+ *   x_f16      [T, ld_x] fp16, row t holds x_t in its first d entries.
+ *   eps        in [0, 1]: r = 1 / sqrt(sum_i x_i^2 / d + eps), y = x * r.
+ *   clip_ratio in [1/1024, 1]; scale and codes as in qr_hadamard_quant with
+ *              y in place of the rotated row.
+ *   q_u8       [T, d/2] packed codes (output); scale_f16 [T] fp16 (output).
+ *   r_dbg      NULL, or [T] fp32 (output): r per row.
+ * fp32 recipe, per row: ss = sum of the exact squares x_i^2 (fp32 additions
+ * in an unspecified order); t = fp32(fp32(ss / d) + eps);
+ * r = fp32(1 / fp32(sqrt(t))), or 0 when t == 0; then the qr_hadamard_quant
+ * recipe with z = x and c = r: a = max|x| * r; s_h = fp16(fp32(clip * a) / 7);
+ * m = r * (1 / s_h) (0 if s_h == 0); q_i = clamp(rne(exact x_i * m), -8, 7).
+ * Requirements: T >= 0; d % 8 == 0, 8 <= d <= 16384; ld_x >= d,
+ * ld_x % 8 == 0; x_f16 16-byte aligned; q_u8 4-byte aligned.
+ */
+qr_status qr_rmsnorm_quant(const void* x_f16, int64_t T, int32_t d, int64_t ld_x, float eps,
+                           float clip_ratio, void* q_u8, void* scale_f16, float* r_dbg,
+                           hipStream_t stream);
+
+/*
+ * Hadamard heads fused with per-token symmetric INT4 quantization: the input
+ * quantizer of the O projection (QuaRot paper, attention-block paragraph:
+ * with (I (x) H_dh) fused into W_v and W_out offline, the forward pass applies
+ * Z <- Z (H_nh (x) I) to the attention output; Figure 6).  Per row, with
+ * element i = h * head_dim + j:
+ *   z[h, j] = sum_h' H_nh[h, h'] x[h', j]   (Sylvester H_nh, entries +-1),
+ *   y = z / sqrt(n_heads), then scale and codes as in qr_hadamard_quant.
+ *   x_f16      [T, ld_x] fp16, d = n_heads * head_dim.
+ *   q_u8       [T, d/2] packed codes (output); scale_f16 [T] fp16 (output).
+ *   z_dbg      NULL, or [T, d] fp32 (output): z before the 1/sqrt(n_heads).
+ * fp32 recipe: the qr_hadamard_quant recipe with c = fp32(1/sqrt(n_heads)); the
+ * order of the additions inside z is not specified.
+ * Requirements: T >= 0; n_heads and head_dim powers of two with
+ * 2 <= n_heads <= 64 and 4J <= head_dim <= 64J, J = max(2, min(8, 128 / n_heads))
+ * (n_heads = 64: head_dim 8 .. 128; 32: 16 .. 256; <= 16: 32 .. 512);
+ * ld_x >= d, ld_x % 8 == 0; x_f16 16-byte aligned; q_u8 4-byte aligned; z_dbg
+ * 16-byte aligned if given.
+ */
+qr_status qr_hadamard_heads_quant(const void* x_f16, int64_t T, int32_t n_heads, int32_t head_dim,
+                                  int64_t ld_x, float clip_ratio, void* q_u8, void* scale_f16,
+                                  float* z_dbg, hipStream_t stream);
 
 /*
  * W4A4 GEMM with fused dequantization epilogue:

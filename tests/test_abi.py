@@ -33,6 +33,7 @@ def test_header_declares_the_path():
     names = declared_functions()
     for must in ("qr_hadamard_quant", "qr_hadamard", "qr_w4a4_gemm", "qr_kv_rotate_quant",
                  "qr_kv_decode_attention", "qr_kv_decode_workspace_bytes",
+                 "qr_rmsnorm_quant", "qr_hadamard_heads_quant",
                  "qr_hadamard_factor", "qr_status_str", "qr_abi_version"):
         assert must in names
 
@@ -175,6 +176,53 @@ def test_kv_decode_validation(lib):
     assert kvd(lib, km=A16 + 2) == QR_ERR_ALIGN
 
 
+def rq(lib, x=A16, T=4, d=8192, ld=8192, eps=1e-5, clip=1.0, q=A16, sc=A16, r=None):
+    return lib.qr_rmsnorm_quant(x, T, d, ld, eps, clip, q, sc, r, None)
+
+
+def test_rmsnorm_quant_validation(lib):
+    assert rq(lib, T=0) == QR_OK
+    assert rq(lib, T=0, d=16384, ld=16384) == QR_OK
+    assert rq(lib, T=-1) == QR_ERR_SHAPE
+    assert rq(lib, ld=8184) == QR_ERR_SHAPE
+    assert rq(lib, d=8196, ld=8200) == QR_ERR_UNSUPPORTED   # not a multiple of 8
+    assert rq(lib, d=16392, ld=16392) == QR_ERR_UNSUPPORTED  # wider than 16384
+    assert rq(lib, eps=-1e-6) == QR_ERR_ARG
+    assert rq(lib, eps=float("nan")) == QR_ERR_ARG
+    assert rq(lib, eps=2.0) == QR_ERR_ARG
+    assert rq(lib, clip=0.0) == QR_ERR_ARG
+    assert rq(lib, x=None) == QR_ERR_NULL
+    assert rq(lib, sc=None) == QR_ERR_NULL
+    assert rq(lib, x=A16 + 8) == QR_ERR_ALIGN
+    assert rq(lib, ld=8196) == QR_ERR_ALIGN
+    assert rq(lib, q=A16 + 2) == QR_ERR_ALIGN
+    assert rq(lib, r=A16 + 2) == QR_ERR_ALIGN
+
+
+def hh(lib, x=A16, T=4, nh=64, dh=128, ld=8192, clip=1.0, q=A16, sc=A16, z=None):
+    return lib.qr_hadamard_heads_quant(x, T, nh, dh, ld, clip, q, sc, z, None)
+
+
+def test_hadamard_heads_quant_validation(lib):
+    assert hh(lib, T=0) == QR_OK
+    for nh, dh in ((64, 128), (32, 128), (32, 256), (16, 512), (8, 64), (2, 32), (64, 8)):
+        assert hh(lib, T=0, nh=nh, dh=dh, ld=nh * dh) == QR_OK, (nh, dh)
+    assert hh(lib, T=-1) == QR_ERR_SHAPE
+    assert hh(lib, nh=0) == QR_ERR_SHAPE
+    assert hh(lib, ld=4096) == QR_ERR_SHAPE
+    assert hh(lib, nh=48, ld=6144) == QR_ERR_UNSUPPORTED      # not a power of two
+    assert hh(lib, nh=128, dh=64) == QR_ERR_UNSUPPORTED       # more than 64 heads
+    assert hh(lib, nh=1, dh=128, ld=128) == QR_ERR_UNSUPPORTED
+    assert hh(lib, nh=64, dh=256, ld=16384) == QR_ERR_UNSUPPORTED
+    assert hh(lib, nh=32, dh=96, ld=3072) == QR_ERR_UNSUPPORTED
+    assert hh(lib, nh=16, dh=16, ld=256) == QR_ERR_UNSUPPORTED
+    assert hh(lib, clip=1.5) == QR_ERR_ARG
+    assert hh(lib, q=None) == QR_ERR_NULL
+    assert hh(lib, x=A16 + 2) == QR_ERR_ALIGN
+    assert hh(lib, ld=8196) == QR_ERR_ALIGN
+    assert hh(lib, z=A16 + 4) == QR_ERR_ALIGN
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros((4, 128), dtype=torch.float16)
@@ -182,3 +230,7 @@ def test_binding_refuses_cpu_tensors():
         qr.hadamard_quant(x)
     with pytest.raises(TypeError):
         qr.hadamard_quant(x.float())
+    with pytest.raises(ValueError):
+        qr.rmsnorm_quant(x)
+    with pytest.raises(ValueError):
+        qr.hadamard_heads_quant(x, 4)
