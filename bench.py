@@ -1,7 +1,7 @@
 """Benchmark of the QuaRot online-rotation + INT4 hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload 70b_prefill|7b_prefill|7b_decode|70b_kv]
+                    [--workload 70b_prefill|7b_prefill|7b_decode|70b_kv|70b_block|7b_block]
                     [--no-cpu-baseline] [--copy-calibration] [--fp16-hadamard]
 
 One step is one pass of the whole hot path over one batch of synthetic input
@@ -16,6 +16,12 @@ One step is one pass of the whole hot path over one batch of synthetic input
   the head-wise rotation of Q.  With --fp16-hadamard the down-projection
   rotation (d = 28672, or 11008 for 7b_prefill) runs the fp16 variant of the
   transform (QR_ROT_HADAMARD_F16) instead of the default fp32 one.
+* 70b_block / 7b_block: the same block with the model's own online path
+  (QuaRot paper, Figures 3 and 6): RMSNorm without scale + INT4 in front of
+  QKV and of gate/up, the Hadamard-heads transform + INT4 in front of O, the
+  full online Hadamard + INT4 only in front of down.  The same five GEMMs in
+  fp16 (torch.matmul) are timed separately as context: the pages' speedups
+  are against an FP16 block.
 * 7b_decode: the same four rotations and five GEMMs at T = 1, 8, 32 and 64.
 * 70b_kv: K/V Init of a 32 x 2048-token prompt (8 KV heads of 128), the
   rotation of its queries (64 heads), then 50 decode steps of Append K, V,
@@ -55,7 +61,8 @@ METRIC = "fused Hadamard+INT4-quant HBM GB/s; W4A4 GEMM TOPS at Llama-2 shapes"
 CSRC = ROOT / "hadamard_rotation_int4_amd" / "csrc"
 KERNEL_SOURCE = {"w4a4_gemm": "w4a4_gemm.hip", "hadamard_quant": "hadamard_quant.hip",
                  "kv_rotate_quant": "kv_quant.hip", "hadamard": "hadamard_quant.hip",
-                 "kv_decode_attention": "kv_decode.hip"}
+                 "kv_decode_attention": "kv_decode.hip", "rmsnorm_quant": "block_quant.hip",
+                 "hadamard_heads_quant": "block_quant.hip"}
 
 
 def parse():
@@ -64,7 +71,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="70b_prefill",
-                    choices=["70b_prefill", "7b_prefill", "7b_decode", "70b_kv"])
+                    choices=["70b_prefill", "7b_prefill", "7b_decode", "70b_kv", "70b_block",
+                             "7b_block"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -112,7 +120,7 @@ def decode_bytes(b, hkv, hq, L, dh, group):
 # Workload construction: a list of launches (kernel, label, bytes, ops, fn)
 # ---------------------------------------------------------------------------
 
-def make_block(torch, qr, wl, W, T, dev, with_kv, f16_down=False):
+def make_block(torch, qr, wl, W, T, dev, with_kv, f16_down=False, quarot=False):
     lin = {l.name: l for l in W.linears}
     H, ffn, wid = W.hidden, lin["down"].k, W.wid
     inputs = {}
@@ -134,6 +142,19 @@ def make_block(torch, qr, wl, W, T, dev, with_kv, f16_down=False):
     L = []
     tag = f"T{T}:" if not with_kv else ""
     for name, x in inputs.items():
+        if quarot and name in ("attn_in", "ffn_in"):
+            # the residual rotation is fused into the weights; RMSNorm (no scale) + INT4 online
+            L.append(("rmsnorm_quant", tag + name, hq_bytes(T, x.shape[1]), 0,
+                      (lambda x=x, name=name: qr.rmsnorm_quant(x, 1e-5, 1.0, out=qbuf[name])),
+                      qbuf[name]))
+            continue
+        if quarot and name == "o_in":
+            # (I (x) H_dh) is fused into W_v / W_out; Hadamard heads + INT4 online
+            L.append(("hadamard_heads_quant", tag + name, hq_bytes(T, x.shape[1]), 0,
+                      (lambda x=x, name=name: qr.hadamard_heads_quant(x, H // 128, 1.0,
+                                                                      out=qbuf[name])),
+                      qbuf[name]))
+            continue
         f16 = f16_down and name == "down_in" and x.shape[1] in (28672, 11008)
         L.append(("hadamard_quant", tag + name + (":fp16" if f16 else ""), hq_bytes(T, x.shape[1]), 0,
                   (lambda x=x, name=name, f16=f16: qr.hadamard_quant(
@@ -166,6 +187,24 @@ def make_block(torch, qr, wl, W, T, dev, with_kv, f16_down=False):
         desc = (f"K/V init into a 4-bit cache ({B}x{S}x{Hkv}x{Dh}, group {G}), "
                 f"Q rotation ({Hq} heads)")
     return L, lin, desc
+
+
+def fp16_linears(torch, wl, W, T, dev):
+    """The block's five linear layers in fp16 (torch.matmul): the FP16 baseline
+    the pages' block speedups are measured against (context, not the path)."""
+    lin = {l.name: l for l in W.linears}
+    xs = {}
+    for i, name in enumerate(("attn_in", "o_in", "ffn_in", "down_in")):
+        d = lin["down"].k if name == "down_in" else W.hidden
+        xs[name] = wl.activations_torch(torch, dev, W.wid, 10 + i, T, d, W.n_outliers,
+                                        W.outlier_lo, W.outlier_hi)
+    L = []
+    for i, (name, l) in enumerate(lin.items()):
+        w = wl.weights_torch(torch, dev, W.wid, 1 + i, l.n, l.k)
+        y = torch.empty((T, l.n), dtype=torch.float16, device=dev)
+        L.append(("fp16_gemm", name, gemm_bytes(T, l.n, l.k), gemm_ops(T, l.n, l.k),
+                  (lambda x=xs[l.input], w=w, y=y: torch.matmul(x, w.t(), out=y)), (y,)))
+    return L
 
 
 def make_kv_decode(torch, qr, wl, W, dev):
@@ -371,15 +410,23 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wname = args.workload
-    W = wl.WORKLOADS[wname]
-    print(f"[bench] workload {W.name}", file=sys.stderr, flush=True)
+    quarot = wname in ("70b_block", "7b_block")
+    W = wl.WORKLOADS[wname.replace("block", "prefill") if quarot else wname]
+    print(f"[bench] workload {W.name}{' (QuaRot online path)' if quarot else ''}", file=sys.stderr,
+          flush=True)
     config = {"workload": None}
-    if wname in ("70b_prefill", "7b_prefill"):
+    if wname in ("70b_prefill", "7b_prefill") or quarot:
         T = W.tokens[0]
-        launches, lin, kvdesc = make_block(torch, qr, wl, W, T, dev, True, args.fp16_hadamard)
+        launches, lin, kvdesc = make_block(torch, qr, wl, W, T, dev, True, args.fp16_hadamard,
+                                           quarot)
+        inputs_desc = ("RMSNorm (no scale) + INT4 before QKV and gate/up, Hadamard heads "
+                       f"({W.hidden // 128} heads of 128) + INT4 before O, online Hadamard "
+                       f"d = {lin['down'].k} + INT4 before down" if quarot
+                       else "4 fused rotate+quant")
         config.update({
-            "workload": f"{W.name}: T={T} tokens, hidden {W.hidden}, FFN {lin['down'].k}, QKV "
-                        f"{lin['qkv'].n}; 4 fused rotate+quant, 5 W4A4 GEMMs, {kvdesc}",
+            "workload": f"{W.name}{' (QuaRot online path)' if quarot else ''}: T={T} tokens, "
+                        f"hidden {W.hidden}, FFN {lin['down'].k}, QKV {lin['qkv'].n}; "
+                        f"{inputs_desc}, 5 W4A4 GEMMs, {kvdesc}",
             "tokens": T, "hidden": W.hidden, "ffn": lin["down"].k,
             "hadamard_arithmetic": (f"fp16 for d = {lin['down'].k}, fp32 otherwise"
                                     if args.fp16_hadamard else "fp32")})
@@ -435,14 +482,17 @@ def main():
         "config": config,
         "roofline": roofline(dominant, wname, launches, per, bound),
     }
-    if any(l[0] == "hadamard_quant" for l in launches):
-        out["roofline_hadamard_quant"] = roofline("hadamard_quant", wname, launches, per, "hbm")
+    for k in ("hadamard_quant", "rmsnorm_quant", "hadamard_heads_quant"):
+        if any(l[0] == k for l in launches):
+            out["roofline_" + k] = roofline(k, wname, launches, per, "hbm")
     if dominant != "kv_rotate_quant" and any(l[0] == "kv_rotate_quant" for l in launches):
         out["roofline_kv_rotate_quant"] = roofline("kv_rotate_quant", wname, launches, per, "hbm")
     out["kernels"] = kernels if len(kernels) <= 40 else {
         k: {"ms": round(sum(p for l, p in zip(launches, per) if l[0] == k), 4),
             "launches": sum(1 for l in launches if l[0] == k)}
         for k in sorted({l[0] for l in launches})}
+    if quarot:
+        out["fp16_context"] = fp16_context(torch, wl, W, T, dev, launches, per, args)
     out["wall_s_timed"] = round(wall, 3)
     out["timing"] = ("HIP graph replay of the step; per-launch times from graphs of 20 "
                      "back-to-back launches (outputs checked equal to the eager run)" if graphed
@@ -451,6 +501,26 @@ def main():
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def fp16_context(torch, wl, W, T, dev, launches, per, args):
+    """The five linear layers in fp16 against the same five in the 4-bit path
+    (their input quantizers plus the W4A4 GEMMs); timed after the step, on
+    their own.  Context for the pages' FP16-block speedups, not a target."""
+    L = fp16_linears(torch, wl, W, T, dev)
+    torch.cuda.synchronize()
+    ms16, per16, _ = run_timed(torch, L, max(1, args.steps // 2), 1)
+    del L
+    lin_kernels = ("w4a4_gemm", "rmsnorm_quant", "hadamard_heads_quant", "hadamard_quant")
+    ms4 = sum(p for l, p in zip(launches, per) if l[0] in lin_kernels)
+    ops = 2 * T * sum(l.n * l.k for l in W.linears)
+    return {"fp16_linears_ms": round(ms16, 4),
+            "fp16_TFLOP/s": round(ops / (ms16 * 1e-3) / 1e12, 1),
+            "fp16_per_gemm_ms": {l.name: round(p, 4) for l, p in zip(W.linears, per16)},
+            "int4_linears_ms": round(ms4, 4),
+            "linears_speedup": round(ms16 / ms4, 3),
+            "note": "torch.matmul (hipBLASLt) fp16 GEMMs of the same shapes vs the 4 input "
+                    "quantizers + 5 W4A4 GEMMs of the step"}
 
 
 def cpu_baseline(W, t_sample):
