@@ -45,14 +45,14 @@ def rmsnorm(x: np.ndarray, eps: float) -> np.ndarray:
     return x * rms_multiplier(x, eps)[..., None]
 
 
-def rmsnorm_quant_math(x: np.ndarray, eps: float, clip: float = 1.0):
+def rmsnorm_quant_math(x: np.ndarray, eps: float, clip: float = 1.0, bits: int = 4):
     """Float64 reference of the fused op: (codes, fp16 scales, y64)."""
     y = rmsnorm(x, eps)
-    q, s = sym_quant_math(y, clip)
+    q, s = sym_quant_math(y, clip, bits)
     return q, s, y
 
 
-def rmsnorm_quant_recipe(x_f16: np.ndarray, r_f32: np.ndarray, clip: float = 1.0):
+def rmsnorm_quant_recipe(x_f16: np.ndarray, r_f32: np.ndarray, clip: float = 1.0, bits: int = 4):
     """Codes and fp16 scales the kernel derives from x and its fp32 multiplier r.
 
     The quantizer input is y = x * r with x exact (fp16 -> fp32) and r one fp32
@@ -63,7 +63,7 @@ def rmsnorm_quant_recipe(x_f16: np.ndarray, r_f32: np.ndarray, clip: float = 1.0
     against rms_multiplier() within its error bound.
     """
     x32 = np.asarray(x_f16, dtype=F16).astype(F32)
-    return sym_quant_recipe_rows(x32, np.asarray(r_f32, dtype=F32), clip)
+    return sym_quant_recipe_rows(x32, np.asarray(r_f32, dtype=F32), clip, bits)
 
 
 # ---------------------------------------------------------------------------
@@ -87,16 +87,16 @@ def hadamard_heads(x: np.ndarray, n_heads: int) -> np.ndarray:
     return hadamard_heads_unnormalised(x, n_heads) / np.sqrt(np.float64(n_heads))
 
 
-def hadamard_heads_quant_math(x: np.ndarray, n_heads: int, clip: float = 1.0):
+def hadamard_heads_quant_math(x: np.ndarray, n_heads: int, clip: float = 1.0, bits: int = 4):
     """Float64 reference of the fused op: (codes, fp16 scales, y64)."""
     y = hadamard_heads(x, n_heads)
-    q, s = sym_quant_math(y, clip)
+    q, s = sym_quant_math(y, clip, bits)
     return q, s, y
 
 
-def hadamard_heads_quant_recipe(z: np.ndarray, n_heads: int, clip: float = 1.0):
+def hadamard_heads_quant_recipe(z: np.ndarray, n_heads: int, clip: float = 1.0, bits: int = 4):
     """Codes and fp16 scales from the fp32 transform output z (no 1/sqrt(n_h)),
     with c = fp32(1/sqrt(n_h)) per row, as in the rotate+quantize recipe."""
     z32 = np.asarray(z, dtype=F32)
     c = np.full(z32.shape[:-1], F32(1.0 / np.sqrt(np.float64(n_heads))), dtype=F32)
-    return sym_quant_recipe_rows(z32, c, clip)
+    return sym_quant_recipe_rows(z32, c, clip, bits)

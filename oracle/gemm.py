@@ -20,17 +20,21 @@ F32 = np.float32
 F16 = np.float16
 
 
-def int4_matmul_exact(a_codes: np.ndarray, w_codes: np.ndarray) -> np.ndarray:
-    """acc = A W^T for int codes, exact, as int64.
+def int_matmul_exact(a_codes: np.ndarray, w_codes: np.ndarray) -> np.ndarray:
+    """acc = A W^T for int codes of at most 8 bits, exact, as int64.
 
     float64 BLAS is exact here: every product and partial sum is an integer of
-    magnitude <= 64 K < 2^53, so no rounding happens in any summation order.
+    magnitude <= 2^14 K < 2^53, so no rounding happens in any summation order.
     """
     a = np.asarray(a_codes, dtype=np.float64)
     w = np.asarray(w_codes, dtype=np.float64)
     assert a.shape[-1] == w.shape[-1]
-    assert a.shape[-1] * 64 < 2 ** 53
+    assert np.abs(a).max(initial=0) <= 128 and np.abs(w).max(initial=0) <= 128
+    assert a.shape[-1] * (1 << 14) < 2 ** 53
     return (a @ w.T).astype(np.int64)
+
+
+int4_matmul_exact = int_matmul_exact
 
 
 def int4_matmul_bruteforce(a_codes: np.ndarray, w_codes: np.ndarray) -> np.ndarray:
@@ -46,8 +50,11 @@ def w4a4_acc(a_packed: np.ndarray, w_packed: np.ndarray) -> np.ndarray:
 
 
 def epilogue_recipe(acc: np.ndarray, a_scale: np.ndarray, w_scale: np.ndarray) -> np.ndarray:
-    """fp16 Y = fp16_rne(fp32(fp32(acc) * a_s[t]) * w_s[n])."""
-    acc32 = np.asarray(acc).astype(F32)   # |acc| < 2^24: exact
+    """fp16 Y = fp16_rne(fp32(fp32(acc) * a_s[t]) * w_s[n]).
+
+    fp32(acc) is exact for INT4 codes (|acc| <= 64 K < 2^24); 8-bit codes can
+    pass 2^24, and the conversion then rounds to nearest even."""
+    acc32 = np.asarray(acc).astype(F32)
     a_s = np.asarray(a_scale, dtype=F16).astype(F32)[:, None]
     w_s = np.asarray(w_scale, dtype=F16).astype(F32)[None, :]
     with np.errstate(over="ignore"):
@@ -60,6 +67,13 @@ def epilogue_math(acc: np.ndarray, a_scale: np.ndarray, w_scale: np.ndarray) -> 
     a_s = np.asarray(a_scale, dtype=F16).astype(np.float64)[:, None]
     w_s = np.asarray(w_scale, dtype=F16).astype(np.float64)[None, :]
     return np.asarray(acc, dtype=np.float64) * a_s * w_s
+
+
+def w8a8_gemm(a_codes, a_scale, w_codes, w_scale) -> tuple[np.ndarray, np.ndarray]:
+    """(fp16 Y, int64 acc) of the linear layer on b-bit codes stored one per
+    byte (int8 [T, K] and [N, K]; QuaRot paper, 6- and 8-bit RTN results)."""
+    acc = int_matmul_exact(a_codes, w_codes)
+    return epilogue_recipe(acc, a_scale, w_scale), acc
 
 
 def w4a4_gemm(a_packed, a_scale, w_packed, w_scale) -> tuple[np.ndarray, np.ndarray]:

@@ -8,6 +8,11 @@ scale and rounded to the nearest integer.  The implementation paragraph adds a
 constant clipping ratio (0.9 for these inputs), so s = clip * max|y| / 7, and
 INT4's range clamps the codes to [-8, 7].
 
+Other bit widths (QuaRot paper, results with 6- and 8-bit round-to-nearest
+weights and activations, Table 9): b-bit symmetric codes use
+s = clip * max|y| / (2^(b-1) - 1) and clamp to [-2^(b-1), 2^(b-1) - 1]; b = 4 is
+the INT4 case above.  Codes of b > 4 bits are stored one per byte (int8).
+
 Readings taken where the pages are silent:
 * ties round half to even (IEEE default, and what PyTorch's round does);
 * the stored scale is fp16 and the division uses that stored value, so codes
@@ -54,26 +59,35 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
 # Math mode (float64)
 # ---------------------------------------------------------------------------
 
-def sym_scale_math(y: np.ndarray, clip: float = 1.0) -> np.ndarray:
-    """fp16 per-row scale: fp16(clip * max|y| / 7) computed in float64."""
+def code_range(bits: int) -> tuple[int, int, int]:
+    """(qmax, lo, hi) of b-bit symmetric codes: qmax = 2^(b-1) - 1, range [-2^(b-1), qmax]."""
+    assert 2 <= bits <= 8
+    qmax = (1 << (bits - 1)) - 1
+    return qmax, -(1 << (bits - 1)), qmax
+
+
+def sym_scale_math(y: np.ndarray, clip: float = 1.0, bits: int = 4) -> np.ndarray:
+    """fp16 per-row scale: fp16(clip * max|y| / qmax) computed in float64 (qmax = 7 for INT4)."""
     y = np.asarray(y, dtype=np.float64)
     amax = np.abs(y).max(axis=-1)
-    return (clip * amax / 7.0).astype(F16)
+    return (clip * amax / float(code_range(bits)[0])).astype(F16)
 
 
-def sym_quant_with_scale(y: np.ndarray, scale_f16: np.ndarray) -> np.ndarray:
-    """Codes clamp(round_half_even(y / s), -8, 7) for given fp16 scales (float64 division)."""
+def sym_quant_with_scale(y: np.ndarray, scale_f16: np.ndarray, bits: int = 4) -> np.ndarray:
+    """Codes clamp(round_half_even(y / s), lo, hi) for given fp16 scales (float64 division);
+    [-8, 7] for INT4."""
+    _, lo, hi = code_range(bits)
     y = np.asarray(y, dtype=np.float64)
     s = np.asarray(scale_f16, dtype=F16).astype(np.float64)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         u = np.where(s > 0, y / np.where(s > 0, s, 1.0), 0.0)
-    return np.clip(np.rint(u), -8, 7).astype(np.int8)
+    return np.clip(np.rint(u), lo, hi).astype(np.int8)
 
 
-def sym_quant_math(y: np.ndarray, clip: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
+def sym_quant_math(y: np.ndarray, clip: float = 1.0, bits: int = 4) -> tuple[np.ndarray, np.ndarray]:
     """(int8 codes, fp16 scales) of the float64 rows y."""
-    s = sym_scale_math(y, clip)
-    return sym_quant_with_scale(y, s), s
+    s = sym_scale_math(y, clip, bits)
+    return sym_quant_with_scale(y, s, bits), s
 
 
 def tie_distance(y: np.ndarray, scale_f16: np.ndarray) -> np.ndarray:
@@ -96,7 +110,7 @@ def norm_constant(d: int, rotated: bool) -> np.float32:
     return F32(1.0 / np.sqrt(np.float64(d)))
 
 
-def sym_quant_recipe(z: np.ndarray, d: int, rotated: bool, clip: float = 1.0
+def sym_quant_recipe(z: np.ndarray, d: int, rotated: bool, clip: float = 1.0, bits: int = 4
                      ) -> tuple[np.ndarray, np.ndarray]:
     """Codes and fp16 scales from the fp32 transform output z = H (s * x).
 
@@ -110,20 +124,22 @@ def sym_quant_recipe(z: np.ndarray, d: int, rotated: bool, clip: float = 1.0
     """
     z32 = np.asarray(z, dtype=F32)
     c = np.full(z32.shape[:-1], norm_constant(d, rotated), dtype=F32)
-    return sym_quant_recipe_rows(z32, c, clip)
+    return sym_quant_recipe_rows(z32, c, clip, bits)
 
 
-def sym_quant_recipe_rows(z: np.ndarray, c: np.ndarray, clip: float = 1.0
+def sym_quant_recipe_rows(z: np.ndarray, c: np.ndarray, clip: float = 1.0, bits: int = 4
                           ) -> tuple[np.ndarray, np.ndarray]:
     """The recipe of sym_quant_recipe() with one fp32 constant c per row: the
     quantizer input is y = z * c, with z the exact fp32 row (the transform
-    output, or the input itself) and c its normalisation."""
+    output, or the input itself) and c its normalisation.  For b bits the 7
+    becomes qmax = 2^(b-1) - 1 and the clamp [-2^(b-1), qmax]."""
+    qmax, lo, hi = code_range(bits)
     z32 = np.asarray(z, dtype=F32)
     c = np.asarray(c, dtype=F32)
     clip32 = F32(clip)
     az = np.abs(z32).max(axis=-1)
     a = (az * c).astype(F32)
-    s = ((clip32 * a).astype(F32) / F32(7.0)).astype(F32)
+    s = ((clip32 * a).astype(F32) / F32(qmax)).astype(F32)
     s_h = s.astype(F16)
     s_h32 = s_h.astype(F32)
     with np.errstate(divide="ignore"):
@@ -133,7 +149,7 @@ def sym_quant_recipe_rows(z: np.ndarray, c: np.ndarray, clip: float = 1.0
     # half-to-even straight to an integer (the kernel does the same with one
     # fused multiply-add against 1.5 * 2^23).
     prod = z32.astype(np.float64) * m.astype(np.float64)[..., None]
-    q = np.clip(np.rint(prod), -8, 7).astype(np.int8)
+    q = np.clip(np.rint(prod), lo, hi).astype(np.int8)
     return q, s_h
 
 
@@ -142,9 +158,10 @@ def dequant(codes: np.ndarray, scale_f16: np.ndarray) -> np.ndarray:
     return np.asarray(codes, dtype=np.float64) * np.asarray(scale_f16, dtype=F16).astype(np.float64)[..., None]
 
 
-def rotate_quant_math(x: np.ndarray, signs, clip: float = 1.0, rotated: bool = True):
+def rotate_quant_math(x: np.ndarray, signs, clip: float = 1.0, rotated: bool = True,
+                      bits: int = 4):
     """Float64 reference of the fused op: (codes, fp16 scales, y64)."""
     from .hadamard import rotate
     y = rotate(x, signs) if rotated else np.asarray(x, dtype=np.float64)
-    q, s = sym_quant_math(y, clip)
+    q, s = sym_quant_math(y, clip, bits)
     return q, s, y

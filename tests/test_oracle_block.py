@@ -148,3 +148,13 @@ def test_heads_quant_recipe_agrees_with_math():
     diff = q_rec.astype(int) - q64.astype(int)
     tie = oq.tie_distance(y64, s64)
     assert not ((diff != 0) & (tie > 1e-3)).any()
+
+
+def test_block_quantizers_take_the_bit_width():
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((4, 256)) * 4).astype(np.float16)
+    q8, s8, y = ob.rmsnorm_quant_math(x, 1e-5, 1.0, 8)
+    assert np.array_equal(s8, oq.sym_scale_math(y, 1.0, 8))
+    assert np.abs(q8).max() == 127
+    qh, sh, yh = ob.hadamard_heads_quant_math(x, 4, 1.0, 6)
+    assert np.abs(qh).max() == 31 and np.array_equal(sh, oq.sym_scale_math(yh, 1.0, 6))

@@ -7,6 +7,7 @@ import pytest
 
 import workloads as wl
 from oracle import gemm, hadamard as had, quant
+from oracle import quant as oq
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -152,3 +153,75 @@ def test_tiny_w4a4_linear_tracks_fp_product():
     y0, _ = gemm.w4a4_gemm(quant.pack_int4(qa0), sa0, quant.pack_int4(qw0), sw0)
     rel0 = np.linalg.norm(y0.astype(np.float64) - ref) / np.linalg.norm(ref)
     assert rel0 > 2 * rel
+
+
+# ---------------------------------------------------------------------------
+# b-bit codes (6- and 8-bit round-to-nearest, QuaRot paper Table 9)
+# ---------------------------------------------------------------------------
+
+def test_bbit_code_ranges():
+    assert oq.code_range(4) == (7, -8, 7)
+    assert oq.code_range(6) == (31, -32, 31)
+    assert oq.code_range(8) == (127, -128, 127)
+    assert oq.code_range(2) == (1, -2, 1)
+
+
+def test_bbit_unit_scale_rows_round_half_even():
+    # max|y| = qmax gives scale exactly 1, so the codes are rne(y)
+    q, s = oq.sym_quant_math(np.array([[127.0, -63.5, 0.5, 1.5, -2.5, 100.49]]), 1.0, 8)
+    assert s[0] == 1.0 and q.tolist() == [[127, -64, 0, 2, -2, 100]]
+    q, s = oq.sym_quant_math(np.array([[31.0, -31.0, 15.5, -2.5, 0.0, 30.5]]), 1.0, 6)
+    assert s[0] == 1.0 and q.tolist() == [[31, -31, 16, -2, 0, 30]]
+    q, s = oq.sym_quant_math(np.array([[1.0, -1.0, 0.5, -0.5]]), 1.0, 2)
+    assert s[0] == 1.0 and q.tolist() == [[1, -1, 0, 0]]
+
+
+def test_bbit_clip_reaches_the_asymmetric_minimum():
+    # clip 1/2: |y| / s ~ 2 qmax, clamped to [-2^(b-1), qmax]
+    for bits in (6, 8):
+        qmax, lo, hi = oq.code_range(bits)
+        q, s = oq.sym_quant_math(np.array([[100.0, -100.0, 0.0, 1.0]]), 0.5, bits)
+        assert s[0] == np.float16(0.5 * 100.0 / qmax)
+        assert q[0, 0] == hi and q[0, 1] == lo and q[0, 2] == 0
+
+
+def test_bbit_four_bits_is_the_int4_quantizer():
+    y = np.random.default_rng(31).standard_normal((8, 256)) * 3
+    for clip in (1.0, 0.9):
+        q4, s4 = oq.sym_quant_math(y, clip)
+        qb, sb = oq.sym_quant_math(y, clip, 4)
+        assert np.array_equal(q4, qb) and np.array_equal(s4, sb)
+
+
+@pytest.mark.parametrize("bits", [6, 8])
+def test_bbit_recipe_agrees_with_math(bits):
+    rng = np.random.default_rng(40 + bits)
+    z = (rng.integers(-2000, 2000, size=(16, 512)) / 8.0).astype(np.float32)  # exact fp32 rows
+    q_rec, s_rec = oq.sym_quant_recipe(z, 512, True, 1.0, bits)
+    q64, s64 = oq.sym_quant_math(z.astype(np.float64) / np.sqrt(512), 1.0, bits)
+    assert np.abs(s_rec.view(np.int16).astype(int) - s64.view(np.int16).astype(int)).max() <= 1
+    diff = q_rec.astype(int) - q64.astype(int)
+    assert np.abs(diff).max() <= 1
+    qmax = oq.code_range(bits)[0]
+    # the 8-bit codes' relative resolution is 1/127: the reconstruction error is
+    # at most half a step of the scale
+    recon = q_rec.astype(np.float64) * s_rec.astype(np.float64)[:, None]
+    y = z.astype(np.float64) / np.sqrt(512)
+    assert (np.abs(recon - y) <= 0.5 * s_rec.astype(np.float64)[:, None] * (1 + 1e-2)).all()
+    assert np.abs(q_rec).max() <= qmax
+
+
+def test_int8_gemm_bruteforce_and_epilogue_rounding():
+    rng = np.random.default_rng(50)
+    a = rng.integers(-128, 128, size=(5, 96)).astype(np.int8)
+    w = rng.integers(-128, 128, size=(7, 96)).astype(np.int8)
+    assert np.array_equal(gemm.int_matmul_exact(a, w), gemm.int4_matmul_bruteforce(a, w))
+    # extreme codes: -128 * -128 summed over K stays exact in int64
+    big = np.full((1, 4096), -128, np.int8)
+    assert gemm.int_matmul_exact(big, big)[0, 0] == 128 * 128 * 4096
+    # accumulators past 2^24 (8-bit codes) still give the nearest fp16 of acc * a_s * w_s
+    acc = np.array([[2 ** 24 + 1, 2 ** 24 + 3, 2 ** 25 + 2, -(2 ** 24) - 1]])
+    y = gemm.epilogue_recipe(acc, np.full(1, 2.0 ** -10, np.float16), np.full(4, 2.0 ** -10, np.float16))
+    assert y.astype(np.float64).tolist() == [[16.0, 16.0, 32.0, -16.0]]
+    yq, accq = gemm.w8a8_gemm(a, np.ones(5, np.float16), w, np.ones(7, np.float16))
+    assert np.array_equal(accq, gemm.int4_matmul_bruteforce(a, w))
