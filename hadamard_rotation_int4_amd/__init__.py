@@ -15,6 +15,9 @@ Functions (same names as the C entry points without the ``qr_`` prefix):
                   rotate=True, z_dbg=False) -> None[, z]
   rmsnorm_quant(x, eps, clip_ratio, r_dbg=False) -> (q_u8, scale_f16[, r])
   hadamard_heads_quant(x, n_heads, clip_ratio, z_dbg=False) -> (q_u8, scale_f16[, z])
+  hadamard_quant_i8 / rmsnorm_quant_i8 / hadamard_heads_quant_i8(..., bits=8)
+      -> (q_i8, scale_f16[, dbg]): b-bit codes one per byte (2 <= bits <= 8)
+  w8a8_gemm(a_q, a_scale, w_q, w_scale, acc_dbg=False) -> y_f16[, acc_i32]
   hadamard_factor(d) -> (n, m);  abi_version();  status_str(code)
 """
 from __future__ import annotations
@@ -62,6 +65,15 @@ def _load():
     lib.qr_rmsnorm_quant.argtypes = [vp, i64, i32, i64, f32, f32, vp, vp, vp, vp]
     lib.qr_hadamard_heads_quant.restype = ctypes.c_int
     lib.qr_hadamard_heads_quant.argtypes = [vp, i64, i32, i32, i64, f32, vp, vp, vp, vp]
+    lib.qr_hadamard_quant_i8.restype = ctypes.c_int
+    lib.qr_hadamard_quant_i8.argtypes = [vp, i64, i32, i64, ctypes.c_int, vp, f32, i32, vp, vp, vp,
+                                         vp]
+    lib.qr_rmsnorm_quant_i8.restype = ctypes.c_int
+    lib.qr_rmsnorm_quant_i8.argtypes = [vp, i64, i32, i64, f32, f32, i32, vp, vp, vp, vp]
+    lib.qr_hadamard_heads_quant_i8.restype = ctypes.c_int
+    lib.qr_hadamard_heads_quant_i8.argtypes = [vp, i64, i32, i32, i64, f32, i32, vp, vp, vp, vp]
+    lib.qr_w8a8_gemm.restype = ctypes.c_int
+    lib.qr_w8a8_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp, vp]
     lib.qr_kv_decode_workspace_bytes.restype = i64
     lib.qr_kv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.qr_kv_decode_attention.restype = ctypes.c_int
@@ -171,17 +183,27 @@ def hadamard_quant(x, signs=None, clip_ratio: float = 1.0, rotate: bool = True,
     return (q, sc, z) if z_dbg else (q, sc)
 
 
-def _quant_out(out, T, d, device):
+def _quant_out(out, T, d, device, i8=False):
+    """(codes, scales) outputs: packed uint8 [T, d/2], or int8 [T, d] one code per byte."""
     torch = _torch()
+    qdt, qw = (torch.int8, d) if i8 else (torch.uint8, d // 2)
     if out is None:
-        return (torch.empty((T, d // 2), dtype=torch.uint8, device=device),
+        return (torch.empty((T, qw), dtype=qdt, device=device),
                 torch.empty((T,), dtype=torch.float16, device=device))
     q, sc = out
-    _need(q, torch.uint8, "q")
+    _need(q, qdt, "q")
     _need(sc, torch.float16, "scale")
-    if q.numel() != T * (d // 2) or not q.is_contiguous() or sc.numel() != T:
+    if q.numel() != T * qw or not q.is_contiguous() or sc.numel() != T:
         raise ValueError("out tensors have the wrong size or layout")
     return q, sc
+
+
+def _rows(x):
+    torch = _torch()
+    _need(x, torch.float16, "x", 2)
+    if x.numel() and x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous (stride(1) == 1)")
+    return x.shape
 
 
 def rmsnorm_quant(x, eps: float = 1e-5, clip_ratio: float = 1.0, r_dbg: bool = False,
@@ -225,6 +247,53 @@ def hadamard_heads_quant(x, n_heads: int, clip_ratio: float = 1.0, z_dbg: bool =
     return (q, sc, z) if z_dbg else (q, sc)
 
 
+def hadamard_quant_i8(x, signs=None, clip_ratio: float = 1.0, bits: int = 8,
+                      rotate: bool = True, z_dbg: bool = False, out=None, stream=None):
+    """As hadamard_quant with b-bit codes one per byte: (q int8 [T, d], scale[, z])."""
+    torch = _torch()
+    T, d = _rows(x)
+    s = _signs(signs, d, x.device) if rotate else None
+    q, sc = _quant_out(out, T, d, x.device, i8=True)
+    z = torch.empty((T, d), dtype=torch.float32, device=x.device) if z_dbg else None
+    code = _load().qr_hadamard_quant_i8(_ptr(x), T, d, x.stride(0) if T > 0 else d,
+                                        QR_ROT_HADAMARD if rotate else QR_ROT_NONE, _ptr(s),
+                                        float(clip_ratio), int(bits), _ptr(q), _ptr(sc), _ptr(z),
+                                        _stream(stream))
+    _check(code, "qr_hadamard_quant_i8")
+    return (q, sc, z) if z_dbg else (q, sc)
+
+
+def rmsnorm_quant_i8(x, eps: float = 1e-5, clip_ratio: float = 1.0, bits: int = 8,
+                     r_dbg: bool = False, out=None, stream=None):
+    """As rmsnorm_quant with b-bit codes one per byte: (q int8 [T, d], scale[, r])."""
+    torch = _torch()
+    T, d = _rows(x)
+    q, sc = _quant_out(out, T, d, x.device, i8=True)
+    r = torch.empty((T,), dtype=torch.float32, device=x.device) if r_dbg else None
+    code = _load().qr_rmsnorm_quant_i8(_ptr(x), T, d, x.stride(0) if T > 0 else d, float(eps),
+                                       float(clip_ratio), int(bits), _ptr(q), _ptr(sc), _ptr(r),
+                                       _stream(stream))
+    _check(code, "qr_rmsnorm_quant_i8")
+    return (q, sc, r) if r_dbg else (q, sc)
+
+
+def hadamard_heads_quant_i8(x, n_heads: int, clip_ratio: float = 1.0, bits: int = 8,
+                            z_dbg: bool = False, out=None, stream=None):
+    """As hadamard_heads_quant with b-bit codes one per byte: (q int8 [T, d], scale[, z])."""
+    torch = _torch()
+    T, d = _rows(x)
+    if n_heads <= 0 or d % n_heads:
+        raise ValueError(f"row width {d} is not a multiple of n_heads={n_heads}")
+    q, sc = _quant_out(out, T, d, x.device, i8=True)
+    z = torch.empty((T, d), dtype=torch.float32, device=x.device) if z_dbg else None
+    code = _load().qr_hadamard_heads_quant_i8(_ptr(x), T, int(n_heads), d // int(n_heads),
+                                              x.stride(0) if T > 0 else d, float(clip_ratio),
+                                              int(bits), _ptr(q), _ptr(sc), _ptr(z),
+                                              _stream(stream))
+    _check(code, "qr_hadamard_heads_quant_i8")
+    return (q, sc, z) if z_dbg else (q, sc)
+
+
 def hadamard(x, signs=None, out_dtype=None, stream=None, out=None):
     """y = H_d diag(s) x / sqrt(d) row-wise; x fp16 [T, d]; y fp32 (default) or fp16.
 
@@ -253,9 +322,19 @@ def hadamard(x, signs=None, out_dtype=None, stream=None, out=None):
 
 def w4a4_gemm(a_q, a_scale, w_q, w_scale, acc_dbg: bool = False, out=None, stream=None):
     """Y fp16 [T, N] = dequant(A_q W_q^T); a_q uint8 [T, K/2], w_q uint8 [N, K/2]."""
+    return _gemm(a_q, a_scale, w_q, w_scale, acc_dbg, out, stream, False)
+
+
+def w8a8_gemm(a_q, a_scale, w_q, w_scale, acc_dbg: bool = False, out=None, stream=None):
+    """Y fp16 [T, N] = dequant(A_q W_q^T); a_q int8 [T, K], w_q int8 [N, K] (codes one per byte)."""
+    return _gemm(a_q, a_scale, w_q, w_scale, acc_dbg, out, stream, True)
+
+
+def _gemm(a_q, a_scale, w_q, w_scale, acc_dbg, out, stream, i8):
     torch = _torch()
-    _need(a_q, torch.uint8, "a_q", 2)
-    _need(w_q, torch.uint8, "w_q", 2)
+    cdt = torch.int8 if i8 else torch.uint8
+    _need(a_q, cdt, "a_q", 2)
+    _need(w_q, cdt, "w_q", 2)
     _need(a_scale, torch.float16, "a_scale", 1)
     _need(w_scale, torch.float16, "w_scale", 1)
     for name, t in (("a_q", a_q), ("w_q", w_q), ("a_scale", a_scale), ("w_scale", w_scale)):
@@ -265,16 +344,17 @@ def w4a4_gemm(a_q, a_scale, w_q, w_scale, acc_dbg: bool = False, out=None, strea
     N, kh2 = w_q.shape
     if kh != kh2 or a_scale.numel() != T or w_scale.numel() != N:
         raise ValueError("inconsistent GEMM operand shapes")
-    K = 2 * kh
+    K = kh if i8 else 2 * kh
     y = torch.empty((T, N), dtype=torch.float16, device=a_q.device) if out is None else out
     if out is not None:
         _need(y, torch.float16, "out", 2)
         if tuple(y.shape) != (T, N) or not y.is_contiguous():
             raise ValueError("out must be a contiguous fp16 [T, N] tensor")
     acc = torch.empty((T, N), dtype=torch.int32, device=a_q.device) if acc_dbg else None
-    code = _load().qr_w4a4_gemm(_ptr(a_q), _ptr(a_scale), T, _ptr(w_q), _ptr(w_scale), N, K,
-                                _ptr(y), _ptr(acc), _stream(stream))
-    _check(code, "qr_w4a4_gemm")
+    fn = _load().qr_w8a8_gemm if i8 else _load().qr_w4a4_gemm
+    code = fn(_ptr(a_q), _ptr(a_scale), T, _ptr(w_q), _ptr(w_scale), N, K, _ptr(y), _ptr(acc),
+              _stream(stream))
+    _check(code, "qr_w8a8_gemm" if i8 else "qr_w4a4_gemm")
     return (y, acc) if acc_dbg else y
 
 

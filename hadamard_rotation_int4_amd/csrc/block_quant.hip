@@ -28,10 +28,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 // k_rms_quant: one wavefront per row, lane l holds the 8-element chunks
 // l, l + 64, ... (16-byte loads, 4-byte stores of packed codes).
 // ===========================================================================
-template <int NCH>
+// Q8: b-bit codes one per byte (8-byte stores per chunk) instead of packed INT4.
+template <int NCH, bool Q8>
 __global__ __launch_bounds__(256) void k_rms_quant(const uint16_t* __restrict__ x, int64_t T,
                                                    int d, int64_t ld, float eps, float clip,
-                                                   uint8_t* __restrict__ q,
+                                                   int bits, uint8_t* __restrict__ q,
                                                    uint16_t* __restrict__ scale,
                                                    float* __restrict__ rdbg) {
   const int lane = threadIdx.x & 63;
@@ -62,12 +63,13 @@ __global__ __launch_bounds__(256) void k_rms_quant(const uint16_t* __restrict__ 
   // mean square plus eps is 0 (an all-zero row with eps = 0)
   const float t = __fadd_rn(__fdiv_rn(ss, (float)d), eps);
   const float r = t > 0.0f ? __fdiv_rn(1.0f, __fsqrt_rn(t)) : 0.0f;
+  const QRange rg = q_range(Q8 ? bits : 4);
   uint16_t sh;
   float m;
-  sym_scale(am, r, clip, &sh, &m);
-  // |x m| <= 7 (1 + 2^-11) < 7.5 unless clip < 1 or the scale is subnormal
+  sym_scale(am, r, clip, &sh, &m, rg.qmax);
+  // |x m| <= qmax (1 + 2^-11) < qmax + 1/2 unless clip < 1 or the scale is subnormal
   const bool clamp = clip < 1.0f || (sh & 0x7fffu) < 0x0400u;
-  uint8_t* qr_ = q + row * (d / 2);
+  uint8_t* qr_ = q + row * (Q8 ? d : d / 2);
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
     const int c = lane + 64 * k;
@@ -78,7 +80,17 @@ __global__ __launch_bounds__(256) void k_rms_quant(const uint16_t* __restrict__ 
         v[2 * j] = h2f((uint16_t)(raw[k][j] & 0xffffu));
         v[2 * j + 1] = h2f((uint16_t)(raw[k][j] >> 16));
       }
-      st_stream((uint32_t*)(qr_ + 4 * c), clamp ? quant_pack8<true>(v, m) : quant_pack8<false>(v, m));
+      if constexpr (Q8) {
+        if (clamp)
+          st_stream8(qr_ + 8 * c, quant_pack4_i8<true>(v, m, rg.lo, rg.hi),
+                     quant_pack4_i8<true>(v + 4, m, rg.lo, rg.hi));
+        else
+          st_stream8(qr_ + 8 * c, quant_pack4_i8<false>(v, m, rg.lo, rg.hi),
+                     quant_pack4_i8<false>(v + 4, m, rg.lo, rg.hi));
+      } else {
+        st_stream((uint32_t*)(qr_ + 4 * c),
+                  clamp ? quant_pack8<true>(v, m) : quant_pack8<false>(v, m));
+      }
     }
   }
   if (lane == 0) {
@@ -143,9 +155,9 @@ __device__ __forceinline__ uint32_t quant_packJ(const float* v, float m) {
   }
 }
 
-template <int NH, int J, int LPR>
+template <int NH, int J, int LPR, bool Q8>
 __global__ __launch_bounds__(256) void k_heads_quant(const uint16_t* __restrict__ x, int64_t T,
-                                                     int64_t ld, float c, float clip,
+                                                     int64_t ld, float c, float clip, int bits,
                                                      uint8_t* __restrict__ q,
                                                      uint16_t* __restrict__ scale,
                                                      float* __restrict__ zdbg) {
@@ -200,11 +212,39 @@ __global__ __launch_bounds__(256) void k_heads_quant(const uint16_t* __restrict_
     for (int j = 0; j < J; ++j) am = fmaxf(am, fabsf(v[h][j]));
 #pragma unroll
   for (int o = 1; o < LPR; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
+  const QRange rg = q_range(Q8 ? bits : 4);
   uint16_t sh;
   float m;
-  sym_scale(am, c, clip, &sh, &m);
+  sym_scale(am, c, clip, &sh, &m, rg.qmax);
   if (!valid) return;
   const bool clamp = clip < 1.0f || (sh & 0x7fffu) < 0x0400u;
+  if constexpr (Q8) {
+    // J codes of one byte each per head
+    uint8_t* q8 = q + row * D + j0;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      uint8_t* dst = q8 + h * DH;
+      if constexpr (J == 2) {
+        const uint32_t p = clamp ? quant_pack2_i8<true>(v[h], m, rg.lo, rg.hi)
+                                 : quant_pack2_i8<false>(v[h], m, rg.lo, rg.hi);
+        if (QR_NT) __builtin_nontemporal_store((uint16_t)p, (uint16_t*)dst);
+        else *(uint16_t*)dst = (uint16_t)p;
+      } else if constexpr (J == 4) {
+        const uint32_t p = clamp ? quant_pack4_i8<true>(v[h], m, rg.lo, rg.hi)
+                                 : quant_pack4_i8<false>(v[h], m, rg.lo, rg.hi);
+        st_stream((uint32_t*)dst, p);
+      } else {
+        if (clamp)
+          st_stream8(dst, quant_pack4_i8<true>(v[h], m, rg.lo, rg.hi),
+                     quant_pack4_i8<true>(v[h] + 4, m, rg.lo, rg.hi));
+        else
+          st_stream8(dst, quant_pack4_i8<false>(v[h], m, rg.lo, rg.hi),
+                     quant_pack4_i8<false>(v[h] + 4, m, rg.lo, rg.hi));
+      }
+    }
+    if (sub == 0) scale[row] = sh;
+    return;
+  }
   uint8_t* qr_ = q + row * (D / 2) + j0 / 2;
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
@@ -227,13 +267,14 @@ static int blocks_for(int64_t rows, int rows_per_block) {
   return (int)((rows + rows_per_block - 1) / rows_per_block);
 }
 
+template <bool Q8>
 static qr_status launch_rms(const uint16_t* x, int64_t T, int d, int64_t ld, float eps, float clip,
-                            uint8_t* q, uint16_t* sc, float* r, hipStream_t st) {
+                            int bits, uint8_t* q, uint16_t* sc, float* r, hipStream_t st) {
   const int per_lane = (d / 8 + 63) / 64;
   const int grid = blocks_for(T, 4);
 #define QR_RMS(N)                                                                              \
-  hipLaunchKernelGGL((k_rms_quant<N>), dim3(grid), dim3(256), 0, st, x, T, d, ld, eps, clip, q, \
-                     sc, r)
+  hipLaunchKernelGGL((k_rms_quant<N, Q8>), dim3(grid), dim3(256), 0, st, x, T, d, ld, eps, clip, \
+                     bits, q, sc, r)
   if (per_lane <= 1) QR_RMS(1);
   else if (per_lane <= 2) QR_RMS(2);
   else if (per_lane <= 4) QR_RMS(4);
@@ -248,17 +289,18 @@ static qr_status launch_rms(const uint16_t* x, int64_t T, int d, int64_t ld, flo
 // values per lane J = min(8, 128 / NH); lanes per row = head_dim / J
 static int heads_j(int nh) { return nh >= 16 ? 128 / nh : 8; }
 
-template <int NH>
+template <int NH, bool Q8>
 static qr_status launch_heads_nh(int dh, const uint16_t* x, int64_t T, int64_t ld, float c,
-                                 float clip, uint8_t* q, uint16_t* sc, float* z, hipStream_t st) {
+                                 float clip, int bits, uint8_t* q, uint16_t* sc, float* z,
+                                 hipStream_t st) {
   constexpr int J = NH >= 16 ? 128 / NH : 8;
   const int lpr = dh / J;
   const int grid = blocks_for(T, 4 * (64 / lpr));
   switch (lpr) {
 #define QR_CASE(L)                                                                             \
   case L:                                                                                      \
-    hipLaunchKernelGGL((k_heads_quant<NH, J, L>), dim3(grid), dim3(256), 0, st, x, T, ld, c, clip, \
-                       q, sc, z);                                                              \
+    hipLaunchKernelGGL((k_heads_quant<NH, J, L, Q8>), dim3(grid), dim3(256), 0, st, x, T, ld, c, \
+                       clip, bits, q, sc, z);                                                  \
     break;
     QR_CASE(4)
     QR_CASE(8)
@@ -272,6 +314,64 @@ static qr_status launch_heads_nh(int dh, const uint16_t* x, int64_t T, int64_t l
   return launch_status();
 }
 
+static qr_status rmsnorm_entry(const void* x_f16, int64_t T, int32_t d, int64_t ld_x, float eps,
+                               float clip_ratio, int bits, bool q8, void* q, void* scale_f16,
+                               float* r_dbg, hipStream_t stream) {
+  if (T < 0 || d <= 0 || ld_x < d) return QR_ERR_SHAPE;
+  if (!valid_clip(clip_ratio) || !(eps >= 0.0f) || !(eps <= 1.0f)) return QR_ERR_ARG;
+  if (q8 && (bits < 2 || bits > 8)) return QR_ERR_ARG;
+  if (d % 8 != 0 || d > 16384) return QR_ERR_UNSUPPORTED;
+  if (T == 0) return QR_OK;
+  if (!x_f16 || !q || !scale_f16) return QR_ERR_NULL;
+  if (ld_x % 8 != 0 || !aligned(x_f16, 16) || !aligned(q, q8 ? 8 : 4) || !aligned(scale_f16, 2) ||
+      (r_dbg && !aligned(r_dbg, 4)))
+    return QR_ERR_ALIGN;
+  const uint16_t* x = (const uint16_t*)x_f16;
+  return q8 ? launch_rms<true>(x, T, d, ld_x, eps, clip_ratio, bits, (uint8_t*)q,
+                               (uint16_t*)scale_f16, r_dbg, stream)
+            : launch_rms<false>(x, T, d, ld_x, eps, clip_ratio, 4, (uint8_t*)q,
+                                (uint16_t*)scale_f16, r_dbg, stream);
+}
+
+template <bool Q8>
+static qr_status heads_dispatch(int n_heads, int head_dim, const uint16_t* x, int64_t T, int64_t ld,
+                                float c, float clip, int bits, uint8_t* q, uint16_t* sc, float* z,
+                                hipStream_t st) {
+  switch (n_heads) {
+    case 2: return launch_heads_nh<2, Q8>(head_dim, x, T, ld, c, clip, bits, q, sc, z, st);
+    case 4: return launch_heads_nh<4, Q8>(head_dim, x, T, ld, c, clip, bits, q, sc, z, st);
+    case 8: return launch_heads_nh<8, Q8>(head_dim, x, T, ld, c, clip, bits, q, sc, z, st);
+    case 16: return launch_heads_nh<16, Q8>(head_dim, x, T, ld, c, clip, bits, q, sc, z, st);
+    case 32: return launch_heads_nh<32, Q8>(head_dim, x, T, ld, c, clip, bits, q, sc, z, st);
+    default: return launch_heads_nh<64, Q8>(head_dim, x, T, ld, c, clip, bits, q, sc, z, st);
+  }
+}
+
+static qr_status heads_entry(const void* x_f16, int64_t T, int32_t n_heads, int32_t head_dim,
+                             int64_t ld_x, float clip_ratio, int bits, bool q8, void* q,
+                             void* scale_f16, float* z_dbg, hipStream_t stream) {
+  if (T < 0 || n_heads <= 0 || head_dim <= 0) return QR_ERR_SHAPE;
+  const int64_t d = (int64_t)n_heads * head_dim;
+  if (ld_x < d) return QR_ERR_SHAPE;
+  if (!valid_clip(clip_ratio)) return QR_ERR_ARG;
+  if (q8 && (bits < 2 || bits > 8)) return QR_ERR_ARG;
+  const bool pow2 = !(n_heads & (n_heads - 1)) && !(head_dim & (head_dim - 1));
+  if (!pow2 || n_heads < 2 || n_heads > 64) return QR_ERR_UNSUPPORTED;
+  const int J = heads_j(n_heads);
+  if (head_dim < 4 * J || head_dim > 64 * J) return QR_ERR_UNSUPPORTED;
+  if (T == 0) return QR_OK;
+  if (!x_f16 || !q || !scale_f16) return QR_ERR_NULL;
+  if (ld_x % 8 != 0 || !aligned(x_f16, 16) || !aligned(q, q8 ? 8 : 4) || !aligned(scale_f16, 2) ||
+      (z_dbg && !aligned(z_dbg, 16)))
+    return QR_ERR_ALIGN;
+  const float c = norm_constant(n_heads);
+  const uint16_t* x = (const uint16_t*)x_f16;
+  return q8 ? heads_dispatch<true>(n_heads, head_dim, x, T, ld_x, c, clip_ratio, bits,
+                                   (uint8_t*)q, (uint16_t*)scale_f16, z_dbg, stream)
+            : heads_dispatch<false>(n_heads, head_dim, x, T, ld_x, c, clip_ratio, 4, (uint8_t*)q,
+                                    (uint16_t*)scale_f16, z_dbg, stream);
+}
+
 }  // namespace qr
 
 using namespace qr;
@@ -279,45 +379,29 @@ using namespace qr;
 extern "C" qr_status qr_rmsnorm_quant(const void* x_f16, int64_t T, int32_t d, int64_t ld_x,
                                       float eps, float clip_ratio, void* q_u8, void* scale_f16,
                                       float* r_dbg, hipStream_t stream) {
-  if (T < 0 || d <= 0 || ld_x < d) return QR_ERR_SHAPE;
-  if (!valid_clip(clip_ratio) || !(eps >= 0.0f) || !(eps <= 1.0f)) return QR_ERR_ARG;
-  if (d % 8 != 0 || d > 16384) return QR_ERR_UNSUPPORTED;
-  if (T == 0) return QR_OK;
-  if (!x_f16 || !q_u8 || !scale_f16) return QR_ERR_NULL;
-  if (ld_x % 8 != 0 || !aligned(x_f16, 16) || !aligned(q_u8, 4) || !aligned(scale_f16, 2) ||
-      (r_dbg && !aligned(r_dbg, 4)))
-    return QR_ERR_ALIGN;
-  return launch_rms((const uint16_t*)x_f16, T, d, ld_x, eps, clip_ratio, (uint8_t*)q_u8,
-                    (uint16_t*)scale_f16, r_dbg, stream);
+  return rmsnorm_entry(x_f16, T, d, ld_x, eps, clip_ratio, 4, false, q_u8, scale_f16, r_dbg,
+                       stream);
+}
+
+extern "C" qr_status qr_rmsnorm_quant_i8(const void* x_f16, int64_t T, int32_t d, int64_t ld_x,
+                                         float eps, float clip_ratio, int32_t bits, void* q_i8,
+                                         void* scale_f16, float* r_dbg, hipStream_t stream) {
+  return rmsnorm_entry(x_f16, T, d, ld_x, eps, clip_ratio, bits, true, q_i8, scale_f16, r_dbg,
+                       stream);
 }
 
 extern "C" qr_status qr_hadamard_heads_quant(const void* x_f16, int64_t T, int32_t n_heads,
                                              int32_t head_dim, int64_t ld_x, float clip_ratio,
                                              void* q_u8, void* scale_f16, float* z_dbg,
                                              hipStream_t stream) {
-  if (T < 0 || n_heads <= 0 || head_dim <= 0) return QR_ERR_SHAPE;
-  const int64_t d = (int64_t)n_heads * head_dim;
-  if (ld_x < d) return QR_ERR_SHAPE;
-  if (!valid_clip(clip_ratio)) return QR_ERR_ARG;
-  const bool pow2 = !(n_heads & (n_heads - 1)) && !(head_dim & (head_dim - 1));
-  if (!pow2 || n_heads < 2 || n_heads > 64) return QR_ERR_UNSUPPORTED;
-  const int J = heads_j(n_heads);
-  if (head_dim < 4 * J || head_dim > 64 * J) return QR_ERR_UNSUPPORTED;
-  if (T == 0) return QR_OK;
-  if (!x_f16 || !q_u8 || !scale_f16) return QR_ERR_NULL;
-  if (ld_x % 8 != 0 || !aligned(x_f16, 16) || !aligned(q_u8, 4) || !aligned(scale_f16, 2) ||
-      (z_dbg && !aligned(z_dbg, 16)))
-    return QR_ERR_ALIGN;
-  const float c = norm_constant(n_heads);
-  const uint16_t* x = (const uint16_t*)x_f16;
-  uint8_t* q = (uint8_t*)q_u8;
-  uint16_t* sc = (uint16_t*)scale_f16;
-  switch (n_heads) {
-    case 2: return launch_heads_nh<2>(head_dim, x, T, ld_x, c, clip_ratio, q, sc, z_dbg, stream);
-    case 4: return launch_heads_nh<4>(head_dim, x, T, ld_x, c, clip_ratio, q, sc, z_dbg, stream);
-    case 8: return launch_heads_nh<8>(head_dim, x, T, ld_x, c, clip_ratio, q, sc, z_dbg, stream);
-    case 16: return launch_heads_nh<16>(head_dim, x, T, ld_x, c, clip_ratio, q, sc, z_dbg, stream);
-    case 32: return launch_heads_nh<32>(head_dim, x, T, ld_x, c, clip_ratio, q, sc, z_dbg, stream);
-    default: return launch_heads_nh<64>(head_dim, x, T, ld_x, c, clip_ratio, q, sc, z_dbg, stream);
-  }
+  return heads_entry(x_f16, T, n_heads, head_dim, ld_x, clip_ratio, 4, false, q_u8, scale_f16,
+                     z_dbg, stream);
+}
+
+extern "C" qr_status qr_hadamard_heads_quant_i8(const void* x_f16, int64_t T, int32_t n_heads,
+                                                int32_t head_dim, int64_t ld_x, float clip_ratio,
+                                                int32_t bits, void* q_i8, void* scale_f16,
+                                                float* z_dbg, hipStream_t stream) {
+  return heads_entry(x_f16, T, n_heads, head_dim, ld_x, clip_ratio, bits, true, q_i8, scale_f16,
+                     z_dbg, stream);
 }

@@ -40,7 +40,8 @@ namespace qr {
 __constant__ HTable<28> g_h28 = make_h28();
 __constant__ HTable<172> g_h172 = make_h172();
 
-enum { MODE_QUANT = 0, MODE_ROT_F32 = 1, MODE_ROT_F16 = 2 };
+// MODE_QUANT8: b-bit codes stored one per byte (k_hq_lds only).
+enum { MODE_QUANT = 0, MODE_ROT_F32 = 1, MODE_ROT_F16 = 2, MODE_QUANT8 = 3 };
 
 // Sign-bit masks of 8 consecutive fp16 values from their 8 int8 signs (+1 or
 // -1; the int8 sign bit decides): dword j gets bit 15 if sign 2j is negative
@@ -501,7 +502,7 @@ template <int M, int MODE, bool CLAMP, bool ROT>
 __global__ __launch_bounds__(256) void k_hq_lds(const uint16_t* __restrict__ x, int64_t T, int d,
                                                 int n, int64_t ld,
                                                 const int8_t* __restrict__ signs, float c,
-                                                float clip, uint8_t* __restrict__ q,
+                                                float clip, int bits, uint8_t* __restrict__ q,
                                                 uint16_t* __restrict__ scale,
                                                 float* __restrict__ zdbg,
                                                 void* __restrict__ yout) {
@@ -576,7 +577,7 @@ __global__ __launch_bounds__(256) void k_hq_lds(const uint16_t* __restrict__ x, 
     if (zdbg) {
       for (int i = tid; i < d; i += 256) zdbg[row * d + i] = buf[pad(i)];
     }
-    if (MODE == MODE_QUANT) {
+    if (MODE == MODE_QUANT || MODE == MODE_QUANT8) {
       // 4. amax over the row
       float am = 0.0f;
       for (int i = tid; i < d; i += 256) am = fmaxf(am, fabsf(buf[pad(i)]));
@@ -584,9 +585,10 @@ __global__ __launch_bounds__(256) void k_hq_lds(const uint16_t* __restrict__ x, 
       if ((tid & 63) == 0) red[tid >> 6] = am;
       __syncthreads();
       am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      const QRange rg = q_range(MODE == MODE_QUANT8 ? bits : 4);
       uint16_t sh;
       float m;
-      sym_scale(am, c, clip, &sh, &m);
+      sym_scale(am, c, clip, &sh, &m, rg.qmax);
       sh = (uint16_t)__builtin_amdgcn_readfirstlane(sh);  // the same on every lane
       // 5. quantize + pack, 8 elements per thread and step
       const bool clamp = CLAMP || (sh & 0x7fffu) < 0x0400u;  // block-uniform
@@ -594,8 +596,16 @@ __global__ __launch_bounds__(256) void k_hq_lds(const uint16_t* __restrict__ x, 
         float v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = buf[pad(i + j)];
-        *(uint32_t*)(q + row * (d / 2) + i / 2) =
-            clamp ? quant_pack8<true>(v, m) : quant_pack8<false>(v, m);
+        if (MODE == MODE_QUANT8) {
+          *(uint2*)(q + row * d + i) =
+              clamp ? make_uint2(quant_pack4_i8<true>(v, m, rg.lo, rg.hi),
+                                 quant_pack4_i8<true>(v + 4, m, rg.lo, rg.hi))
+                    : make_uint2(quant_pack4_i8<false>(v, m, rg.lo, rg.hi),
+                                 quant_pack4_i8<false>(v + 4, m, rg.lo, rg.hi));
+        } else {
+          *(uint32_t*)(q + row * (d / 2) + i / 2) =
+              clamp ? quant_pack8<true>(v, m) : quant_pack8<false>(v, m);
+        }
       }
       if (tid == 0) scale[row] = sh;
     } else if (MODE == MODE_ROT_F32) {
@@ -1490,7 +1500,7 @@ static qr_status launch_small(int d, int rot, const uint16_t* x, int64_t T, int6
 template <int M, int MODE, bool CLAMP, bool ROT>
 static qr_status launch_lds_t(int d, int n, const uint16_t* x, int64_t T, int64_t ld,
                               const int8_t* s, float c, float clip, uint8_t* q, uint16_t* sc,
-                              float* z, void* y, hipStream_t st) {
+                              float* z, void* y, hipStream_t st, int bits = 4) {
   const int plen = (d + (d >> 5)) + 1;
   const size_t bytes = ((size_t)((M == 172 && ROT) ? 2 : 1) * plen + 8) * sizeof(float);
   if (bytes > 160 * 1024) return QR_ERR_UNSUPPORTED;
@@ -1500,8 +1510,8 @@ static qr_status launch_lds_t(int d, int n, const uint16_t* x, int64_t T, int64_
                           (int)bytes) != hipSuccess)
     return QR_ERR_LAUNCH;
   const int grid = grid_for(T, 1, 2048);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), bytes, st, x, T, d, n, ld, s, c, clip, q, sc, z,
-                     y);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), bytes, st, x, T, d, n, ld, s, c, clip, bits, q,
+                     sc, z, y);
   return launch_status();
 }
 
@@ -1552,9 +1562,57 @@ static qr_status dispatch(const void* x_f16, int64_t T, int32_t d, int64_t ld, i
   return launch_lds_t<172, MODE, CLAMP, true>(d, n, x, T, ld, signs, c, clip, qq, ss, z, y, st);
 }
 
+// b-bit codes one per byte: every width through the LDS-staged kernel.
+template <bool CLAMP>
+static qr_status dispatch_q8(const uint16_t* x, int64_t T, int32_t d, int64_t ld, int rot,
+                             const int8_t* signs, float clip, int bits, uint8_t* q, uint16_t* sc,
+                             float* z, hipStream_t st) {
+  if (!rot)
+    return launch_lds_t<1, MODE_QUANT8, CLAMP, false>(d, 0, x, T, ld, signs, 1.0f, clip, q, sc, z,
+                                                      nullptr, st, bits);
+  int n = 0, m = 0;
+  if (!factor_width(d, &n, &m)) return QR_ERR_UNSUPPORTED;
+  const float c = norm_constant(d);
+  if (m == 1)
+    return launch_lds_t<1, MODE_QUANT8, CLAMP, true>(d, n, x, T, ld, signs, c, clip, q, sc, z,
+                                                     nullptr, st, bits);
+  if (m == 28)
+    return launch_lds_t<28, MODE_QUANT8, CLAMP, true>(d, n, x, T, ld, signs, c, clip, q, sc, z,
+                                                      nullptr, st, bits);
+  return launch_lds_t<172, MODE_QUANT8, CLAMP, true>(d, n, x, T, ld, signs, c, clip, q, sc, z,
+                                                     nullptr, st, bits);
+}
+
 }  // namespace qr
 
 using namespace qr;
+
+extern "C" qr_status qr_hadamard_quant_i8(const void* x_f16, int64_t T, int32_t d, int64_t ld_x,
+                                          qr_rot rot, const int8_t* signs, float clip_ratio,
+                                          int32_t bits, void* q_i8, void* scale_f16, float* z_dbg,
+                                          hipStream_t stream) {
+  if (T < 0 || d <= 0 || ld_x < d) return QR_ERR_SHAPE;
+  if (rot != QR_ROT_NONE && rot != QR_ROT_HADAMARD) return QR_ERR_ARG;
+  if (!valid_clip(clip_ratio) || bits < 2 || bits > 8) return QR_ERR_ARG;
+  int n = 0, m = 0;
+  if (rot != QR_ROT_NONE) {
+    if (!factor_width(d, &n, &m)) return QR_ERR_UNSUPPORTED;
+  } else if (d % 8 != 0 || d > 32768) {
+    return QR_ERR_UNSUPPORTED;
+  }
+  if (T == 0) return QR_OK;
+  if (!x_f16 || !q_i8 || !scale_f16) return QR_ERR_NULL;
+  if (ld_x % 8 != 0 || !aligned(x_f16, 16) || !aligned(q_i8, 8) || !aligned(scale_f16, 2) ||
+      (z_dbg && !aligned(z_dbg, 16)) || (signs && !aligned(signs, 4)))
+    return QR_ERR_ALIGN;
+  const int r = rot == QR_ROT_HADAMARD ? 1 : 0;
+  const uint16_t* x = (const uint16_t*)x_f16;
+  if (clip_ratio < 1.0f)
+    return dispatch_q8<true>(x, T, d, ld_x, r, signs, clip_ratio, bits, (uint8_t*)q_i8,
+                             (uint16_t*)scale_f16, z_dbg, stream);
+  return dispatch_q8<false>(x, T, d, ld_x, r, signs, clip_ratio, bits, (uint8_t*)q_i8,
+                            (uint16_t*)scale_f16, z_dbg, stream);
+}
 
 extern "C" qr_status qr_hadamard_quant(const void* x_f16, int64_t T, int32_t d, int64_t ld_x,
                                        qr_rot rot, const int8_t* signs, float clip_ratio,

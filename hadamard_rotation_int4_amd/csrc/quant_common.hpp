@@ -15,11 +15,12 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Per-row scale recipe (identical for every kernel): returns the fp16 scale
-// bits and the multiplier m = c * (1 / s_h) (0 if s_h == 0).
+// bits and the multiplier m = c * (1 / s_h) (0 if s_h == 0).  qmax is the
+// largest code: 7 for INT4, 2^(b-1) - 1 for b-bit codes.
 __device__ __forceinline__ void sym_scale(float amax_z, float c, float clip, uint16_t* sh_out,
-                                          float* m_out) {
+                                          float* m_out, float qmax = 7.0f) {
   const float a = __fmul_rn(amax_z, c);
-  const float s = __fdiv_rn(__fmul_rn(clip, a), 7.0f);
+  const float s = __fdiv_rn(__fmul_rn(clip, a), qmax);
   const uint16_t sh = f2h(s);
   const float shf = h2f(sh);
   const float inv = shf > 0.0f ? __fdiv_rn(1.0f, shf) : 0.0f;
@@ -48,6 +49,36 @@ __device__ __forceinline__ uint32_t quant_pack8(const float* v, float m) {
   return lo ^ hi ^ 0x88888888u;  // offset binary -> two's complement nibbles
 }
 
+// b-bit codes stored one per byte (b <= 8; QuaRot paper, 6- and 8-bit RTN):
+// fma(v, m, kMagic) = kMagic + rne(v m), whose low byte is the two's-complement
+// code; the clamp to [lo, hi] = [-2^(b-1), 2^(b-1) - 1] is a med3 on the same
+// biased values.  Four codes per dword, code j in byte j.
+template <bool CLAMP>
+__device__ __forceinline__ uint32_t q8_word(float v, float m, float lo, float hi) {
+  float t = fmaf(v, m, kMagic);
+  if (CLAMP) t = __builtin_amdgcn_fmed3f(t, kMagic + lo, kMagic + hi);
+  return __float_as_uint(t);
+}
+template <bool CLAMP>
+__device__ __forceinline__ uint32_t quant_pack4_i8(const float* v, float m, float lo, float hi) {
+  const uint32_t f0 = q8_word<CLAMP>(v[0], m, lo, hi), f1 = q8_word<CLAMP>(v[1], m, lo, hi);
+  const uint32_t f2 = q8_word<CLAMP>(v[2], m, lo, hi), f3 = q8_word<CLAMP>(v[3], m, lo, hi);
+  return __builtin_amdgcn_perm(f1, f0, 0x0c0c0400u) | __builtin_amdgcn_perm(f3, f2, 0x04000c0cu);
+}
+template <bool CLAMP>
+__device__ __forceinline__ uint32_t quant_pack2_i8(const float* v, float m, float lo, float hi) {
+  const uint32_t f0 = q8_word<CLAMP>(v[0], m, lo, hi), f1 = q8_word<CLAMP>(v[1], m, lo, hi);
+  return __builtin_amdgcn_perm(f1, f0, 0x0c0c0400u);
+}
+// Code range of b-bit symmetric codes as the floats the packers take.
+struct QRange {
+  float qmax, lo, hi;
+};
+__host__ __device__ inline QRange q_range(int bits) {
+  const int h = 1 << (bits - 1);
+  return QRange{(float)(h - 1), (float)(-h), (float)(h - 1)};
+}
+
 // Streaming accesses: every input row is read once and every output written
 // once, so both bypass cache retention (non-temporal).
 #ifndef QR_NT
@@ -59,6 +90,12 @@ __device__ __forceinline__ v4u ld_stream(const uint16_t* p) {
 __device__ __forceinline__ void st_stream(uint32_t* p, uint32_t v) {
   if (QR_NT) __builtin_nontemporal_store(v, p);
   else *p = v;
+}
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_stream8(void* p, uint32_t lo, uint32_t hi) {
+  const v2u v = {lo, hi};
+  if (QR_NT) __builtin_nontemporal_store(v, (v2u*)p);
+  else *(v2u*)p = v;
 }
 
 }  // namespace qr

@@ -15,6 +15,9 @@
 //    A and W use the same permutation of k, so the dot product is unchanged,
 //    and the int32 accumulator holds 256 * acc exactly (|256 acc| <= 256 * 64 * K
 //    < 2^31 for K <= 131008); the epilogue shifts it back.
+//  * qr_w8a8_gemm (QuaRot paper, 6- and 8-bit RTN results) runs the same
+//    kernel on codes stored one per byte: chunks go to the matrix cores as
+//    loaded, one per MFMA step, and a K step covers 128 elements.
 //  * Tiles: (64 WM) x (64 WN) outputs per workgroup of 4 wavefronts (one per
 //    SIMD, 2 x 2), each owning a (32 WM) x (32 WN) block = WM x WN MFMA tiles
 //    whose accumulators live in the AGPR half of the register file.  256 x 256
@@ -44,9 +47,16 @@
 
 namespace qr {
 
-constexpr int BK = 256;            // K step in int4 elements (128 bytes per row)
-constexpr int KCH = BK / 32;       // 16-byte k-chunks per row and step
+constexpr int KCH = 8;             // 16-byte k-chunks per row and step
 constexpr int GEMM_THREADS = 256;
+// Codes per 16-byte chunk and per K step for BITS = 4 (packed) or 8 (one per byte).
+template <int BITS>
+struct CodeFmt {
+  static constexpr int EPC = 128 / BITS;     // elements per 16-byte chunk: 32 or 16
+  static constexpr int BKE = KCH * EPC;      // elements per K step: 256 or 128
+  static constexpr int FR = BITS == 4 ? 1 : 2;  // chunks per lane and MFMA pair
+  static constexpr int SHIFT = BITS == 4 ? 8 : 0;  // the int4 accumulator holds 256 * acc
+};
 
 __device__ __forceinline__ v4i unpack16(uint2 d) {
   v4i r;
@@ -64,25 +74,31 @@ __device__ __forceinline__ int lds_off(int kk, int r) {
   return kk * (ROWS * 16) + ((r ^ f) << 4);
 }
 
-template <int WM, int WN>
+template <int WM, int WN, int BITS = 4>
 struct GemmTile {
   static constexpr int BM = 64 * WM, BN = 64 * WN;
-  static constexpr int A_BYTES = BM * BK / 2, W_BYTES = BN * BK / 2;
+  static constexpr int A_BYTES = BM * KCH * 16, W_BYTES = BN * KCH * 16;
   static constexpr int STAGE = A_BYTES + W_BYTES;
   static constexpr int LDS = 2 * STAGE;
   static constexpr int PA = BM * KCH / GEMM_THREADS, PW = BN * KCH / GEMM_THREADS;
   static constexpr int MF = WM * WN;                      // MFMAs per half step
-  static constexpr int VPM = (6 * (WM + WN) + MF - 1) / MF;  // unpack VALU per MFMA
-  static constexpr int DSR = WM + WN;                     // fragment reads per pair
+  // unpack VALU per MFMA (int8 operands go to the matrix cores as loaded)
+  static constexpr int VPM = BITS == 4 ? (6 * (WM + WN) + MF - 1) / MF : 1;
+  static constexpr int DSR = (WM + WN) * CodeFmt<BITS>::FR;  // fragment reads per pair
   static constexpr int SPM = (PA + PW + MF - 1) / MF;     // staging writes/loads per MFMA
 };
 
-template <int WM, int WN, bool DBG, bool KTAIL>
+// BITS = 4: packed INT4 operands (K/2 bytes per row), unpacked in registers.
+// BITS = 8: codes stored one per byte (K bytes per row, b <= 8 bits), fed to
+// the matrix cores as loaded; the LDS geometry (128 bytes per row and step)
+// is the same, so a K step covers 128 instead of 256 elements.
+template <int WM, int WN, bool DBG, bool KTAIL, int BITS = 4>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
     const uint8_t* __restrict__ A, const uint16_t* __restrict__ a_scale, int T,
     const uint8_t* __restrict__ W, const uint16_t* __restrict__ w_scale, int N, int K,
     uint16_t* __restrict__ Y, int32_t* __restrict__ acc_dbg, int tiles_m, int tiles_n) {
-  using Tl = GemmTile<WM, WN>;
+  using Tl = GemmTile<WM, WN, BITS>;
+  using CF = CodeFmt<BITS>;
   constexpr int BM = Tl::BM, BN = Tl::BN;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -104,7 +120,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
   const int wave = tid >> 6;
   const int wm = (wave >> 1) * (32 * WM), wn = (wave & 1) * (32 * WN);  // wave's block
   const int li = lane & 31, lg = lane >> 5;  // MFMA row/col lane, k-half
-  const int64_t rowbytes = K / 2;
+  const int64_t rowbytes = (int64_t)K * BITS / 8;
 
   // ---- global -> register staging: 16-byte pieces, row = (tid >> 3) + 32 j,
   //      k-chunk = tid & 7 (fixed per thread).  Raw buffer loads over the tile's
@@ -126,12 +142,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
 #pragma unroll
     for (int j = 0; j < Tl::PA; ++j)
       ra[j] = __builtin_bit_cast(
-          v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff + j * rstep + k0 / 2, 0, 0));
+          v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff + j * rstep + k0 * BITS / 8, 0, 0));
 #pragma unroll
     for (int j = 0; j < Tl::PW; ++j)
       rw[j] = __builtin_bit_cast(
-          v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_w, voff + j * rstep + k0 / 2, 0, 0));
-    if (KTAIL && last && k0 + st_kk * 32 >= K) {  // chunk past K (K is a multiple of 32)
+          v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_w, voff + j * rstep + k0 * BITS / 8, 0, 0));
+    if (KTAIL && last && k0 + st_kk * CF::EPC >= K) {  // chunk past K (K is a multiple of EPC)
 #pragma unroll
       for (int j = 0; j < Tl::PA; ++j) ra[j] = v4u{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -146,16 +162,22 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
 #pragma unroll
     for (int j = 0; j < Tl::PW; ++j) *(v4u*)(pw + lds_off<BN>(st_kk, st_r0 + 32 * j)) = rw[j];
   };
-  // packed fragments of chunk pair p (lane takes chunk 2p + lg): WM of A
-  // (rows wm + 32 i + li) and WN of W
-  auto lread = [&](int stage, int p, v4u* fa, v4u* fb) {
+  // fragments of chunk pair p: WM of A (rows wm + 32 i + li) and WN of W.
+  // INT4: the lane takes chunk 2p + lg, both halves of which feed the pair's
+  // two MFMA steps; int8: chunks 4p + 2e + lg, one per MFMA step e.
+  auto lread = [&](int stage, int p, v4u (*fa)[WM], v4u (*fb)[WN]) {
     const uint8_t* pa = smem + stage * Tl::STAGE;
     const uint8_t* pw = pa + Tl::A_BYTES;
-    const int kk = 2 * p + lg;
 #pragma unroll
-    for (int i = 0; i < WM; ++i) fa[i] = *(const v4u*)(pa + lds_off<BM>(kk, wm + i * 32 + li));
+    for (int f = 0; f < CF::FR; ++f) {
+      const int kk = BITS == 4 ? 2 * p + lg : 4 * p + 2 * f + lg;
 #pragma unroll
-    for (int j = 0; j < WN; ++j) fb[j] = *(const v4u*)(pw + lds_off<BN>(kk, wn + j * 32 + li));
+      for (int i = 0; i < WM; ++i)
+        fa[f][i] = *(const v4u*)(pa + lds_off<BM>(kk, wm + i * 32 + li));
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+        fb[f][j] = *(const v4u*)(pw + lds_off<BN>(kk, wn + j * 32 + li));
+    }
   };
 
   v16i acc[WM][WN];
@@ -170,13 +192,22 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
   // ahead), unpacked halves ua/ub[0] (e = 0) and [1] (e = 1).  While the MFMAs
   // of one half run, the VALU unpacks the other and the LDS reads of the next
   // pair are in flight; sched_group_barrier pins that order.
-  v4u fa[2][WM], fb[2][WN];
+  v4u fa[2][CF::FR][WM], fb[2][CF::FR][WN];
   v4i ua[2][WM], ub[2][WN];
-  auto unpack_half = [&](const v4u* xa, const v4u* xb, int e, v4i* oa, v4i* ob) {
+  auto unpack_half = [&](const v4u (*xa)[WM], const v4u (*xb)[WN], int e, v4i* oa, v4i* ob) {
+    if constexpr (BITS == 4) {
 #pragma unroll
-    for (int i = 0; i < WM; ++i) oa[i] = unpack16(make_uint2(xa[i][2 * e], xa[i][2 * e + 1]));
+      for (int i = 0; i < WM; ++i)
+        oa[i] = unpack16(make_uint2(xa[0][i][2 * e], xa[0][i][2 * e + 1]));
 #pragma unroll
-    for (int j = 0; j < WN; ++j) ob[j] = unpack16(make_uint2(xb[j][2 * e], xb[j][2 * e + 1]));
+      for (int j = 0; j < WN; ++j)
+        ob[j] = unpack16(make_uint2(xb[0][j][2 * e], xb[0][j][2 * e + 1]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < WM; ++i) oa[i] = __builtin_bit_cast(v4i, xa[e][i]);
+#pragma unroll
+      for (int j = 0; j < WN; ++j) ob[j] = __builtin_bit_cast(v4i, xb[e][j]);
+    }
   };
   auto mfma_half = [&](const v4i* a, const v4i* b) {
 #pragma unroll
@@ -185,8 +216,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
       for (int j = 0; j < WN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
   };
-  constexpr int NP = KCH / 2;  // chunk pairs per step
-  const int ksteps = (K + BK - 1) / BK;
+  constexpr int NP = BITS == 4 ? KCH / 2 : KCH / 4;  // MFMA pairs per step
+  const int ksteps = (K + CF::BKE - 1) / CF::BKE;
   // One K step from LDS stage `stage`.  MORE: a next step exists -- stage its
   // panels (loaded one step earlier) into the other LDS stage during the last
   // half-step, fetch the step after it, and start reading the other stage.
@@ -221,7 +252,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
         unpack_half(fa[cur], fb[cur], 1, ua[1], ub[1]);
         if (MORE) {
           lstore(stage ^ 1);
-          gload(min(ks + 2, ksteps - 1) * BK, ks + 3 >= ksteps);
+          gload(min(ks + 2, ksteps - 1) * CF::BKE, ks + 3 >= ksteps);
 #pragma unroll
           for (int m = 0; m < Tl::MF; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
@@ -251,7 +282,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
   gload(0, ksteps == 1);
   lstore(0);
   __syncthreads();
-  gload(min(1, ksteps - 1) * BK, ksteps <= 2);
+  gload(min(1, ksteps - 1) * CF::BKE, ksteps <= 2);
   lread(0, 0, fa[0], fb[0]);
   unpack_half(fa[0], fb[0], 0, ua[0], ub[0]);
   for (int ks = 0; ks + 1 < ksteps; ++ks) kstep(ks & 1, ks, std::true_type{});
@@ -279,7 +310,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
       for (int r = 0; r < 16; ++r) {
         const int t = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
         if (t < T) {
-          const int32_t a = acc[i][j][r] >> 8;  // exact: the accumulator is 256 * acc
+          const int32_t a = acc[i][j][r] >> CF::SHIFT;  // exact (INT4: 256 * acc)
           Y[(int64_t)t * N + n] = f2h(__fmul_rn(__fmul_rn((float)a, asc[r]), wsc[j]));
           if (DBG) acc_dbg[(int64_t)t * N + n] = a;
         }
@@ -288,12 +319,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
   }
 }
 
-template <int WM, int WN, bool DBG, bool KTAIL>
+template <int WM, int WN, bool DBG, bool KTAIL, int BITS>
 static qr_status launch_gemm(const void* a_q, const void* a_scale, int64_t T, const void* w_q,
                              const void* w_scale, int64_t N, int64_t K, void* y, int32_t* acc,
                              hipStream_t stream) {
-  using Tl = GemmTile<WM, WN>;
-  auto kern = k_w4a4_gemm<WM, WN, DBG, KTAIL>;
+  using Tl = GemmTile<WM, WN, BITS>;
+  auto kern = k_w4a4_gemm<WM, WN, DBG, KTAIL, BITS>;
   // Opting in to more than 64 KB of LDS is a per-kernel attribute; setting it
   // again on every call is cheap and keeps the entry point free of state.
   if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -310,16 +341,16 @@ static qr_status launch_gemm(const void* a_q, const void* a_scale, int64_t T, co
   return launch_status();
 }
 
-template <int WM, int WN>
+template <int WM, int WN, int BITS = 4>
 static qr_status launch_tile(const void* a_q, const void* a_scale, int64_t T, const void* w_q,
                              const void* w_scale, int64_t N, int64_t K, void* y, int32_t* acc,
                              hipStream_t stream) {
-  const bool tail = (K % BK) != 0;
+  const bool tail = (K % CodeFmt<BITS>::BKE) != 0;
   if (acc)
-    return tail ? launch_gemm<WM, WN, true, true>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream)
-                : launch_gemm<WM, WN, true, false>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
-  return tail ? launch_gemm<WM, WN, false, true>(a_q, a_scale, T, w_q, w_scale, N, K, y, nullptr, stream)
-              : launch_gemm<WM, WN, false, false>(a_q, a_scale, T, w_q, w_scale, N, K, y, nullptr, stream);
+    return tail ? launch_gemm<WM, WN, true, true, BITS>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream)
+                : launch_gemm<WM, WN, true, false, BITS>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
+  return tail ? launch_gemm<WM, WN, false, true, BITS>(a_q, a_scale, T, w_q, w_scale, N, K, y, nullptr, stream)
+              : launch_gemm<WM, WN, false, false, BITS>(a_q, a_scale, T, w_q, w_scale, N, K, y, nullptr, stream);
 }
 
 // Fraction of the machine's workgroup slots a tile grid keeps busy, times a
@@ -572,4 +603,27 @@ extern "C" qr_status qr_w4a4_gemm(const void* a_q, const void* a_scale_f16, int6
   if (s42 >= s24)
     return launch_tile<4, 2>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
   return launch_tile<2, 4>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
+}
+
+extern "C" qr_status qr_w8a8_gemm(const void* a_q, const void* a_scale_f16, int64_t T,
+                                  const void* w_q, const void* w_scale_f16, int64_t N, int64_t K,
+                                  void* y_f16, int32_t* acc_dbg, hipStream_t stream) {
+  if (T < 0 || N < 0 || K <= 0) return QR_ERR_SHAPE;
+  if (K % 16 != 0 || K > 131008) return QR_ERR_UNSUPPORTED;
+  if (T > INT32_MAX / 2 || N > INT32_MAX / 2) return QR_ERR_SHAPE;
+  if (T == 0 || N == 0) return QR_OK;
+  if (!a_q || !a_scale_f16 || !w_q || !w_scale_f16 || !y_f16) return QR_ERR_NULL;
+  if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(y_f16, 4) || !aligned(a_scale_f16, 2) ||
+      !aligned(w_scale_f16, 2) || (acc_dbg && !aligned(acc_dbg, 4)))
+    return QR_ERR_ALIGN;
+  // no weight-streaming kernel for this format: every T goes through the tiles
+  constexpr int kSlots = 256;
+  const double s44 = tile_score(T, N, 256, 256, 1.0, kSlots);
+  const double s42 = tile_score(T, N, 256, 128, 0.9, kSlots);
+  const double s24 = tile_score(T, N, 128, 256, 0.9, kSlots);
+  if (s44 >= s42 && s44 >= s24)
+    return launch_tile<4, 4, 8>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
+  if (s42 >= s24)
+    return launch_tile<4, 2, 8>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
+  return launch_tile<2, 4, 8>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
 }

@@ -214,6 +214,46 @@ qr_status qr_w4a4_gemm(const void* a_q, const void* a_scale_f16, int64_t T, cons
                        int32_t* acc_dbg, hipStream_t stream);
 
 /*
+ * b-bit variants (QuaRot paper: round-to-nearest 6- and 8-bit weights and
+ * activations are lossless, Table 9).  Codes are symmetric b-bit integers,
+ * 2 <= bits <= 8, stored one per byte (int8, two's complement):
+ *   scale = fp16(clip * max|y| / qmax), qmax = 2^(bits-1) - 1,
+ *   q = clamp(rne(y / scale), -2^(bits-1), qmax), q = 0 if scale == 0,
+ * with the fp32 recipe of the INT4 entry points and 7 replaced by qmax.
+ *   qr_hadamard_quant_i8: as qr_hadamard_quant (QR_ROT_NONE or
+ *     QR_ROT_HADAMARD, the same widths), q_i8 [T, d]; every width runs the
+ *     LDS-staged kernel (one workgroup per row).
+ *   qr_rmsnorm_quant_i8, qr_hadamard_heads_quant_i8: as their INT4 versions,
+ *     q_i8 [T, d].
+ * Requirements as the INT4 versions, with q_i8 8-byte aligned.
+ */
+qr_status qr_hadamard_quant_i8(const void* x_f16, int64_t T, int32_t d, int64_t ld_x, qr_rot rot,
+                               const int8_t* signs, float clip_ratio, int32_t bits, void* q_i8,
+                               void* scale_f16, float* z_dbg, hipStream_t stream);
+qr_status qr_rmsnorm_quant_i8(const void* x_f16, int64_t T, int32_t d, int64_t ld_x, float eps,
+                              float clip_ratio, int32_t bits, void* q_i8, void* scale_f16,
+                              float* r_dbg, hipStream_t stream);
+qr_status qr_hadamard_heads_quant_i8(const void* x_f16, int64_t T, int32_t n_heads,
+                                     int32_t head_dim, int64_t ld_x, float clip_ratio,
+                                     int32_t bits, void* q_i8, void* scale_f16, float* z_dbg,
+                                     hipStream_t stream);
+
+/*
+ * GEMM on codes stored one per byte (b <= 8 bits, for example the outputs of
+ * the _i8 quantizers above), with the epilogue of qr_w4a4_gemm:
+ *   acc[t, n] = sum_k A[t, k] W[n, k]   (int32, exact: |acc| <= 2^14 K < 2^31),
+ *   Y[t, n]   = fp16(fp32(fp32(acc) * a_scale[t]) * w_scale[n]); fp32(acc)
+ *               rounds to nearest even once |acc| > 2^24.
+ *   a_q [T, K] int8, w_q [N, K] int8 (row-major, contiguous); a_scale [T],
+ *   w_scale [N] fp16; y_f16 [T, N] fp16; acc_dbg NULL or [T, N] int32.
+ * Requirements: T, N >= 0; K > 0, K % 16 == 0, K <= 131008; a_q and w_q
+ * 16-byte aligned; y_f16 and acc_dbg 4-byte aligned.
+ */
+qr_status qr_w8a8_gemm(const void* a_q, const void* a_scale_f16, int64_t T, const void* w_q,
+                       const void* w_scale_f16, int64_t N, int64_t K, void* y_f16,
+                       int32_t* acc_dbg, hipStream_t stream);
+
+/*
  * Head-wise rotation + asymmetric 4-bit group quantization of new K or V
  * tokens, written into a packed cache (Init: start_pos = 0, S_new = prompt
  * length; Append: S_new = 1 at the next position).

@@ -33,7 +33,8 @@ def test_header_declares_the_path():
     names = declared_functions()
     for must in ("qr_hadamard_quant", "qr_hadamard", "qr_w4a4_gemm", "qr_kv_rotate_quant",
                  "qr_kv_decode_attention", "qr_kv_decode_workspace_bytes",
-                 "qr_rmsnorm_quant", "qr_hadamard_heads_quant",
+                 "qr_rmsnorm_quant", "qr_hadamard_heads_quant", "qr_hadamard_quant_i8",
+                 "qr_rmsnorm_quant_i8", "qr_hadamard_heads_quant_i8", "qr_w8a8_gemm",
                  "qr_hadamard_factor", "qr_status_str", "qr_abi_version"):
         assert must in names
 
@@ -221,6 +222,38 @@ def test_hadamard_heads_quant_validation(lib):
     assert hh(lib, x=A16 + 2) == QR_ERR_ALIGN
     assert hh(lib, ld=8196) == QR_ERR_ALIGN
     assert hh(lib, z=A16 + 4) == QR_ERR_ALIGN
+
+
+def test_i8_quantizers_validation(lib):
+    A8 = A16 + 8  # 8-byte but not 16-byte aligned: fine for int8 codes, not for x
+    f = lib.qr_hadamard_quant_i8
+    assert f(A16, 0, 8192, 8192, 1, None, 1.0, 8, A16, A16, None, None) == QR_OK
+    assert f(A16, 0, 28672, 28672, 1, None, 1.0, 6, A16, A16, None, None) == QR_OK
+    assert f(A16, 4, 8192, 8192, 2, None, 1.0, 8, A16, A16, None, None) == QR_ERR_ARG  # no fp16 transform
+    assert f(A16, 4, 8192, 8192, 1, None, 1.0, 9, A16, A16, None, None) == QR_ERR_ARG
+    assert f(A16, 4, 8192, 8192, 1, None, 1.0, 1, A16, A16, None, None) == QR_ERR_ARG
+    assert f(A16, 4, 4100, 4104, 1, None, 1.0, 8, A16, A16, None, None) == QR_ERR_UNSUPPORTED
+    assert f(A16, 4, 8192, 8192, 1, None, 1.0, 8, A16 + 4, A16, None, None) == QR_ERR_ALIGN
+    assert f(None, 4, 8192, 8192, 1, None, 1.0, 8, A16, A16, None, None) == QR_ERR_NULL
+    g = lib.qr_rmsnorm_quant_i8
+    assert g(A16, 0, 8192, 8192, 1e-5, 1.0, 8, A8, A16, None, None) == QR_OK
+    assert g(A16, 4, 8192, 8192, 1e-5, 1.0, 0, A8, A16, None, None) == QR_ERR_ARG
+    assert g(A16, 4, 8192, 8192, 1e-5, 1.0, 8, A16 + 4, A16, None, None) == QR_ERR_ALIGN
+    h = lib.qr_hadamard_heads_quant_i8
+    assert h(A16, 0, 64, 128, 8192, 1.0, 6, A8, A16, None, None) == QR_OK
+    assert h(A16, 4, 64, 128, 8192, 1.0, 12, A8, A16, None, None) == QR_ERR_ARG
+    assert h(A16, 4, 48, 128, 6144, 1.0, 8, A8, A16, None, None) == QR_ERR_UNSUPPORTED
+
+
+def test_w8a8_gemm_validation(lib):
+    f = lib.qr_w8a8_gemm
+    assert f(A16, A16, 0, A16, A16, 16, 4096, A16, None, None) == QR_OK
+    assert f(A16, A16, 16, A16, A16, 0, 4112, A16, None, None) == QR_OK
+    assert f(A16, A16, 16, A16, A16, 16, 4100, A16, None, None) == QR_ERR_UNSUPPORTED  # K % 16
+    assert f(A16, A16, 16, A16, A16, 16, 131024, A16, None, None) == QR_ERR_UNSUPPORTED
+    assert f(A16, A16, -1, A16, A16, 16, 4096, A16, None, None) == QR_ERR_SHAPE
+    assert f(None, A16, 16, A16, A16, 16, 4096, A16, None, None) == QR_ERR_NULL
+    assert f(A16 + 8, A16, 16, A16, A16, 16, 4096, A16, None, None) == QR_ERR_ALIGN
 
 
 def test_binding_refuses_cpu_tensors():
