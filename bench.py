@@ -1,7 +1,8 @@
 """Benchmark of the QuaRot online-rotation + INT4 hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload 70b_prefill|7b_prefill|7b_decode|70b_kv|70b_block|7b_block]
+                    [--workload 70b_prefill|7b_prefill|7b_decode|70b_kv|70b_block|7b_block|
+                                70b_block_w8a8|7b_block_w8a8]
                     [--no-cpu-baseline] [--copy-calibration] [--fp16-hadamard]
 
 One step is one pass of the whole hot path over one batch of synthetic input
@@ -21,7 +22,8 @@ One step is one pass of the whole hot path over one batch of synthetic input
   QKV and of gate/up, the Hadamard-heads transform + INT4 in front of O, the
   full online Hadamard + INT4 only in front of down.  The same five GEMMs in
   fp16 (torch.matmul) are timed separately as context: the pages' speedups
-  are against an FP16 block.
+  are against an FP16 block.  The _w8a8 forms run the same online path with
+  8-bit codes one per byte and the W8A8 GEMM (the pages' 8-bit RTN setting).
 * 7b_decode: the same four rotations and five GEMMs at T = 1, 8, 32 and 64.
 * 70b_kv: K/V Init of a 32 x 2048-token prompt (8 KV heads of 128), the
   rotation of its queries (64 heads), then 50 decode steps of Append K, V,
@@ -62,7 +64,9 @@ CSRC = ROOT / "hadamard_rotation_int4_amd" / "csrc"
 KERNEL_SOURCE = {"w4a4_gemm": "w4a4_gemm.hip", "hadamard_quant": "hadamard_quant.hip",
                  "kv_rotate_quant": "kv_quant.hip", "hadamard": "hadamard_quant.hip",
                  "kv_decode_attention": "kv_decode.hip", "rmsnorm_quant": "block_quant.hip",
-                 "hadamard_heads_quant": "block_quant.hip"}
+                 "hadamard_heads_quant": "block_quant.hip", "w8a8_gemm": "w4a4_gemm.hip",
+                 "hadamard_quant_i8": "hadamard_quant.hip", "rmsnorm_quant_i8": "block_quant.hip",
+                 "hadamard_heads_quant_i8": "block_quant.hip"}
 
 
 def parse():
@@ -72,7 +76,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="70b_prefill",
                     choices=["70b_prefill", "7b_prefill", "7b_decode", "70b_kv", "70b_block",
-                             "7b_block"])
+                             "7b_block", "70b_block_w8a8", "7b_block_w8a8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -120,7 +124,16 @@ def decode_bytes(b, hkv, hq, L, dh, group):
 # Workload construction: a list of launches (kernel, label, bytes, ops, fn)
 # ---------------------------------------------------------------------------
 
-def make_block(torch, qr, wl, W, T, dev, with_kv, f16_down=False, quarot=False):
+def i8_bytes(T, d):
+    """b-bit quantizer: read fp16 x, write one byte per code and the fp16 scale."""
+    return T * (2 * d + d + 2)
+
+
+def gemm8_bytes(T, N, K):
+    return T * K + N * K + 2 * T + 2 * N + 2 * T * N
+
+
+def make_block(torch, qr, wl, W, T, dev, with_kv, f16_down=False, quarot=False, bits=4):
     lin = {l.name: l for l in W.linears}
     H, ffn, wid = W.hidden, lin["down"].k, W.wid
     inputs = {}
@@ -131,17 +144,35 @@ def make_block(torch, qr, wl, W, T, dev, with_kv, f16_down=False, quarot=False):
     signs = {d: torch.from_numpy(wl.signs(wid, d)).to(dev) for d in (H, ffn)}
     # weights: random init, rotated by the same R_K and quantized per output
     # channel with the library's own kernel (offline preparation, not timed)
+    i8 = bits != 4
     wq = {}
     for i, (name, l) in enumerate(lin.items()):
         w = wl.weights_torch(torch, dev, wid, 1 + i, l.n, l.k)
-        wq[name] = qr.hadamard_quant(w, signs[l.k], 1.0)
+        wq[name] = (qr.hadamard_quant_i8(w, signs[l.k], 1.0, bits) if i8
+                    else qr.hadamard_quant(w, signs[l.k], 1.0))
         del w
-    qbuf = {n: (torch.empty((T, x.shape[1] // 2), dtype=torch.uint8, device=dev),
+    qbuf = {n: (torch.empty((T, x.shape[1]) if i8 else (T, x.shape[1] // 2),
+                            dtype=torch.int8 if i8 else torch.uint8, device=dev),
                 torch.empty((T,), dtype=torch.float16, device=dev)) for n, x in inputs.items()}
     ybuf = {n: torch.empty((T, l.n), dtype=torch.float16, device=dev) for n, l in lin.items()}
     L = []
     tag = f"T{T}:" if not with_kv else ""
     for name, x in inputs.items():
+        if i8:
+            # b-bit codes one per byte: the model's online path with the _i8 quantizers
+            if name in ("attn_in", "ffn_in"):
+                fn = (lambda x=x, name=name: qr.rmsnorm_quant_i8(x, 1e-5, 1.0, bits, out=qbuf[name]))
+                kname = "rmsnorm_quant_i8"
+            elif name == "o_in":
+                fn = (lambda x=x, name=name: qr.hadamard_heads_quant_i8(x, H // 128, 1.0, bits,
+                                                                        out=qbuf[name]))
+                kname = "hadamard_heads_quant_i8"
+            else:
+                fn = (lambda x=x, name=name: qr.hadamard_quant_i8(x, signs[x.shape[1]], 1.0, bits,
+                                                                  out=qbuf[name]))
+                kname = "hadamard_quant_i8"
+            L.append((kname, tag + name, i8_bytes(T, x.shape[1]), 0, fn, qbuf[name]))
+            continue
         if quarot and name in ("attn_in", "ffn_in"):
             # the residual rotation is fused into the weights; RMSNorm (no scale) + INT4 online
             L.append(("rmsnorm_quant", tag + name, hq_bytes(T, x.shape[1]), 0,
@@ -160,6 +191,11 @@ def make_block(torch, qr, wl, W, T, dev, with_kv, f16_down=False, quarot=False):
                   (lambda x=x, name=name, f16=f16: qr.hadamard_quant(
                       x, signs[x.shape[1]], 1.0, out=qbuf[name], fp16_transform=f16)), qbuf[name]))
     for name, l in lin.items():
+        if i8:
+            L.append(("w8a8_gemm", tag + name, gemm8_bytes(T, l.n, l.k), gemm_ops(T, l.n, l.k),
+                      (lambda name=name, l=l: qr.w8a8_gemm(*qbuf[l.input], *wq[name],
+                                                            out=ybuf[name])), (ybuf[name],)))
+            continue
         L.append(("w4a4_gemm", tag + name, gemm_bytes(T, l.n, l.k), gemm_ops(T, l.n, l.k),
                   (lambda name=name, l=l: qr.w4a4_gemm(*qbuf[l.input], *wq[name],
                                                         out=ybuf[name])), (ybuf[name],)))
@@ -410,19 +446,22 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wname = args.workload
-    quarot = wname in ("70b_block", "7b_block")
-    W = wl.WORKLOADS[wname.replace("block", "prefill") if quarot else wname]
+    bits = 8 if wname.endswith("_w8a8") else 4
+    quarot = wname in ("70b_block", "7b_block", "70b_block_w8a8", "7b_block_w8a8")
+    W = wl.WORKLOADS[wname.replace("_w8a8", "").replace("block", "prefill") if quarot else wname]
     print(f"[bench] workload {W.name}{' (QuaRot online path)' if quarot else ''}", file=sys.stderr,
           flush=True)
     config = {"workload": None}
     if wname in ("70b_prefill", "7b_prefill") or quarot:
         T = W.tokens[0]
         launches, lin, kvdesc = make_block(torch, qr, wl, W, T, dev, True, args.fp16_hadamard,
-                                           quarot)
+                                           quarot, bits)
         inputs_desc = ("RMSNorm (no scale) + INT4 before QKV and gate/up, Hadamard heads "
                        f"({W.hidden // 128} heads of 128) + INT4 before O, online Hadamard "
                        f"d = {lin['down'].k} + INT4 before down" if quarot
                        else "4 fused rotate+quant")
+        if bits != 4:
+            inputs_desc = f"{bits}-bit codes one per byte: " + inputs_desc.replace(" + INT4", "")
         config.update({
             "workload": f"{W.name}{' (QuaRot online path)' if quarot else ''}: T={T} tokens, "
                         f"hidden {W.hidden}, FFN {lin['down'].k}, QKV {lin['qkv'].n}; "
@@ -430,7 +469,7 @@ def main():
             "tokens": T, "hidden": W.hidden, "ffn": lin["down"].k,
             "hadamard_arithmetic": (f"fp16 for d = {lin['down'].k}, fp32 otherwise"
                                     if args.fp16_hadamard else "fp32")})
-        dominant, bound = "w4a4_gemm", "mfma"
+        dominant, bound = ("w4a4_gemm" if bits == 4 else "w8a8_gemm"), "mfma"
     elif wname == "7b_decode":
         launches = []
         for T in W.tokens:
@@ -482,7 +521,8 @@ def main():
         "config": config,
         "roofline": roofline(dominant, wname, launches, per, bound),
     }
-    for k in ("hadamard_quant", "rmsnorm_quant", "hadamard_heads_quant"):
+    for k in ("hadamard_quant", "rmsnorm_quant", "hadamard_heads_quant", "hadamard_quant_i8",
+              "rmsnorm_quant_i8", "hadamard_heads_quant_i8"):
         if any(l[0] == k for l in launches):
             out["roofline_" + k] = roofline(k, wname, launches, per, "hbm")
     if dominant != "kv_rotate_quant" and any(l[0] == "kv_rotate_quant" for l in launches):
@@ -511,13 +551,14 @@ def fp16_context(torch, wl, W, T, dev, launches, per, args):
     torch.cuda.synchronize()
     ms16, per16, _ = run_timed(torch, L, max(1, args.steps // 2), 1)
     del L
-    lin_kernels = ("w4a4_gemm", "rmsnorm_quant", "hadamard_heads_quant", "hadamard_quant")
+    lin_kernels = ("w4a4_gemm", "rmsnorm_quant", "hadamard_heads_quant", "hadamard_quant",
+                   "w8a8_gemm", "rmsnorm_quant_i8", "hadamard_heads_quant_i8", "hadamard_quant_i8")
     ms4 = sum(p for l, p in zip(launches, per) if l[0] in lin_kernels)
     ops = 2 * T * sum(l.n * l.k for l in W.linears)
     return {"fp16_linears_ms": round(ms16, 4),
             "fp16_TFLOP/s": round(ops / (ms16 * 1e-3) / 1e12, 1),
             "fp16_per_gemm_ms": {l.name: round(p, 4) for l, p in zip(W.linears, per16)},
-            "int4_linears_ms": round(ms4, 4),
+            "quantized_linears_ms": round(ms4, 4),
             "linears_speedup": round(ms16 / ms4, 3),
             "note": "torch.matmul (hipBLASLt) fp16 GEMMs of the same shapes vs the 4 input "
                     "quantizers + 5 W4A4 GEMMs of the step"}

@@ -850,7 +850,8 @@ __device__ __forceinline__ void k28_finish_f16(const float (&v)[4][28], int64_t 
 template <int MODE, bool CLAMP, bool F16>
 __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uint16_t* __restrict__ x, int64_t T,
                                                    int64_t ld, const int8_t* __restrict__ signs,
-                                                   float c, float clip, uint8_t* __restrict__ q,
+                                                   float c, float clip, int bits,
+                                                   uint8_t* __restrict__ q,
                                                    uint16_t* __restrict__ scale,
                                                    float* __restrict__ zdbg,
                                                    void* __restrict__ yout) {
@@ -1044,7 +1045,7 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
                                 o[w2][k + 3] * sigma};
       }
     }
-    if (MODE == MODE_QUANT) {
+    if (MODE == MODE_QUANT || MODE == MODE_QUANT8) {
       float am = 0.0f;
 #pragma unroll
       for (int w2 = 0; w2 < 4; ++w2)
@@ -1054,9 +1055,10 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
       if (lane == 0) s_red[w] = am;
       __syncthreads();
       am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+      const QRange rg = q_range(MODE == MODE_QUANT8 ? bits : 4);
       uint16_t sh;
       float m;
-      sym_scale(am, c, clip, &sh, &m);
+      sym_scale(am, c, clip, &sh, &m, rg.qmax);
       // The scale is the same on every lane: make that visible, so that the
       // clamp decision below is one scalar branch and not a per-lane mask.
       sh = (uint16_t)__builtin_amdgcn_readfirstlane(sh);
@@ -1064,6 +1066,17 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
       uint16_t* qrow = (uint16_t*)(q + row * (D / 2));
       auto emit = [&](auto clamp_tag) {
         constexpr bool CL = decltype(clamp_tag)::value;
+        if constexpr (MODE == MODE_QUANT8) {
+          // 28 codes of one byte per chunk: seven dwords
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) {
+            uint32_t* qc = (uint32_t*)(q + row * D + chunk_of(w2) * 28);
+#pragma unroll
+            for (int k = 0; k < 7; ++k)
+              st_stream(qc + k, quant_pack4_i8<CL>(&o[w2][4 * k], ml, rg.lo, rg.hi));
+          }
+          return;
+        }
 #pragma unroll
         for (int w2 = 0; w2 < 4; ++w2) {
           uint32_t words[4];
@@ -1151,7 +1164,8 @@ __device__ const H172Frags g_h172_frags16 = make_h172_frags(0x1C00u, 0x9C00u);
 template <int MODE, bool CLAMP, bool F16>
 __global__ __launch_bounds__(256, 2) void k_hq_k172(const uint16_t* __restrict__ x, int64_t T,
                                                     int64_t ld, const int8_t* __restrict__ signs,
-                                                    float c, float clip, uint8_t* __restrict__ q,
+                                                    float c, float clip, int bits,
+                                                    uint8_t* __restrict__ q,
                                                     uint16_t* __restrict__ scale,
                                                     float* __restrict__ zdbg,
                                                     void* __restrict__ yout) {
@@ -1364,7 +1378,7 @@ __global__ __launch_bounds__(256, 2) void k_hq_k172(const uint16_t* __restrict__
             *(v4f*)(zdbg + row * D + elem_of(t, ct)) =
                 v4f{v[t][ct][0] * sigma, v[t][ct][1] * sigma, v[t][ct][2] * sigma, v[t][ct][3] * sigma};
     }
-    if (MODE == MODE_QUANT) {
+    if (MODE == MODE_QUANT || MODE == MODE_QUANT8) {
       float am = 0.0f;
 #pragma unroll
       for (int t = 0; t < 3; ++t)
@@ -1376,12 +1390,27 @@ __global__ __launch_bounds__(256, 2) void k_hq_k172(const uint16_t* __restrict__
       if (lane == 0) s_red[w] = am;
       __syncthreads();
       am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+      const QRange rg = q_range(MODE == MODE_QUANT8 ? bits : 4);
       uint16_t sh;
       float m;
-      sym_scale(am, c, clip, &sh, &m);
+      sym_scale(am, c, clip, &sh, &m, rg.qmax);
       sh = (uint16_t)__builtin_amdgcn_readfirstlane(sh);  // the same on every lane
       const float ml = m * sigma;
       const bool clamp = CLAMP || (sh & 0x7fffu) < 0x0400u;  // block-uniform
+      if constexpr (MODE == MODE_QUANT8) {
+        // four consecutive codes of one byte per (t, ct): one dword each, in place
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+          if (valid(t))
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+              st_stream((uint32_t*)(q + row * D + elem_of(t, ct)),
+                        clamp ? quant_pack4_i8<true>(v[t][ct], ml, rg.lo, rg.hi)
+                              : quant_pack4_i8<false>(v[t][ct], ml, rg.lo, rg.hi));
+        if (tid == 0) scale[row] = sh;
+        __syncthreads();  // s_red is reused by the next row
+        continue;
+      }
 #pragma unroll
       for (int t = 0; t < 3; ++t)
         if (valid(t))
@@ -1521,20 +1550,20 @@ static qr_status launch_lds_t(int d, int n, const uint16_t* x, int64_t T, int64_
 template <int MODE, bool CLAMP, bool F16>
 static qr_status launch_k28(const uint16_t* x, int64_t T, int64_t ld, const int8_t* signs, float c,
                             float clip, uint8_t* qq, uint16_t* ss, float* z, void* y,
-                            hipStream_t st) {
+                            hipStream_t st, int bits = 4) {
   const int grid = grid_for(T, 1, QR_K28_GRID);
   hipLaunchKernelGGL((k_hq_k28<MODE, CLAMP, F16>), dim3(grid), dim3(256), 0, st, x, T, ld, signs,
-                     c, clip, qq, ss, z, y);
+                     c, clip, bits, qq, ss, z, y);
   return launch_status();
 }
 
 template <int MODE, bool CLAMP, bool F16>
 static qr_status launch_k172(const uint16_t* x, int64_t T, int64_t ld, const int8_t* signs,
                              float c, float clip, uint8_t* qq, uint16_t* ss, float* z, void* y,
-                             hipStream_t st) {
+                             hipStream_t st, int bits = 4) {
   const int grid = grid_for(T, 1, 512);
   hipLaunchKernelGGL((k_hq_k172<MODE, CLAMP, F16>), dim3(grid), dim3(256), 0, st, x, T, ld,
-                     signs, c, clip, qq, ss, z, y);
+                     signs, c, clip, bits, qq, ss, z, y);
   return launch_status();
 }
 
@@ -1562,7 +1591,8 @@ static qr_status dispatch(const void* x_f16, int64_t T, int32_t d, int64_t ld, i
   return launch_lds_t<172, MODE, CLAMP, true>(d, n, x, T, ld, signs, c, clip, qq, ss, z, y, st);
 }
 
-// b-bit codes one per byte: every width through the LDS-staged kernel.
+// b-bit codes one per byte: d = 1024 * 28 and 64 * 172 through their own
+// kernels, every other width through the LDS-staged kernel.
 template <bool CLAMP>
 static qr_status dispatch_q8(const uint16_t* x, int64_t T, int32_t d, int64_t ld, int rot,
                              const int8_t* signs, float clip, int bits, uint8_t* q, uint16_t* sc,
@@ -1576,9 +1606,15 @@ static qr_status dispatch_q8(const uint16_t* x, int64_t T, int32_t d, int64_t ld
   if (m == 1)
     return launch_lds_t<1, MODE_QUANT8, CLAMP, true>(d, n, x, T, ld, signs, c, clip, q, sc, z,
                                                      nullptr, st, bits);
+  if (m == 28 && n == 10)
+    return launch_k28<MODE_QUANT8, CLAMP, false>(x, T, ld, signs, c, clip, q, sc, z, nullptr, st,
+                                                 bits);
   if (m == 28)
     return launch_lds_t<28, MODE_QUANT8, CLAMP, true>(d, n, x, T, ld, signs, c, clip, q, sc, z,
                                                       nullptr, st, bits);
+  if (n == 6)
+    return launch_k172<MODE_QUANT8, CLAMP, false>(x, T, ld, signs, c, clip, q, sc, z, nullptr, st,
+                                                  bits);
   return launch_lds_t<172, MODE_QUANT8, CLAMP, true>(d, n, x, T, ld, signs, c, clip, q, sc, z,
                                                      nullptr, st, bits);
 }

@@ -82,7 +82,7 @@ def test_hadamard_quant_i8_clip_and_no_rotation(bits):
     assert q.min() == lo and q.max() == hi
 
 
-@pytest.mark.parametrize("d", [4096, 28672])
+@pytest.mark.parametrize("d", [4096, 28672, 11008])
 def test_i8_with_four_bits_matches_the_int4_kernels(d):
     # grid inputs: both transforms are exact, so the 4-bit codes one per byte
     # must be the nibbles the INT4 kernel packs
@@ -92,6 +92,25 @@ def test_i8_with_four_bits_matches_the_int4_kernels(d):
     q4, s4 = qr.hadamard_quant(dev(x), dev(s), 1.0)
     assert np.array_equal(host(s8).view(np.uint16), host(s4).view(np.uint16))
     assert np.array_equal(host(q8), oq.unpack_int4(host(q4)))
+
+
+@pytest.mark.parametrize("bits", [8, 6])
+@pytest.mark.parametrize("d", [28672, 11008, 8192])
+def test_hadamard_quant_i8_edge_rows(d, bits):
+    # zero row, constant row, a row whose scale is an fp16 subnormal (clamped
+    # path), a single spike, a Gaussian row; bit-exact against the recipe
+    s = wl.signs(44, d)
+    x = np.zeros((5, d), dtype=np.float16)
+    x[1] = 1.0
+    x[2] = (wl.grid_activations(44, 0, 1, d)[0].astype(np.float64) * 2.0 ** -20).astype(np.float16)
+    x[3, d // 3] = 3.0
+    x[4] = wl.activations(44, 1, 1, d)[0]
+    q, sc, z = (host(t) for t in qr.hadamard_quant_i8(dev(x), dev(s), 1.0, bits, z_dbg=True))
+    z64 = oh.rotate_unnormalised(x.astype(np.float64), s)
+    assert np.array_equal(z[:4].astype(np.float64), z64[:4])
+    q_rec, s_rec = oq.sym_quant_recipe(z, d, True, 1.0, bits)
+    assert np.array_equal(sc.view(np.uint16), s_rec.view(np.uint16)) and np.array_equal(q, q_rec)
+    assert sc[0] == 0 and not q[0].any()
 
 
 # ---------------------------------------------------------------------------
