@@ -74,6 +74,9 @@ def _load():
     lib.qr_hadamard_heads_quant_i8.argtypes = [vp, i64, i32, i32, i64, f32, i32, vp, vp, vp, vp]
     lib.qr_w8a8_gemm.restype = ctypes.c_int
     lib.qr_w8a8_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp, vp]
+    lib.qr_kv_rotate_quant_bits.restype = ctypes.c_int
+    lib.qr_kv_rotate_quant_bits.argtypes = [vp, i32, i32, i32, i32, i64, ctypes.c_int, vp, i32, f32,
+                                            i32, vp, vp, i32, i32, vp, vp]
     lib.qr_kv_decode_workspace_bytes.restype = i64
     lib.qr_kv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.qr_kv_decode_attention.restype = ctypes.c_int
@@ -359,10 +362,12 @@ def _gemm(a_q, a_scale, w_q, w_scale, acc_dbg, out, stream, i8):
 
 
 def kv_rotate_quant(kv, signs, group: int, clip_ratio: float, cache_q, cache_meta,
-                    start_pos: int, rotate: bool = True, z_dbg: bool = False, stream=None):
+                    start_pos: int, rotate: bool = True, z_dbg: bool = False, stream=None,
+                    bits: int = 4):
     """Quantize kv fp16 [B, S_new, H, Dh] (last dim contiguous, heads packed) into the cache.
 
     cache_q uint8 [B, H, S_max, Dh/2]; cache_meta fp16 [B, H, S_max, Dh/group, 2].
+    bits in {2, 3, 4}: codes with 2^bits - 1 levels, in the same 4-bit layout.
     Returns z fp32 [B, S_new, H, Dh] when z_dbg.
     """
     torch = _torch()
@@ -381,12 +386,17 @@ def kv_rotate_quant(kv, signs, group: int, clip_ratio: float, cache_q, cache_met
     ld = kv.stride(1) if S_new > 1 else (kv.stride(0) if B > 1 else H * Dh)
     s = _signs(signs, Dh, kv.device) if rotate else None
     z = torch.empty((B, S_new, H, Dh), dtype=torch.float32, device=kv.device) if z_dbg else None
-    code = _load().qr_kv_rotate_quant(_ptr(kv), B, S_new, H, Dh, ld,
-                                      QR_ROT_HADAMARD if rotate else QR_ROT_NONE, _ptr(s),
-                                      int(group), float(clip_ratio), _ptr(cache_q),
-                                      _ptr(cache_meta), S_max, int(start_pos), _ptr(z),
-                                      _stream(stream))
-    _check(code, "qr_kv_rotate_quant")
+    rot = QR_ROT_HADAMARD if rotate else QR_ROT_NONE
+    if bits == 4:
+        code = _load().qr_kv_rotate_quant(_ptr(kv), B, S_new, H, Dh, ld, rot, _ptr(s), int(group),
+                                          float(clip_ratio), _ptr(cache_q), _ptr(cache_meta),
+                                          S_max, int(start_pos), _ptr(z), _stream(stream))
+    else:
+        code = _load().qr_kv_rotate_quant_bits(_ptr(kv), B, S_new, H, Dh, ld, rot, _ptr(s),
+                                               int(group), float(clip_ratio), int(bits),
+                                               _ptr(cache_q), _ptr(cache_meta), S_max,
+                                               int(start_pos), _ptr(z), _stream(stream))
+    _check(code, "qr_kv_rotate_quant" if bits == 4 else "qr_kv_rotate_quant_bits")
     return z
 
 

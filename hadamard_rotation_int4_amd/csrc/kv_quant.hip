@@ -79,9 +79,9 @@ __device__ __forceinline__ float dpp_f(float v) {
 template <int LPR, bool ROT>
 __global__ __launch_bounds__(256) void k_kv_quant(
     const uint16_t* __restrict__ x, int64_t rows, int S_new, int H, int64_t ld_token,
-    const int8_t* __restrict__ signs, int group, float c, float clip, uint8_t* __restrict__ cq,
-    uint16_t* __restrict__ meta, int S_max, int start_pos, float* __restrict__ zdbg, FastDiv fdH,
-    FastDiv fdS) {
+    const int8_t* __restrict__ signs, int group, float c, float clip, float levels,
+    uint8_t* __restrict__ cq, uint16_t* __restrict__ meta, int S_max, int start_pos,
+    float* __restrict__ zdbg, FastDiv fdH, FastDiv fdS) {
   constexpr int DH = LPR * 8;
   constexpr int RPW = 64 / LPR;
   const int tid = threadIdx.x;
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void k_kv_quant(
     }
     const float mxc = __fmul_rn(clip, mx);
     const float mnc = __fmul_rn(clip, mn);
-    const uint16_t sh = f2h(__fdiv_rn(__fsub_rn(mxc, mnc), 15.0f));
+    const uint16_t sh = f2h(__fdiv_rn(__fsub_rn(mxc, mnc), levels));
     const uint16_t mh = f2h(mnc);
     const float shf = h2f(sh);
     const float mhf = h2f(mh);
@@ -190,10 +190,11 @@ __global__ __launch_bounds__(256) void k_kv_quant(
     uint32_t f[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      // kMagic + rne((y - m_h) * inv), clamped to [0, 15].  The clamp is needed
-      // even without clipping: m_h is mn rounded to fp16 and s_h is rounded too.
+      // kMagic + rne((y - m_h) * inv), clamped to [0, levels].  The clamp is
+      // needed even without clipping: m_h is mn rounded to fp16 and s_h is
+      // rounded too.
       float t = fmaf(__fsub_rn(y[j], mhf), inv, kMagic);
-      t = __builtin_amdgcn_fmed3f(t, kMagic, kMagic + 15.0f);
+      t = __builtin_amdgcn_fmed3f(t, kMagic, kMagic + levels);
       f[j] = __float_as_uint(t);
     }
     const uint32_t p0 = (f[1] << 4) | (f[0] & 0xfu);
@@ -218,8 +219,8 @@ __global__ __launch_bounds__(256) void k_kv_quant(
 template <bool ROT>
 static qr_status launch_kv(int dh, const uint16_t* x, int64_t rows, int S_new, int H,
                            int64_t ld_token, const int8_t* signs, int group, float c, float clip,
-                           uint8_t* cq, uint16_t* meta, int S_max, int start_pos, float* zdbg,
-                           hipStream_t st) {
+                           float levels, uint8_t* cq, uint16_t* meta, int S_max, int start_pos,
+                           float* zdbg, hipStream_t st) {
   const int lpr = dh / 8;
   const int64_t rows_per_block = 4 * (64 / lpr);
   int64_t grid = (rows + rows_per_block - 1) / rows_per_block;
@@ -228,7 +229,8 @@ static qr_status launch_kv(int dh, const uint16_t* x, int64_t rows, int S_new, i
 #define QR_CASE(L)                                                                              \
   case L:                                                                                       \
     hipLaunchKernelGGL((k_kv_quant<L, ROT>), dim3((int)grid), dim3(256), 0, st, x, rows, \
-                       S_new, H, ld_token, signs, group, c, clip, cq, meta, S_max, start_pos,   \
+                       S_new, H, ld_token, signs, group, c, clip, levels, cq, meta, S_max,      \
+                       start_pos,                                                               \
                        zdbg, make_fastdiv((uint32_t)H), make_fastdiv((uint32_t)S_new));         \
     break;
     QR_CASE(1)
@@ -244,22 +246,17 @@ static qr_status launch_kv(int dh, const uint16_t* x, int64_t rows, int S_new, i
   return launch_status();
 }
 
-}  // namespace qr
-
-using namespace qr;
-
-extern "C" qr_status qr_kv_rotate_quant(const void* kv_f16, int32_t B, int32_t S_new, int32_t H,
-                                        int32_t Dh, int64_t ld_token, qr_rot rot,
-                                        const int8_t* signs, int32_t group, float clip_ratio,
-                                        void* cache_q, void* cache_meta, int32_t S_max,
-                                        int32_t start_pos, float* z_dbg, hipStream_t stream) {
+static qr_status kv_entry(const void* kv_f16, int32_t B, int32_t S_new, int32_t H, int32_t Dh,
+                          int64_t ld_token, qr_rot rot, const int8_t* signs, int32_t group,
+                          float clip_ratio, int32_t bits, void* cache_q, void* cache_meta,
+                          int32_t S_max, int32_t start_pos, float* z_dbg, hipStream_t stream) {
   if (B < 1 || H < 1 || S_new < 0 || S_max < 0 || start_pos < 0) return QR_ERR_SHAPE;
   if ((int64_t)start_pos + S_new > S_max) return QR_ERR_SHAPE;
   if (Dh < 8 || Dh > 256 || (Dh & (Dh - 1))) return QR_ERR_UNSUPPORTED;
   if (group < 8 || group > Dh || Dh % group != 0 || (group & (group - 1))) return QR_ERR_UNSUPPORTED;
   if (ld_token < (int64_t)H * Dh) return QR_ERR_SHAPE;
   if (rot != QR_ROT_NONE && rot != QR_ROT_HADAMARD) return QR_ERR_ARG;
-  if (!valid_clip(clip_ratio)) return QR_ERR_ARG;
+  if (!valid_clip(clip_ratio) || bits < 2 || bits > 4) return QR_ERR_ARG;
   if (S_new == 0) return QR_OK;
   if (!kv_f16 || !cache_q || !cache_meta) return QR_ERR_NULL;
   if (ld_token % 8 != 0 || !aligned(kv_f16, 16) || !aligned(cache_q, 4) ||
@@ -271,9 +268,33 @@ extern "C" qr_status qr_kv_rotate_quant(const void* kv_f16, int32_t B, int32_t S
   const uint16_t* x = (const uint16_t*)kv_f16;
   uint8_t* cq = (uint8_t*)cache_q;
   uint16_t* meta = (uint16_t*)cache_meta;
+  const float levels = (float)((1 << bits) - 1);
   if (rot == QR_ROT_HADAMARD)
     return launch_kv<true>(Dh, x, rows, S_new, H, ld_token, signs, group, norm_constant(Dh),
-                           clip_ratio, cq, meta, S_max, start_pos, z_dbg, stream);
-  return launch_kv<false>(Dh, x, rows, S_new, H, ld_token, signs, group, 1.0f, clip_ratio, cq,
-                          meta, S_max, start_pos, z_dbg, stream);
+                           clip_ratio, levels, cq, meta, S_max, start_pos, z_dbg, stream);
+  return launch_kv<false>(Dh, x, rows, S_new, H, ld_token, signs, group, 1.0f, clip_ratio, levels,
+                          cq, meta, S_max, start_pos, z_dbg, stream);
+}
+
+}  // namespace qr
+
+using namespace qr;
+
+extern "C" qr_status qr_kv_rotate_quant(const void* kv_f16, int32_t B, int32_t S_new, int32_t H,
+                                        int32_t Dh, int64_t ld_token, qr_rot rot,
+                                        const int8_t* signs, int32_t group, float clip_ratio,
+                                        void* cache_q, void* cache_meta, int32_t S_max,
+                                        int32_t start_pos, float* z_dbg, hipStream_t stream) {
+  return kv_entry(kv_f16, B, S_new, H, Dh, ld_token, rot, signs, group, clip_ratio, 4, cache_q,
+                  cache_meta, S_max, start_pos, z_dbg, stream);
+}
+
+extern "C" qr_status qr_kv_rotate_quant_bits(const void* kv_f16, int32_t B, int32_t S_new,
+                                             int32_t H, int32_t Dh, int64_t ld_token, qr_rot rot,
+                                             const int8_t* signs, int32_t group, float clip_ratio,
+                                             int32_t bits, void* cache_q, void* cache_meta,
+                                             int32_t S_max, int32_t start_pos, float* z_dbg,
+                                             hipStream_t stream) {
+  return kv_entry(kv_f16, B, S_new, H, Dh, ld_token, rot, signs, group, clip_ratio, bits, cache_q,
+                  cache_meta, S_max, start_pos, z_dbg, stream);
 }

@@ -284,6 +284,20 @@ qr_status qr_kv_rotate_quant(const void* kv_f16, int32_t B, int32_t S_new, int32
                              int32_t start_pos, float* z_dbg, hipStream_t stream);
 
 /*
+ * qr_kv_rotate_quant with b-bit codes, 2 <= bits <= 4 (QuaRot paper, KV
+ * bit-width study, Table 6): 15 becomes L = 2^bits - 1 in the formulas above
+ * (scale = fp16((mx - mn) / L), q = clamp(rne((y - min) / scale), 0, L)).  The
+ * codes keep the 4-bit cache layout, so qr_kv_decode_attention reads a cache
+ * of any of these widths unchanged.  bits = 4 is qr_kv_rotate_quant.
+ * Requirements as qr_kv_rotate_quant; bits outside [2, 4] is QR_ERR_ARG.
+ */
+qr_status qr_kv_rotate_quant_bits(const void* kv_f16, int32_t B, int32_t S_new, int32_t H,
+                                  int32_t Dh, int64_t ld_token, qr_rot rot, const int8_t* signs,
+                                  int32_t group, float clip_ratio, int32_t bits, void* cache_q,
+                                  void* cache_meta, int32_t S_max, int32_t start_pos,
+                                  float* z_dbg, hipStream_t stream);
+
+/*
  * Decode routine (QuaRot paper, attention routines Init / Append / Decode):
  * attention of one new query per sequence over the 4-bit K/V cache that
  * qr_kv_rotate_quant wrote, for grouped-query heads.  For batch b, query head

@@ -60,9 +60,10 @@ def check_sym_exact(q_gpu_packed, s_gpu, z_exact, d, rotated, clip):
     assert np.array_equal(np.asarray(q_gpu_packed), oq.pack_int4(q_ref)), "R4: packed codes"
 
 
-def check_asym(codes_gpu, s_gpu, m_gpu, y64, group, clip):
-    """KV analogue of R2 + R3 (codes unpacked, [..., Dh])."""
-    q_ref, s_ref, m_ref = okv.asym_quant_math(y64, group, clip)
+def check_asym(codes_gpu, s_gpu, m_gpu, y64, group, clip, bits=4):
+    """KV analogue of R2 + R3 (codes unpacked, [..., Dh]); 2^bits - 1 levels."""
+    levels = (1 << bits) - 1
+    q_ref, s_ref, m_ref = okv.asym_quant_math(y64, group, clip, bits)
     us = f16_ulp_diff(s_gpu, s_ref)
     um = f16_ulp_diff(m_gpu, m_ref)
     assert us.max() <= 1 and um.max() <= 1, f"KV scale/min ulps {us.max()}/{um.max()}"
@@ -72,7 +73,7 @@ def check_asym(codes_gpu, s_gpu, m_gpu, y64, group, clip):
     s_r = s_ref.astype(np.float64)
     ds = np.abs(np.asarray(s_gpu, np.float64) - s_r)
     dm = np.abs(np.asarray(m_gpu, np.float64) - m_ref.astype(np.float64))
-    shift = np.where(s_r > 0, (15 * ds + dm) / np.where(s_r > 0, s_r, 1), 0)
+    shift = np.where(s_r > 0, (levels * ds + dm) / np.where(s_r > 0, s_r, 1), 0)
     win = TIE_TOL + np.repeat(shift, group, axis=-1).reshape(diff.shape)
     bad = (diff != 0) & (tie >= win)
     assert not bad.any(), f"KV: {int(bad.sum())} codes differ away from a .5 boundary"

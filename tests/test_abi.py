@@ -35,6 +35,7 @@ def test_header_declares_the_path():
                  "qr_kv_decode_attention", "qr_kv_decode_workspace_bytes",
                  "qr_rmsnorm_quant", "qr_hadamard_heads_quant", "qr_hadamard_quant_i8",
                  "qr_rmsnorm_quant_i8", "qr_hadamard_heads_quant_i8", "qr_w8a8_gemm",
+                 "qr_kv_rotate_quant_bits",
                  "qr_hadamard_factor", "qr_status_str", "qr_abi_version"):
         assert must in names
 
@@ -149,6 +150,17 @@ def test_kv_validation(lib):
     assert kvq(lib, kv=None) == QR_ERR_NULL
     assert kvq(lib, cq=A16 + 2) == QR_ERR_ALIGN
     assert kvq(lib, ld=1028) == QR_ERR_ALIGN
+
+
+def test_kv_bits_validation(lib):
+    def kb(bits, S_new=3, start=0):
+        return lib.qr_kv_rotate_quant_bits(A16, 2, S_new, 8, 128, 1024, 1, None, 128, 0.95, bits,
+                                           A16, A16, 10, start, None, None)
+    assert kb(3, S_new=0) == QR_OK
+    assert kb(2, S_new=0) == QR_OK
+    assert kb(1) == QR_ERR_ARG
+    assert kb(5) == QR_ERR_ARG
+    assert kb(3, start=8) == QR_ERR_SHAPE
 
 
 def kvd(lib, q=A16, B=2, Hq=16, Hkv=2, Dh=128, kq=A16, km=A16, vq=A16, vm=A16, S_max=300, L=260,

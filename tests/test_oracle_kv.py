@@ -96,3 +96,35 @@ def test_recipe_agrees_with_math_away_from_ties(rotated):
     assert np.abs(diff).max() <= 1
     near = kv.asym_tie_distance(y, 128, sm, mm) < 5e-3
     assert not np.any((diff != 0) & ~near)
+
+
+# ---------------------------------------------------------------------------
+# 2- and 3-bit KV (QuaRot paper, KV bit-width study, Table 6)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_bbit_ramp_group_codes(bits):
+    # y = mn + k s with s, mn exact in fp16 and k = 0 .. 2^b - 1: codes are k
+    levels = (1 << bits) - 1
+    k = np.tile(np.arange(levels + 1), 128 // (levels + 1))
+    y = (-1.5 + 0.25 * k).astype(np.float64)[None, :]
+    q, s, m = kv.asym_quant_math(y, 128, bits=bits)
+    assert float(s[0, 0]) == 0.25 and float(m[0, 0]) == -1.5 and np.array_equal(q[0], k)
+    q2, s2, m2 = kv.asym_quant_recipe(y.astype(np.float32), 128, rotated=False, group=128, bits=bits)
+    assert np.array_equal(q2[0], k) and s2[0, 0] == s[0, 0]
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_bbit_range_and_error(bits):
+    levels = (1 << bits) - 1
+    y = np.random.default_rng(60 + bits).standard_normal((16, 128))
+    q, s, m = kv.asym_quant_math(y, 128, bits=bits)
+    assert q.min() == 0 and q.max() == levels
+    # reconstruction error within half a step (plus the fp16 rounding of scale and min)
+    err = np.abs(kv.asym_dequant(q, s, m, 128) - y)
+    step = s.astype(np.float64)[..., 0][:, None]
+    assert (err <= 0.5 * step * (1 + 1e-2) + 1e-3 * np.abs(y).max()).all()
+    # four bits reproduce the INT4 functions
+    q4, s4, m4 = kv.asym_quant_math(y, 128)
+    q4b, s4b, m4b = kv.asym_quant_math(y, 128, bits=4)
+    assert np.array_equal(q4, q4b) and np.array_equal(s4, s4b) and np.array_equal(m4, m4b)
