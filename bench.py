@@ -555,13 +555,34 @@ def fp16_context(torch, wl, W, T, dev, launches, per, args):
                    "w8a8_gemm", "rmsnorm_quant_i8", "hadamard_heads_quant_i8", "hadamard_quant_i8")
     ms4 = sum(p for l, p in zip(launches, per) if l[0] in lin_kernels)
     ops = 2 * T * sum(l.n * l.k for l in W.linears)
+    # hipBLASLt's int8 GEMM (torch._int_mm, int32 out, no epilogue) at the same
+    # shapes: what the vendor library reaches with the same int8 matrix cores
+    Li = []
+    for i, l in enumerate(W.linears):
+        g = torch.Generator(device=dev)
+        g.manual_seed(1000 + i)
+        a = torch.randint(-8, 8, (T, l.k), generator=g, device=dev, dtype=torch.int8)
+        b = torch.randint(-8, 8, (l.n, l.k), generator=g, device=dev, dtype=torch.int8)
+        Li.append(("int8_gemm", l.name, 0, gemm_ops(T, l.n, l.k),
+                   (lambda a=a, b=b: torch._int_mm(a, b.t())), ()))
+    try:
+        ms8, per8, _ = run_timed(torch, Li, max(1, args.steps // 2), 1)
+        int8_ctx = {"hipblaslt_int8_linears_ms": round(ms8, 4),
+                    "hipblaslt_int8_TOPS": round(ops / (ms8 * 1e-3) / 1e12, 1),
+                    "hipblaslt_int8_per_gemm_TOPS": {l.name: round(gemm_ops(T, l.n, l.k) / p / 1e9, 1)
+                                                      for l, p in zip(W.linears, per8)}}
+    except RuntimeError as e:  # shapes the library does not take
+        int8_ctx = {"hipblaslt_int8": f"unavailable: {e}"[:200]}
+    del Li
     return {"fp16_linears_ms": round(ms16, 4),
             "fp16_TFLOP/s": round(ops / (ms16 * 1e-3) / 1e12, 1),
             "fp16_per_gemm_ms": {l.name: round(p, 4) for l, p in zip(W.linears, per16)},
             "quantized_linears_ms": round(ms4, 4),
             "linears_speedup": round(ms16 / ms4, 3),
+            **int8_ctx,
             "note": "torch.matmul (hipBLASLt) fp16 GEMMs of the same shapes vs the 4 input "
-                    "quantizers + 5 W4A4 GEMMs of the step"}
+                    "quantizers + 5 quantized GEMMs of the step; hipBLASLt int8 (torch._int_mm, "
+                    "int32 output, no scales) at the same shapes for calibration"}
 
 
 def cpu_baseline(W, t_sample):
