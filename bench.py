@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the fp16 / hipBLASLt int8 context timings of the block workloads")
     ap.add_argument("--fp16-hadamard", action="store_true",
                     help="down-projection rotation with the fp16 transform")
     return ap.parse_args()
@@ -531,7 +533,7 @@ def main():
         k: {"ms": round(sum(p for l, p in zip(launches, per) if l[0] == k), 4),
             "launches": sum(1 for l in launches if l[0] == k)}
         for k in sorted({l[0] for l in launches})}
-    if quarot:
+    if quarot and not args.no_context:
         out["fp16_context"] = fp16_context(torch, wl, W, T, dev, launches, per, args)
     out["wall_s_timed"] = round(wall, 3)
     out["timing"] = ("HIP graph replay of the step; per-launch times from graphs of 20 "
@@ -574,11 +576,42 @@ def fp16_context(torch, wl, W, T, dev, launches, per, args):
     except RuntimeError as e:  # shapes the library does not take
         int8_ctx = {"hipblaslt_int8": f"unavailable: {e}"[:200]}
     del Li
+    # prefill attention runs in fp16 on both sides (the pages use an off-the-shelf
+    # flash attention on the unquantized Q/K/V): time it once and add it to both
+    attn_ms = None
+    try:
+        Hq, Hkv, Dh = W.hidden // 128, (8 if W.hidden == 8192 else W.hidden // 128), 128
+        B = 32 if T % 32 == 0 and T >= 32 * 128 else 1
+        S = T // B
+        g = torch.Generator(device=dev)
+        g.manual_seed(77)
+        q = torch.randn((B, Hq, S, Dh), generator=g, device=dev, dtype=torch.float16)
+        k = torch.randn((B, Hkv, S, Dh), generator=g, device=dev, dtype=torch.float16)
+        v = torch.randn((B, Hkv, S, Dh), generator=g, device=dev, dtype=torch.float16)
+        k = k.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+        v = v.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+        La = [("fp16_attention", "sdpa", 0, 0,
+               (lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)),
+               ())]
+        attn_ms, _, _ = run_timed(torch, La, max(1, args.steps // 2), 1)
+        del q, k, v, La
+    except RuntimeError as e:  # no attention kernel for these shapes
+        attn_ms = f"unavailable: {e}"[:200]
+    block = {}
+    if isinstance(attn_ms, float):
+        block = {"fp16_attention_ms": round(attn_ms, 4),
+                 "block_speedup": round((ms16 + attn_ms) / (ms4 + attn_ms), 3),
+                 "block_note": f"(fp16 linears + causal SDPA, B={B} x S={S}, {Hq} heads) vs "
+                               "(4 quantizers + 5 quantized GEMMs + the same SDPA); KV "
+                               "quantization and norms left out of both"}
+    else:
+        block = {"fp16_attention": attn_ms}
     return {"fp16_linears_ms": round(ms16, 4),
             "fp16_TFLOP/s": round(ops / (ms16 * 1e-3) / 1e12, 1),
             "fp16_per_gemm_ms": {l.name: round(p, 4) for l, p in zip(W.linears, per16)},
             "quantized_linears_ms": round(ms4, 4),
             "linears_speedup": round(ms16 / ms4, 3),
+            **block,
             **int8_ctx,
             "note": "torch.matmul (hipBLASLt) fp16 GEMMs of the same shapes vs the 4 input "
                     "quantizers + 5 quantized GEMMs of the step; hipBLASLt int8 (torch._int_mm, "
