@@ -12,7 +12,9 @@
 //
 // Both are HBM-bound streams (2 bytes in, half a byte out per element) with
 // little arithmetic, so they run on the VALU: one pass over each row, the row
-// held in registers, reductions across the lanes of the row, one store.
+// held in registers, reductions across the lanes of the row, one store.  The
+// _i8 entry points write b-bit codes one per byte instead (QuaRot paper, 6-
+// and 8-bit round-to-nearest results).
 #include "common.hpp"
 #include "quant_common.hpp"
 
@@ -104,7 +106,8 @@ __global__ __launch_bounds__(256) void k_rms_quant(const uint16_t* __restrict__ 
 // A lane holds J consecutive positions j of every head (NH * J = 128 values
 // for NH >= 16), so all log2(NH) butterfly stages are between its own
 // registers; LPR = DH / J lanes cover a row and a wavefront takes 64 / LPR
-// rows.  Loads are J fp16 per head, stores J/2 bytes of codes per head.
+// rows.  Loads are J fp16 per head, stores J/2 bytes of packed codes per
+// head (J bytes of b-bit codes).
 // ===========================================================================
 template <int J>
 struct HeadsIO;

@@ -30,6 +30,9 @@
 //                rotation: one workgroup per row, the row staged in LDS as fp32,
 //                the dense +-1 H_m products on contiguous m-chunks followed by
 //                radix-32 butterfly passes in LDS.
+// MODE_QUANT8 (qr_hadamard_quant_i8: b-bit codes one per byte, QuaRot paper's
+// 6- and 8-bit round-to-nearest results) is implemented by k_hq_k28, k_hq_k172
+// and k_hq_lds, which then also serves d = 2^n.
 #include <type_traits>
 
 #include "common.hpp"
