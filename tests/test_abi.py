@@ -268,6 +268,26 @@ def test_w8a8_gemm_validation(lib):
     assert f(A16 + 8, A16, 16, A16, A16, 16, 4096, A16, None, None) == QR_ERR_ALIGN
 
 
+def test_c_program_against_the_header(tmp_path):
+    # the header is plain C: a C99 program compiled with gcc links every entry
+    # point and gets the documented host-side answers
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None or not Path("/opt/rocm/include/hip/hip_runtime_api.h").exists():
+        pytest.skip("gcc or the HIP headers are not available")
+    if not qr.LIB_PATH.exists():
+        pytest.fail(f"{qr.LIB_PATH} not built")
+    exe = tmp_path / "abi_check"
+    libdir = str(qr.LIB_PATH.parent)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    f"-I{ROOT / 'include'}", "-I/opt/rocm/include",
+                    str(ROOT / "tests" / "abi_check.c"), "-o", str(exe), f"-L{libdir}",
+                    "-lquarot_hip", f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stderr
+    assert "abi_check: ok" in out.stdout
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros((4, 128), dtype=torch.float16)
