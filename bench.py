@@ -533,6 +533,8 @@ def main():
         k: {"ms": round(sum(p for l, p in zip(launches, per) if l[0] == k), 4),
             "launches": sum(1 for l in launches if l[0] == k)}
         for k in sorted({l[0] for l in launches})}
+    if wname in ("70b_prefill", "7b_prefill") and not args.no_context:
+        out["quality"] = quality_report(torch, qr, wl, W, dev)
     if quarot and not args.no_context:
         out["fp16_context"] = fp16_context(torch, wl, W, T, dev, launches, per, args)
     out["wall_s_timed"] = round(wall, 3)
@@ -616,6 +618,31 @@ def fp16_context(torch, wl, W, T, dev, launches, per, args):
             "note": "torch.matmul (hipBLASLt) fp16 GEMMs of the same shapes vs the 4 input "
                     "quantizers + 5 quantized GEMMs of the step; hipBLASLt int8 (torch._int_mm, "
                     "int32 output, no scales) at the same shapes for calibration"}
+
+
+def quality_report(torch, qr, wl, W, dev, t=64, n=512):
+    """SQNR of the W4A4 output against the unquantized product X W^T (float64 on
+    the host) on a sample of the QKV GEMM: t tokens of its input, n output
+    channels, with the randomized Hadamard and without it (quantization only).
+    Reported, not a target: it shows what the rotation buys on outlier inputs."""
+    import numpy as np
+    lin = {l.name: l for l in W.linears}
+    K = lin["qkv"].k
+    x = wl.activations_torch(torch, dev, W.wid, 10, t, K, W.n_outliers, W.outlier_lo,
+                             W.outlier_hi)
+    w = wl.weights_torch(torch, dev, W.wid, 1, n, K)
+    s = torch.from_numpy(wl.signs(W.wid, K)).to(dev)
+    ref = x.double().cpu().numpy() @ w.double().cpu().numpy().T
+    res = {}
+    for rot in (True, False):
+        qa, sa = qr.hadamard_quant(x, s, 1.0, rotate=rot)
+        qw, sw = qr.hadamard_quant(w, s, 1.0, rotate=rot)
+        y = qr.w4a4_gemm(qa, sa, qw, sw).double().cpu().numpy()
+        res["sqnr_db_rotated" if rot else "sqnr_db_no_rotation"] = round(
+            float(10 * np.log10(np.sum(ref ** 2) / np.sum((y - ref) ** 2))), 2)
+    res["sample"] = (f"{t} tokens of the QKV input (outlier channels planted) x {n} output "
+                     "channels, against float64 X W^T")
+    return res
 
 
 def cpu_baseline(W, t_sample):

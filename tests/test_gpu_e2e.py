@@ -52,3 +52,26 @@ def test_linear_chain(d, N):
     ref = x.astype(np.float64) @ w.astype(np.float64).T
     rel = np.linalg.norm(y.astype(np.float64) - ref) / np.linalg.norm(ref)
     assert rel < 0.3
+
+
+def sqnr_db(y, ref):
+    return 10 * np.log10(np.sum(ref ** 2) / np.sum((y - ref) ** 2))
+
+
+def test_rotation_improves_sqnr():
+    # the point of the method: with outlier channels, the W4A4 product of the
+    # rotated operands tracks X W^T far better than quantizing them as they are
+    W = wl.WORKLOADS["tiny"]
+    T, N, d = 32, 1024, 4096
+    x = wl.activations(W.wid, 0, T, d, n_outliers=4, lo=50, hi=50)
+    w = wl.weights(W.wid, 1, N, d)
+    s = dev(wl.signs(W.wid, d))
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    ys = {}
+    for rot in (True, False):
+        qa, sa = qr.hadamard_quant(dev(x), s, rotate=rot)
+        qw, sw = qr.hadamard_quant(dev(w), s, rotate=rot)
+        ys[rot] = host(qr.w4a4_gemm(qa, sa, qw, sw)).astype(np.float64)
+    rotated, plain = sqnr_db(ys[True], ref), sqnr_db(ys[False], ref)
+    assert rotated > plain + 6.0, (rotated, plain)
+    assert rotated > 10.0, rotated
