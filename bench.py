@@ -541,8 +541,8 @@ def main():
     out["timing"] = ("HIP graph replay of the step; per-launch times from graphs of 20 "
                      "back-to-back launches (outputs checked equal to the eager run)" if graphed
                      else "eager launches, HIP events around each launch on its stream")
-    if not args.no_cpu_baseline and wname == "70b_prefill":
-        out["cpu_baseline"] = cpu_baseline(W, args.cpu_sample_tokens)
+    if not args.no_cpu_baseline and wname in ("70b_prefill", "70b_block"):
+        out["cpu_baseline"] = cpu_baseline(W, args.cpu_sample_tokens, quarot=quarot)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -645,14 +645,17 @@ def quality_report(torch, qr, wl, W, dev, t=64, n=512):
     return res
 
 
-def cpu_baseline(W, t_sample):
+def cpu_baseline(W, t_sample, quarot=False):
     """Time the oracle (float64 rotation + quantization, exact GEMM via float64
     BLAS on the codes, KV quantization) on a bounded sample of the step:
     t_sample tokens against the first 1024 output channels of each GEMM.
+    With quarot the GEMM inputs go through the block's own quantizers
+    (RMSNorm + INT4, Hadamard heads + INT4, online Hadamard + INT4 before down).
     Reported as TOPS over the same GEMM operations (2 per MAC)."""
     import numpy as np
 
     import workloads as wl
+    from oracle import block as ob
     from oracle import gemm as og
     from oracle import hadamard as oh
     from oracle import kv as okv
@@ -674,7 +677,12 @@ def cpu_baseline(W, t_sample):
     t0 = time.perf_counter()
     qa = {}
     for name, x in xs.items():
-        q, s = oq.sym_quant_math(oh.rotate(x.astype(np.float64), sg[x.shape[1]]))
+        if quarot and name in ("attn_in", "ffn_in"):
+            q, s, _ = ob.rmsnorm_quant_math(x, 1e-5)
+        elif quarot and name == "o_in":
+            q, s, _ = ob.hadamard_heads_quant_math(x, W.hidden // 128)
+        else:
+            q, s = oq.sym_quant_math(oh.rotate(x.astype(np.float64), sg[x.shape[1]]))
         qa[name] = (oq.pack_int4(q), s)
     ops = 0
     for name, l in lin.items():
@@ -694,8 +702,9 @@ def cpu_baseline(W, t_sample):
     return {
         "value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": cores, "kind": "oracle",
         "sample": f"{t_sample} tokens x first {n_s} output channels of each of the 5 GEMMs "
-                  f"(full K), their 4 fused rotate+quant inputs, K/V of {t_sample} tokens x 8 heads; "
-                  f"float64 oracle, {dt:.2f} s",
+                  f"(full K), their 4 " + ("input quantizers (RMSNorm, Hadamard heads, online "
+                                           "Hadamard)" if quarot else "fused rotate+quant inputs")
+                  + f", K/V of {t_sample} tokens x 8 heads; float64 oracle, {dt:.2f} s",
         "seconds": round(dt, 3), "cpu": platform.processor() or platform.machine(), "blas": blas,
     }
 
