@@ -96,3 +96,47 @@ def test_all_entry_points_replay_in_a_graph():
         got = snapshot()
         for i, (a, b) in enumerate(zip(eager, got)):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}, output {i}"
+
+
+def test_threads_and_streams_in_parallel():
+    # the entry points keep no global state: four host threads, each on its own
+    # stream and buffers, get the same results as one thread running them in turn
+    import threading
+    dev = torch.device("cuda")
+    T, d, N = 96, 8192, 768
+    jobs = []
+    for i in range(4):
+        x = wl.activations_torch(torch, dev, 61, i, T, d)
+        w = wl.weights_torch(torch, dev, 61, 10 + i, N, d)
+        s = torch.from_numpy(wl.signs(61, d)).to(dev)
+        jobs.append((x, w, s))
+
+    def run(job, stream):
+        x, w, s = job
+        with torch.cuda.stream(stream):
+            qw, sw = qr.hadamard_quant(w, s, 1.0)
+            qa, sa = qr.rmsnorm_quant(x, 1e-5, 1.0)
+            y = qr.w4a4_gemm(qa, sa, qw, sw)
+            q8, s8 = qr.hadamard_heads_quant_i8(x, 64, 1.0, 8)
+            w8, ws8 = qr.hadamard_quant_i8(w, s, 1.0, 8)
+            y8 = qr.w8a8_gemm(q8, s8, w8, ws8)
+        stream.synchronize()
+        return y, y8
+
+    ref = [run(j, torch.cuda.current_stream()) for j in jobs]
+    results = [None] * len(jobs)
+    streams = [torch.cuda.Stream() for _ in jobs]
+
+    def worker(i):
+        for _ in range(3):
+            results[i] = run(jobs[i], streams[i])
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(jobs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for (y, y8), (ry, ry8) in zip(results, ref):
+        assert torch.equal(y.view(torch.int16), ry.view(torch.int16))
+        assert torch.equal(y8.view(torch.int16), ry8.view(torch.int16))
