@@ -6,6 +6,10 @@ paragraph: INT4 GEMM with an INT32 accumulator): acc[t, n] = sum_k
 A_q[t, k] W_q[n, k] exactly, then the output is acc times the token (row)
 scale times the channel (column) scale.
 
+Group-wise scales (one of the paper's studied variants): the accumulator of
+each group of G consecutive k is scaled by that group's token and channel
+scales and the groups are summed in fp32.
+
 Reading taken: the pages cast the INT32 result to FP16 before scaling; that
 overflows once |acc| > 65504 (|acc| can reach 64 K), so the epilogue works in
 fp32 as Y = fp16_rne(fp32(fp32(acc) * a_s[t]) * w_s[n]).
@@ -80,3 +84,41 @@ def w4a4_gemm(a_packed, a_scale, w_packed, w_scale) -> tuple[np.ndarray, np.ndar
     """(fp16 Y, int64 acc) of the W4A4 linear layer."""
     acc = w4a4_acc(a_packed, w_packed)
     return epilogue_recipe(acc, a_scale, w_scale), acc
+
+
+def w4a4_gemm_groups_math(a_packed, a_scales, w_packed, w_scales, group: int) -> np.ndarray:
+    """float64 Y = sum over groups g of acc_g * a_s[t, g] * w_s[n, g], acc_g the
+    exact product of the codes of group g (group-wise scales on both operands)."""
+    a = unpack_int4(a_packed).astype(np.float64)
+    w = unpack_int4(w_packed).astype(np.float64)
+    K = a.shape[-1]
+    y = np.zeros((a.shape[0], w.shape[0]))
+    for gi in range(K // group):
+        sl = slice(gi * group, (gi + 1) * group)
+        acc = a[:, sl] @ w[:, sl].T
+        y += acc * np.asarray(a_scales, F16)[:, gi].astype(np.float64)[:, None] \
+            * np.asarray(w_scales, F16)[:, gi].astype(np.float64)[None, :]
+    return y
+
+
+def w4a4_gemm_groups_recipe(a_packed, a_scales, w_packed, w_scales, group: int):
+    """(fp16 Y, int64 per-group accumulators [G, T, N]) in the fp32 step order of
+    the kernel: for g = 0, 1, ... in turn,
+        p = fp32(fp32(fp32(acc_g) * a_s[t, g]) * w_s[n, g]);  f = fp32(f + p),
+    starting from f = 0, then Y = fp16(f)."""
+    a = unpack_int4(a_packed)
+    w = unpack_int4(w_packed)
+    K = a.shape[-1]
+    f = np.zeros((a.shape[0], w.shape[0]), dtype=F32)
+    accs = []
+    for gi in range(K // group):
+        sl = slice(gi * group, (gi + 1) * group)
+        acc = int_matmul_exact(a[:, sl], w[:, sl])
+        accs.append(acc)
+        a_s = np.asarray(a_scales, F16)[:, gi].astype(F32)[:, None]
+        w_s = np.asarray(w_scales, F16)[:, gi].astype(F32)[None, :]
+        with np.errstate(over="ignore"):
+            p = ((acc.astype(F32) * a_s).astype(F32) * w_s).astype(F32)
+            f = (f + p).astype(F32)
+    with np.errstate(over="ignore"):
+        return f.astype(F16), np.stack(accs)

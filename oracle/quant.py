@@ -153,6 +153,34 @@ def sym_quant_recipe_rows(z: np.ndarray, c: np.ndarray, clip: float = 1.0, bits:
     return q, s_h
 
 
+# ---------------------------------------------------------------------------
+# Group-wise scales (QuaRot paper: group-wise quantization with different
+# group sizes, one of its studied variants): the row is cut into groups of G
+# consecutive elements along K and each group gets its own scale.
+# ---------------------------------------------------------------------------
+
+def sym_quant_groups_math(y: np.ndarray, group: int, clip: float = 1.0, bits: int = 4):
+    """(codes [..., d], fp16 scales [..., d/G]) with one symmetric scale per group."""
+    y = np.asarray(y, dtype=np.float64)
+    d = y.shape[-1]
+    assert d % group == 0
+    g = y.reshape(*y.shape[:-1], d // group, group)
+    q, s = sym_quant_math(g, clip, bits)
+    return q.reshape(y.shape), s
+
+
+def sym_quant_groups_recipe(z: np.ndarray, c: np.ndarray, group: int, clip: float = 1.0,
+                            bits: int = 4):
+    """The fp32 recipe per group: sym_quant_recipe_rows() on every group of G
+    elements of each row, with the row's constant c."""
+    z32 = np.asarray(z, dtype=F32)
+    d = z32.shape[-1]
+    g = z32.reshape(*z32.shape[:-1], d // group, group)
+    cg = np.broadcast_to(np.asarray(c, dtype=F32)[..., None], g.shape[:-1])
+    q, s = sym_quant_recipe_rows(g, cg, clip, bits)
+    return q.reshape(z32.shape), s
+
+
 def dequant(codes: np.ndarray, scale_f16: np.ndarray) -> np.ndarray:
     """float64 codes * scale."""
     return np.asarray(codes, dtype=np.float64) * np.asarray(scale_f16, dtype=F16).astype(np.float64)[..., None]

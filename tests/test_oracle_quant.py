@@ -225,3 +225,55 @@ def test_int8_gemm_bruteforce_and_epilogue_rounding():
     assert y.astype(np.float64).tolist() == [[16.0, 16.0, 32.0, -16.0]]
     yq, accq = gemm.w8a8_gemm(a, np.ones(5, np.float16), w, np.ones(7, np.float16))
     assert np.array_equal(accq, gemm.int4_matmul_bruteforce(a, w))
+
+
+# ---------------------------------------------------------------------------
+# Group-wise scales
+# ---------------------------------------------------------------------------
+
+def test_groups_with_one_group_is_per_token():
+    y = np.random.default_rng(70).standard_normal((6, 256)) * 3
+    qg, sg = oq.sym_quant_groups_math(y, 256)
+    q, s = oq.sym_quant_math(y)
+    assert np.array_equal(qg, q) and np.array_equal(sg[:, 0], s)
+    z = (np.random.default_rng(71).integers(-500, 500, size=(6, 256)) / 4.0).astype(np.float32)
+    c = np.full(6, np.float32(1 / 16), np.float32)
+    qg, sg = oq.sym_quant_groups_recipe(z, c, 256)
+    q, s = oq.sym_quant_recipe(z, 256, True)
+    assert np.array_equal(qg, q) and np.array_equal(sg[:, 0], s)
+
+
+def test_groups_scale_each_group_on_its_own():
+    # group 0 holds an outlier, group 1 small values: group 1's codes keep their
+    # resolution, which a per-token scale would crush to zero
+    y = np.zeros((1, 256))
+    y[0, :128] = np.linspace(-1, 1, 128)
+    y[0, 5] = 70.0
+    y[0, 128:] = np.linspace(-0.1, 0.1, 128)
+    q, s = oq.sym_quant_groups_math(y, 128)
+    assert s[0, 0] == np.float16(10.0) and s[0, 1] == np.float16(0.1 / 7)
+    assert np.abs(q[0, 128:]).max() == 7
+    qt, _ = oq.sym_quant_math(y)
+    assert np.abs(qt[0, 128:]).max() == 0
+
+
+@pytest.mark.parametrize("group", [64, 128, 256])
+def test_groups_gemm_recipe_and_math(group):
+    rng = np.random.default_rng(72 + group)
+    T, N, K = 5, 7, 512
+    a = quant.pack_int4(rng.integers(-8, 8, size=(T, K)))
+    w = quant.pack_int4(rng.integers(-8, 8, size=(N, K)))
+    asc = rng.uniform(1e-3, 1e-1, size=(T, K // group)).astype(np.float16)
+    wsc = rng.uniform(1e-3, 1e-1, size=(N, K // group)).astype(np.float16)
+    y, accs = gemm.w4a4_gemm_groups_recipe(a, asc, w, wsc, group)
+    # the per-group accumulators sum to the full product
+    assert np.array_equal(accs.sum(axis=0), gemm.w4a4_acc(a, w))
+    ua, uw = quant.unpack_int4(a), quant.unpack_int4(w)
+    g0 = gemm.int4_matmul_bruteforce(ua[:, :group], uw[:, :group])
+    assert np.array_equal(accs[0], g0)
+    y64 = gemm.w4a4_gemm_groups_math(a, asc, w, wsc, group)
+    assert np.allclose(y.astype(np.float64), y64, rtol=2e-3, atol=1e-6)
+    # one group over all of K is the per-token epilogue
+    y1, _ = gemm.w4a4_gemm_groups_recipe(a, asc[:, :1], w, wsc[:, :1], K)
+    assert np.array_equal(y1.view(np.uint16), gemm.epilogue_recipe(
+        gemm.w4a4_acc(a, w), asc[:, 0], wsc[:, 0]).view(np.uint16))
