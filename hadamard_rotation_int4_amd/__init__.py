@@ -18,6 +18,7 @@ Functions (same names as the C entry points without the ``qr_`` prefix):
   hadamard_quant_i8 / rmsnorm_quant_i8 / hadamard_heads_quant_i8(..., bits=8)
       -> (q_i8, scale_f16[, dbg]): b-bit codes one per byte (2 <= bits <= 8)
   w8a8_gemm(a_q, a_scale, w_q, w_scale, acc_dbg=False) -> y_f16[, acc_i32]
+  hadamard_quant_groups(x, signs, clip_ratio, group) -> (q_u8, scale_f16 [T, d/group][, z])
   hadamard_factor(d) -> (n, m);  abi_version();  status_str(code)
 """
 from __future__ import annotations
@@ -72,6 +73,9 @@ def _load():
     lib.qr_rmsnorm_quant_i8.argtypes = [vp, i64, i32, i64, f32, f32, i32, vp, vp, vp, vp]
     lib.qr_hadamard_heads_quant_i8.restype = ctypes.c_int
     lib.qr_hadamard_heads_quant_i8.argtypes = [vp, i64, i32, i32, i64, f32, i32, vp, vp, vp, vp]
+    lib.qr_hadamard_quant_groups.restype = ctypes.c_int
+    lib.qr_hadamard_quant_groups.argtypes = [vp, i64, i32, i64, ctypes.c_int, vp, f32, i32, vp, vp,
+                                             vp, vp]
     lib.qr_w8a8_gemm.restype = ctypes.c_int
     lib.qr_w8a8_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp, vp]
     lib.qr_kv_rotate_quant_bits.restype = ctypes.c_int
@@ -263,6 +267,32 @@ def hadamard_quant_i8(x, signs=None, clip_ratio: float = 1.0, bits: int = 8,
                                         float(clip_ratio), int(bits), _ptr(q), _ptr(sc), _ptr(z),
                                         _stream(stream))
     _check(code, "qr_hadamard_quant_i8")
+    return (q, sc, z) if z_dbg else (q, sc)
+
+
+def hadamard_quant_groups(x, signs=None, clip_ratio: float = 1.0, group: int = 128,
+                          rotate: bool = True, z_dbg: bool = False, out=None, stream=None):
+    """As hadamard_quant with one scale per group of `group` elements:
+    (q uint8 [T, d/2], scale fp16 [T, d/group][, z])."""
+    torch = _torch()
+    T, d = _rows(x)
+    s = _signs(signs, d, x.device) if rotate else None
+    if out is None:
+        q = torch.empty((T, d // 2), dtype=torch.uint8, device=x.device)
+        sc = torch.empty((T, max(d // max(group, 1), 1)), dtype=torch.float16, device=x.device)
+    else:
+        q, sc = out
+        _need(q, torch.uint8, "q")
+        _need(sc, torch.float16, "scale")
+        if q.numel() != T * (d // 2) or not q.is_contiguous() or not sc.is_contiguous() or \
+                sc.numel() != T * (d // max(group, 1)):
+            raise ValueError("out tensors have the wrong size or layout")
+    z = torch.empty((T, d), dtype=torch.float32, device=x.device) if z_dbg else None
+    code = _load().qr_hadamard_quant_groups(_ptr(x), T, d, x.stride(0) if T > 0 else d,
+                                            QR_ROT_HADAMARD if rotate else QR_ROT_NONE, _ptr(s),
+                                            float(clip_ratio), int(group), _ptr(q), _ptr(sc),
+                                            _ptr(z), _stream(stream))
+    _check(code, "qr_hadamard_quant_groups")
     return (q, sc, z) if z_dbg else (q, sc)
 
 

@@ -43,8 +43,9 @@ namespace qr {
 __constant__ HTable<28> g_h28 = make_h28();
 __constant__ HTable<172> g_h172 = make_h172();
 
-// MODE_QUANT8: b-bit codes stored one per byte (k_hq_lds only).
-enum { MODE_QUANT = 0, MODE_ROT_F32 = 1, MODE_ROT_F16 = 2, MODE_QUANT8 = 3 };
+// MODE_QUANT8: b-bit codes stored one per byte.  MODE_QUANT_GROUPS: packed
+// INT4 codes with one scale per group of consecutive elements (k_hq_lds only).
+enum { MODE_QUANT = 0, MODE_ROT_F32 = 1, MODE_ROT_F16 = 2, MODE_QUANT8 = 3, MODE_QUANT_GROUPS = 4 };
 
 // Sign-bit masks of 8 consecutive fp16 values from their 8 int8 signs (+1 or
 // -1; the int8 sign bit decides): dword j gets bit 15 if sign 2j is negative
@@ -505,7 +506,8 @@ template <int M, int MODE, bool CLAMP, bool ROT>
 __global__ __launch_bounds__(256) void k_hq_lds(const uint16_t* __restrict__ x, int64_t T, int d,
                                                 int n, int64_t ld,
                                                 const int8_t* __restrict__ signs, float c,
-                                                float clip, int bits, uint8_t* __restrict__ q,
+                                                float clip, int bits, int group,
+                                                uint8_t* __restrict__ q,
                                                 uint16_t* __restrict__ scale,
                                                 float* __restrict__ zdbg,
                                                 void* __restrict__ yout) {
@@ -580,7 +582,29 @@ __global__ __launch_bounds__(256) void k_hq_lds(const uint16_t* __restrict__ x, 
     if (zdbg) {
       for (int i = tid; i < d; i += 256) zdbg[row * d + i] = buf[pad(i)];
     }
-    if (MODE == MODE_QUANT || MODE == MODE_QUANT8) {
+    if (MODE == MODE_QUANT_GROUPS) {
+      // 4'. one scale per group of `group` elements: a group is group / 8
+      // consecutive threads of one wavefront (group <= 512 and aligned), which
+      // reduce its amax among themselves; the group's first thread writes the scale
+      const int lpg = group >> 3;
+      for (int i = tid * 8; i < d; i += 256 * 8) {
+        float v[8];
+        float am = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          v[j] = buf[pad(i + j)];
+          am = fmaxf(am, fabsf(v[j]));
+        }
+        for (int o = 1; o < lpg; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
+        uint16_t sh;
+        float m;
+        sym_scale(am, c, clip, &sh, &m);
+        *(uint32_t*)(q + row * (d / 2) + i / 2) = (CLAMP || (sh & 0x7fffu) < 0x0400u)
+                                                      ? quant_pack8<true>(v, m)
+                                                      : quant_pack8<false>(v, m);
+        if ((i & (group - 1)) == 0) scale[row * (d / group) + i / group] = sh;
+      }
+    } else if (MODE == MODE_QUANT || MODE == MODE_QUANT8) {
       // 4. amax over the row
       float am = 0.0f;
       for (int i = tid; i < d; i += 256) am = fmaxf(am, fabsf(buf[pad(i)]));
@@ -1532,7 +1556,7 @@ static qr_status launch_small(int d, int rot, const uint16_t* x, int64_t T, int6
 template <int M, int MODE, bool CLAMP, bool ROT>
 static qr_status launch_lds_t(int d, int n, const uint16_t* x, int64_t T, int64_t ld,
                               const int8_t* s, float c, float clip, uint8_t* q, uint16_t* sc,
-                              float* z, void* y, hipStream_t st, int bits = 4) {
+                              float* z, void* y, hipStream_t st, int bits = 4, int group = 0) {
   const int plen = (d + (d >> 5)) + 1;
   const size_t bytes = ((size_t)((M == 172 && ROT) ? 2 : 1) * plen + 8) * sizeof(float);
   if (bytes > 160 * 1024) return QR_ERR_UNSUPPORTED;
@@ -1542,8 +1566,8 @@ static qr_status launch_lds_t(int d, int n, const uint16_t* x, int64_t T, int64_
                           (int)bytes) != hipSuccess)
     return QR_ERR_LAUNCH;
   const int grid = grid_for(T, 1, 2048);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), bytes, st, x, T, d, n, ld, s, c, clip, bits, q,
-                     sc, z, y);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), bytes, st, x, T, d, n, ld, s, c, clip, bits,
+                     group, q, sc, z, y);
   return launch_status();
 }
 
@@ -1622,9 +1646,58 @@ static qr_status dispatch_q8(const uint16_t* x, int64_t T, int32_t d, int64_t ld
                                                      nullptr, st, bits);
 }
 
+// Group-wise scales: every width through the LDS-staged kernel.
+template <bool CLAMP>
+static qr_status dispatch_groups(const uint16_t* x, int64_t T, int32_t d, int64_t ld, int rot,
+                                 const int8_t* signs, float clip, int group, uint8_t* q,
+                                 uint16_t* sc, float* z, hipStream_t st) {
+  if (!rot)
+    return launch_lds_t<1, MODE_QUANT_GROUPS, CLAMP, false>(d, 0, x, T, ld, signs, 1.0f, clip, q,
+                                                            sc, z, nullptr, st, 4, group);
+  int n = 0, m = 0;
+  if (!factor_width(d, &n, &m)) return QR_ERR_UNSUPPORTED;
+  const float c = norm_constant(d);
+  if (m == 1)
+    return launch_lds_t<1, MODE_QUANT_GROUPS, CLAMP, true>(d, n, x, T, ld, signs, c, clip, q, sc,
+                                                           z, nullptr, st, 4, group);
+  if (m == 28)
+    return launch_lds_t<28, MODE_QUANT_GROUPS, CLAMP, true>(d, n, x, T, ld, signs, c, clip, q, sc,
+                                                            z, nullptr, st, 4, group);
+  return launch_lds_t<172, MODE_QUANT_GROUPS, CLAMP, true>(d, n, x, T, ld, signs, c, clip, q, sc,
+                                                           z, nullptr, st, 4, group);
+}
+
 }  // namespace qr
 
 using namespace qr;
+
+extern "C" qr_status qr_hadamard_quant_groups(const void* x_f16, int64_t T, int32_t d,
+                                              int64_t ld_x, qr_rot rot, const int8_t* signs,
+                                              float clip_ratio, int32_t group, void* q_u8,
+                                              void* scale_f16, float* z_dbg, hipStream_t stream) {
+  if (T < 0 || d <= 0 || ld_x < d) return QR_ERR_SHAPE;
+  if (rot != QR_ROT_NONE && rot != QR_ROT_HADAMARD) return QR_ERR_ARG;
+  if (!valid_clip(clip_ratio)) return QR_ERR_ARG;
+  if (group < 8 || group > 512 || (group & (group - 1)) || d % group) return QR_ERR_UNSUPPORTED;
+  int n = 0, m = 0;
+  if (rot != QR_ROT_NONE) {
+    if (!factor_width(d, &n, &m)) return QR_ERR_UNSUPPORTED;
+  } else if (d % 8 != 0 || d > 32768) {
+    return QR_ERR_UNSUPPORTED;
+  }
+  if (T == 0) return QR_OK;
+  if (!x_f16 || !q_u8 || !scale_f16) return QR_ERR_NULL;
+  if (ld_x % 8 != 0 || !aligned(x_f16, 16) || !aligned(q_u8, 4) || !aligned(scale_f16, 2) ||
+      (z_dbg && !aligned(z_dbg, 16)) || (signs && !aligned(signs, 4)))
+    return QR_ERR_ALIGN;
+  const int r = rot == QR_ROT_HADAMARD ? 1 : 0;
+  const uint16_t* x = (const uint16_t*)x_f16;
+  if (clip_ratio < 1.0f)
+    return dispatch_groups<true>(x, T, d, ld_x, r, signs, clip_ratio, group, (uint8_t*)q_u8,
+                                 (uint16_t*)scale_f16, z_dbg, stream);
+  return dispatch_groups<false>(x, T, d, ld_x, r, signs, clip_ratio, group, (uint8_t*)q_u8,
+                                (uint16_t*)scale_f16, z_dbg, stream);
+}
 
 extern "C" qr_status qr_hadamard_quant_i8(const void* x_f16, int64_t T, int32_t d, int64_t ld_x,
                                           qr_rot rot, const int8_t* signs, float clip_ratio,

@@ -239,6 +239,21 @@ qr_status qr_hadamard_heads_quant_i8(const void* x_f16, int64_t T, int32_t n_hea
                                      hipStream_t stream);
 
 /*
+ * Group-wise scales (QuaRot paper: group-wise quantization with different group
+ * sizes, one of its studied variants).  As qr_hadamard_quant, but the row is
+ * cut into groups of `group` consecutive elements and each group gets its own
+ * scale, with the same fp32 recipe applied per group:
+ *   scale_f16  [T, d / group] fp16 (output, row-major);
+ *   q_u8       [T, d/2] packed INT4 codes, as qr_hadamard_quant.
+ * group: a power of two with 8 <= group <= 512 dividing d.  Every width runs the
+ * LDS-staged kernel (one workgroup per row).  qr_w4a4_gemm_groups consumes these.
+ */
+qr_status qr_hadamard_quant_groups(const void* x_f16, int64_t T, int32_t d, int64_t ld_x,
+                                   qr_rot rot, const int8_t* signs, float clip_ratio,
+                                   int32_t group, void* q_u8, void* scale_f16, float* z_dbg,
+                                   hipStream_t stream);
+
+/*
  * GEMM on codes stored one per byte (b <= 8 bits, for example the outputs of
  * the _i8 quantizers above), with the epilogue of qr_w4a4_gemm:
  *   acc[t, n] = sum_k A[t, k] W[n, k]   (int32, exact: |acc| <= 2^14 K < 2^31),

@@ -35,7 +35,7 @@ def test_header_declares_the_path():
                  "qr_kv_decode_attention", "qr_kv_decode_workspace_bytes",
                  "qr_rmsnorm_quant", "qr_hadamard_heads_quant", "qr_hadamard_quant_i8",
                  "qr_rmsnorm_quant_i8", "qr_hadamard_heads_quant_i8", "qr_w8a8_gemm",
-                 "qr_kv_rotate_quant_bits",
+                 "qr_kv_rotate_quant_bits", "qr_hadamard_quant_groups",
                  "qr_hadamard_factor", "qr_status_str", "qr_abi_version"):
         assert must in names
 
@@ -255,6 +255,18 @@ def test_i8_quantizers_validation(lib):
     assert h(A16, 0, 64, 128, 8192, 1.0, 6, A8, A16, None, None) == QR_OK
     assert h(A16, 4, 64, 128, 8192, 1.0, 12, A8, A16, None, None) == QR_ERR_ARG
     assert h(A16, 4, 48, 128, 6144, 1.0, 8, A8, A16, None, None) == QR_ERR_UNSUPPORTED
+
+
+def test_groups_quantizer_validation(lib):
+    f = lib.qr_hadamard_quant_groups
+    assert f(A16, 0, 8192, 8192, 1, None, 1.0, 128, A16, A16, None, None) == QR_OK
+    assert f(A16, 0, 28672, 28672, 1, None, 1.0, 512, A16, A16, None, None) == QR_OK
+    assert f(A16, 4, 8192, 8192, 1, None, 1.0, 96, A16, A16, None, None) == QR_ERR_UNSUPPORTED
+    assert f(A16, 4, 8192, 8192, 1, None, 1.0, 1024, A16, A16, None, None) == QR_ERR_UNSUPPORTED
+    assert f(A16, 4, 8192, 8192, 1, None, 1.0, 4, A16, A16, None, None) == QR_ERR_UNSUPPORTED
+    assert f(A16, 4, 11008, 11008, 1, None, 1.0, 512, A16, A16, None, None) == QR_ERR_UNSUPPORTED
+    assert f(A16, 4, 8192, 8192, 2, None, 1.0, 128, A16, A16, None, None) == QR_ERR_ARG
+    assert f(None, 4, 8192, 8192, 1, None, 1.0, 128, A16, A16, None, None) == QR_ERR_NULL
 
 
 def test_w8a8_gemm_validation(lib):

@@ -1,0 +1,94 @@
+"""GPU parity of the group-wise variant (one scale per group of consecutive k;
+QuaRot paper, group-wise quantization study) against the oracle, through the
+C ABI: qr_hadamard_quant_groups, and qr_w4a4_gemm_groups when present.
+
+Rules: R1 on the transform; per group, scales equal or one fp16 ulp apart and
+codes equal or +-1 within 1e-3 of a .5 boundary against float64; bit-exact
+codes and scales against the oracle's fp32 recipe on the GPU's own z; the
+GEMM bit-exact against the oracle's fp32 recipe.
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import gemm as og
+from oracle import hadamard as oh
+from oracle import quant as oq
+
+from parity import TIE_TOL, check_rotation, f16_ulp_diff
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+qr = pytest.importorskip("hadamard_rotation_int4_amd")
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def check_group_codes(q_packed, s_gpu, y64, group, clip):
+    T, d = y64.shape
+    yg = y64.reshape(T, d // group, group)
+    q_ref, s_ref = oq.sym_quant_math(yg, clip)
+    assert f16_ulp_diff(s_gpu, s_ref).max() <= 1
+    q = oq.unpack_int4(q_packed).reshape(T, d // group, group).astype(np.int64)
+    diff = q - q_ref.astype(np.int64)
+    assert np.abs(diff).max(initial=0) <= 1
+    tie = oq.tie_distance(yg, s_ref)
+    s_r = s_ref.astype(np.float64)
+    shift = np.where(s_r > 0, 7.5 * np.abs(s_gpu.astype(np.float64) - s_r) / np.where(s_r > 0, s_r, 1), 0)
+    assert not ((diff != 0) & (tie >= TIE_TOL + shift[..., None])).any()
+
+
+@pytest.mark.parametrize("group", [64, 128, 256])
+@pytest.mark.parametrize("d", [512, 4096, 8192, 11008, 28672])
+def test_quant_groups(d, group):
+    if d % group:
+        pytest.skip("group does not divide d")
+    T = 11
+    x = wl.activations(80, 0, T, d, n_outliers=min(5, d // 8))
+    s = wl.signs(80, d)
+    q, sc, z = (host(t) for t in qr.hadamard_quant_groups(dev(x), dev(s), 1.0, group, z_dbg=True))
+    assert sc.shape == (T, d // group)
+    z64 = oh.rotate_unnormalised(x.astype(np.float64), s)
+    check_rotation(z, z64)
+    check_group_codes(q, sc, z64 / np.sqrt(d), group, 1.0)
+    c = np.full(T, oq.norm_constant(d, True), np.float32)
+    q_rec, s_rec = oq.sym_quant_groups_recipe(z, c, group)
+    assert np.array_equal(sc.view(np.uint16), s_rec.view(np.uint16))
+    assert np.array_equal(q, oq.pack_int4(q_rec))
+
+
+@pytest.mark.parametrize("clip", [1.0, 0.5])
+def test_quant_groups_no_rotation_edge_rows(clip):
+    d, group = 4096, 128
+    x = wl.grid_activations(81, 0, 6, d)
+    x[0] = 0.0                                          # zero row: every scale 0
+    x[1, :group] = 0.0                                  # one zero group
+    x[2, 5] = 60000.0                                   # one huge group
+    x[3] = (x[3].astype(np.float64) * 2.0 ** -20).astype(np.float16)  # subnormal scales
+    q, sc, z = (host(t) for t in qr.hadamard_quant_groups(dev(x), None, clip, group, rotate=False,
+                                                          z_dbg=True))
+    assert np.array_equal(z, x.astype(np.float32))
+    q_rec, s_rec = oq.sym_quant_groups_recipe(x.astype(np.float32), np.ones(6, np.float32), group,
+                                              clip)
+    assert np.array_equal(sc.view(np.uint16), s_rec.view(np.uint16))
+    assert np.array_equal(q, oq.pack_int4(q_rec))
+    assert not sc[0].any() and sc[1, 0] == 0
+
+
+def test_quant_groups_one_group_is_the_per_token_quantizer():
+    # group = d on an exact input: the same codes and scales as qr_hadamard_quant
+    d = 512
+    x = wl.grid_activations(82, 0, 9, d)
+    s = wl.signs(82, d)
+    qg, sg = qr.hadamard_quant_groups(dev(x), dev(s), 1.0, 512)
+    q, sc = qr.hadamard_quant(dev(x), dev(s), 1.0)
+    assert np.array_equal(host(qg), host(q))
+    assert np.array_equal(host(sg)[:, 0].view(np.uint16), host(sc).view(np.uint16))
