@@ -19,6 +19,7 @@ Functions (same names as the C entry points without the ``qr_`` prefix):
       -> (q_i8, scale_f16[, dbg]): b-bit codes one per byte (2 <= bits <= 8)
   w8a8_gemm(a_q, a_scale, w_q, w_scale, acc_dbg=False) -> y_f16[, acc_i32]
   hadamard_quant_groups(x, signs, clip_ratio, group) -> (q_u8, scale_f16 [T, d/group][, z])
+  w4a4_gemm_groups(a_q, a_scale [T, K/group], w_q, w_scale [N, K/group], group) -> y_f16
   hadamard_factor(d) -> (n, m);  abi_version();  status_str(code)
 """
 from __future__ import annotations
@@ -76,6 +77,8 @@ def _load():
     lib.qr_hadamard_quant_groups.restype = ctypes.c_int
     lib.qr_hadamard_quant_groups.argtypes = [vp, i64, i32, i64, ctypes.c_int, vp, f32, i32, vp, vp,
                                              vp, vp]
+    lib.qr_w4a4_gemm_groups.restype = ctypes.c_int
+    lib.qr_w4a4_gemm_groups.argtypes = [vp, vp, i64, vp, vp, i64, i64, i32, vp, vp]
     lib.qr_w8a8_gemm.restype = ctypes.c_int
     lib.qr_w8a8_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp, vp]
     lib.qr_kv_rotate_quant_bits.restype = ctypes.c_int
@@ -361,6 +364,34 @@ def w4a4_gemm(a_q, a_scale, w_q, w_scale, acc_dbg: bool = False, out=None, strea
 def w8a8_gemm(a_q, a_scale, w_q, w_scale, acc_dbg: bool = False, out=None, stream=None):
     """Y fp16 [T, N] = dequant(A_q W_q^T); a_q int8 [T, K], w_q int8 [N, K] (codes one per byte)."""
     return _gemm(a_q, a_scale, w_q, w_scale, acc_dbg, out, stream, True)
+
+
+def w4a4_gemm_groups(a_q, a_scale, w_q, w_scale, group: int, out=None, stream=None):
+    """Y fp16 [T, N] with group-wise scales: a_q uint8 [T, K/2], a_scale fp16 [T, K/group],
+    w_q uint8 [N, K/2], w_scale fp16 [N, K/group]."""
+    torch = _torch()
+    _need(a_q, torch.uint8, "a_q", 2)
+    _need(w_q, torch.uint8, "w_q", 2)
+    _need(a_scale, torch.float16, "a_scale", 2)
+    _need(w_scale, torch.float16, "w_scale", 2)
+    for name, t in (("a_q", a_q), ("w_q", w_q), ("a_scale", a_scale), ("w_scale", w_scale)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    T, kh = a_q.shape
+    N, kh2 = w_q.shape
+    K = 2 * kh
+    if kh != kh2 or group <= 0 or K % group or tuple(a_scale.shape) != (T, K // group) or \
+            tuple(w_scale.shape) != (N, K // group):
+        raise ValueError("inconsistent GEMM operand shapes")
+    y = torch.empty((T, N), dtype=torch.float16, device=a_q.device) if out is None else out
+    if out is not None:
+        _need(y, torch.float16, "out", 2)
+        if tuple(y.shape) != (T, N) or not y.is_contiguous():
+            raise ValueError("out must be a contiguous fp16 [T, N] tensor")
+    code = _load().qr_w4a4_gemm_groups(_ptr(a_q), _ptr(a_scale), T, _ptr(w_q), _ptr(w_scale), N,
+                                       K, int(group), _ptr(y), _stream(stream))
+    _check(code, "qr_w4a4_gemm_groups")
+    return y
 
 
 def _gemm(a_q, a_scale, w_q, w_scale, acc_dbg, out, stream, i8):

@@ -92,11 +92,16 @@ struct GemmTile {
 // BITS = 8: codes stored one per byte (K bytes per row, b <= 8 bits), fed to
 // the matrix cores as loaded; the LDS geometry (128 bytes per row and step)
 // is the same, so a K step covers 128 instead of 256 elements.
-template <int WM, int WN, bool DBG, bool KTAIL, int BITS = 4>
+// GROUPED (INT4 only): one scale per group of `kgroup` consecutive k on both
+// operands (a_scale [T, K/kgroup], w_scale [N, K/kgroup]).  After each pair of
+// MFMA steps that closes a group, every accumulator is scaled by its group's
+// token and channel scales, added to an fp32 sum and reset.
+template <int WM, int WN, bool DBG, bool KTAIL, int BITS = 4, bool GROUPED = false>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
     const uint8_t* __restrict__ A, const uint16_t* __restrict__ a_scale, int T,
     const uint8_t* __restrict__ W, const uint16_t* __restrict__ w_scale, int N, int K,
-    uint16_t* __restrict__ Y, int32_t* __restrict__ acc_dbg, int tiles_m, int tiles_n) {
+    uint16_t* __restrict__ Y, int32_t* __restrict__ acc_dbg, int tiles_m, int tiles_n,
+    int kgroup = 0) {
   using Tl = GemmTile<WM, WN, BITS>;
   using CF = CodeFmt<BITS>;
   constexpr int BM = Tl::BM, BN = Tl::BN;
@@ -188,6 +193,48 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
+  // group-wise scales: fp32 sums of the scaled per-group accumulators
+  constexpr int GW = GROUPED ? WM : 1, GN = GROUPED ? WN : 1;
+  float facc[GW][GN][16];
+  if constexpr (GROUPED) {
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) facc[i][j][r] = 0.0f;
+  }
+  const int ngroups = GROUPED ? K / kgroup : 1;
+  // after pair p of K step ks: if that closes group g, f += fp32(fp32(fp32(acc) * a_s[t, g]) * w_s[n, g])
+  auto rescale = [&](int ks, int p) {
+    if constexpr (GROUPED) {
+      const int done = ks * CF::BKE + 64 * (p + 1);
+      if (done % kgroup != 0 || done > K) return;
+      const int gi = done / kgroup - 1;
+      float wsg[WN];
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+        wsg[j] = h2f(w_scale[(int64_t)min(n0 + wn + j * 32 + li, N - 1) * ngroups + gi]);
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        float asg[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = min(m0 + wm + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3), T - 1);
+          asg[r] = h2f(a_scale[(int64_t)t * ngroups + gi]);
+        }
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pr = __fmul_rn(__fmul_rn((float)(acc[i][j][r] >> CF::SHIFT), asg[r]), wsg[j]);
+            facc[i][j][r] = __fadd_rn(facc[i][j][r], pr);
+            acc[i][j][r] = 0;
+          }
+      }
+    }
+  };
+
   // Register pipeline per chunk pair p: packed fragments f (read one pair
   // ahead), unpacked halves ua/ub[0] (e = 0) and [1] (e = 1).  While the MFMAs
   // of one half run, the VALU unpacks the other and the LDS reads of the next
@@ -246,6 +293,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
           __builtin_amdgcn_sched_group_barrier(0x002, Tl::VPM, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
+        rescale(ks, p);
       } else {
         __builtin_amdgcn_sched_barrier(0);
         mfma_half(ua[0], ub[0]);
@@ -275,6 +323,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
           mfma_half(ua[1], ub[1]);
         }
         __builtin_amdgcn_sched_barrier(0);
+        rescale(ks, p);
       }
     }
   };
@@ -291,16 +340,20 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
   // ---- epilogue: 32x32 accumulator layout: lane (n = li, k-half lg), register r
   //      holds row 8 (r / 4) + 4 lg + (r % 4) ----
   float wsc[WN];
+  if constexpr (!GROUPED) {
 #pragma unroll
-  for (int j = 0; j < WN; ++j) wsc[j] = h2f(w_scale[min(n0 + wn + j * 32 + li, N - 1)]);
+    for (int j = 0; j < WN; ++j) wsc[j] = h2f(w_scale[min(n0 + wn + j * 32 + li, N - 1)]);
+  }
 #pragma unroll
   for (int i = 0; i < WM; ++i) {
     float asc[16];  // [r]: rows 8 (r / 4) + 4 lg + (r % 4) of block i
+    if constexpr (!GROUPED) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int t0 = m0 + wm + i * 32 + 8 * q4 + 4 * lg;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int t0 = m0 + wm + i * 32 + 8 * q4 + 4 * lg;
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) asc[4 * q4 + s2] = h2f(a_scale[min(t0 + s2, T - 1)]);
+        for (int s2 = 0; s2 < 4; ++s2) asc[4 * q4 + s2] = h2f(a_scale[min(t0 + s2, T - 1)]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
@@ -310,21 +363,25 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
       for (int r = 0; r < 16; ++r) {
         const int t = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
         if (t < T) {
-          const int32_t a = acc[i][j][r] >> CF::SHIFT;  // exact (INT4: 256 * acc)
-          Y[(int64_t)t * N + n] = f2h(__fmul_rn(__fmul_rn((float)a, asc[r]), wsc[j]));
-          if (DBG) acc_dbg[(int64_t)t * N + n] = a;
+          if constexpr (GROUPED) {
+            Y[(int64_t)t * N + n] = f2h(facc[i][j][r]);
+          } else {
+            const int32_t a = acc[i][j][r] >> CF::SHIFT;  // exact (INT4: 256 * acc)
+            Y[(int64_t)t * N + n] = f2h(__fmul_rn(__fmul_rn((float)a, asc[r]), wsc[j]));
+            if (DBG) acc_dbg[(int64_t)t * N + n] = a;
+          }
         }
       }
     }
   }
 }
 
-template <int WM, int WN, bool DBG, bool KTAIL, int BITS>
+template <int WM, int WN, bool DBG, bool KTAIL, int BITS, bool GROUPED = false>
 static qr_status launch_gemm(const void* a_q, const void* a_scale, int64_t T, const void* w_q,
                              const void* w_scale, int64_t N, int64_t K, void* y, int32_t* acc,
-                             hipStream_t stream) {
+                             hipStream_t stream, int group = 0) {
   using Tl = GemmTile<WM, WN, BITS>;
-  auto kern = k_w4a4_gemm<WM, WN, DBG, KTAIL, BITS>;
+  auto kern = k_w4a4_gemm<WM, WN, DBG, KTAIL, BITS, GROUPED>;
   // Opting in to more than 64 KB of LDS is a per-kernel attribute; setting it
   // again on every call is cheap and keeps the entry point free of state.
   if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -337,7 +394,7 @@ static qr_status launch_gemm(const void* a_q, const void* a_scale, int64_t T, co
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(GEMM_THREADS), Tl::LDS, stream,
                      (const uint8_t*)a_q, (const uint16_t*)a_scale, (int)T, (const uint8_t*)w_q,
                      (const uint16_t*)w_scale, (int)N, (int)K, (uint16_t*)y, acc, tiles_m,
-                     tiles_n);
+                     tiles_n, group);
   return launch_status();
 }
 
@@ -626,4 +683,25 @@ extern "C" qr_status qr_w8a8_gemm(const void* a_q, const void* a_scale_f16, int6
   if (s42 >= s24)
     return launch_tile<4, 2, 8>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
   return launch_tile<2, 4, 8>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
+}
+
+extern "C" qr_status qr_w4a4_gemm_groups(const void* a_q, const void* a_scale_f16, int64_t T,
+                                         const void* w_q, const void* w_scale_f16, int64_t N,
+                                         int64_t K, int32_t group, void* y_f16,
+                                         hipStream_t stream) {
+  if (T < 0 || N < 0 || K <= 0) return QR_ERR_SHAPE;
+  if (K % 64 != 0 || K > 131008) return QR_ERR_UNSUPPORTED;
+  if (group < 64 || group > 512 || (group & (group - 1)) || K % group) return QR_ERR_UNSUPPORTED;
+  if (T > INT32_MAX / 2 || N > INT32_MAX / 2) return QR_ERR_SHAPE;
+  if (T == 0 || N == 0) return QR_OK;
+  if (!a_q || !a_scale_f16 || !w_q || !w_scale_f16 || !y_f16) return QR_ERR_NULL;
+  if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(y_f16, 4) || !aligned(a_scale_f16, 2) ||
+      !aligned(w_scale_f16, 2))
+    return QR_ERR_ALIGN;
+  // 128 x 128 tiles: the fp32 sums sit beside the int32 accumulators
+  const bool tail = (K % CodeFmt<4>::BKE) != 0;
+  return tail ? launch_gemm<2, 2, false, true, 4, true>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K,
+                                                        y_f16, nullptr, stream, (int)group)
+              : launch_gemm<2, 2, false, false, 4, true>(a_q, a_scale_f16, T, w_q, w_scale_f16, N,
+                                                         K, y_f16, nullptr, stream, (int)group);
 }

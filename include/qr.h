@@ -254,6 +254,21 @@ qr_status qr_hadamard_quant_groups(const void* x_f16, int64_t T, int32_t d, int6
                                    hipStream_t stream);
 
 /*
+ * W4A4 GEMM with group-wise scales on both operands (the outputs of
+ * qr_hadamard_quant_groups for the activations and for the weights, T := N):
+ *   acc_g[t, n] = sum over k in group g of A[t, k] W[n, k]   (int32, exact),
+ *   f = 0;  for g = 0, 1, ...:  f = fp32(f + fp32(fp32(fp32(acc_g) * a_scale[t, g])
+ *                                                * w_scale[n, g])),
+ *   Y[t, n] = fp16(f).
+ *   a_scale [T, K/group], w_scale [N, K/group] fp16 (row-major); codes as
+ *   qr_w4a4_gemm.  group: a power of two, 64 <= group <= 512, dividing K.
+ * Requirements as qr_w4a4_gemm (no accumulator output).
+ */
+qr_status qr_w4a4_gemm_groups(const void* a_q, const void* a_scale_f16, int64_t T, const void* w_q,
+                              const void* w_scale_f16, int64_t N, int64_t K, int32_t group,
+                              void* y_f16, hipStream_t stream);
+
+/*
  * GEMM on codes stored one per byte (b <= 8 bits, for example the outputs of
  * the _i8 quantizers above), with the epilogue of qr_w4a4_gemm:
  *   acc[t, n] = sum_k A[t, k] W[n, k]   (int32, exact: |acc| <= 2^14 K < 2^31),

@@ -35,7 +35,7 @@ def test_header_declares_the_path():
                  "qr_kv_decode_attention", "qr_kv_decode_workspace_bytes",
                  "qr_rmsnorm_quant", "qr_hadamard_heads_quant", "qr_hadamard_quant_i8",
                  "qr_rmsnorm_quant_i8", "qr_hadamard_heads_quant_i8", "qr_w8a8_gemm",
-                 "qr_kv_rotate_quant_bits", "qr_hadamard_quant_groups",
+                 "qr_kv_rotate_quant_bits", "qr_hadamard_quant_groups", "qr_w4a4_gemm_groups",
                  "qr_hadamard_factor", "qr_status_str", "qr_abi_version"):
         assert must in names
 
@@ -267,6 +267,17 @@ def test_groups_quantizer_validation(lib):
     assert f(A16, 4, 11008, 11008, 1, None, 1.0, 512, A16, A16, None, None) == QR_ERR_UNSUPPORTED
     assert f(A16, 4, 8192, 8192, 2, None, 1.0, 128, A16, A16, None, None) == QR_ERR_ARG
     assert f(None, 4, 8192, 8192, 1, None, 1.0, 128, A16, A16, None, None) == QR_ERR_NULL
+
+
+def test_groups_gemm_validation(lib):
+    f = lib.qr_w4a4_gemm_groups
+    assert f(A16, A16, 0, A16, A16, 16, 4096, 128, A16, None) == QR_OK
+    assert f(A16, A16, 16, A16, A16, 16, 4096, 96, A16, None) == QR_ERR_UNSUPPORTED
+    assert f(A16, A16, 16, A16, A16, 16, 4096, 32, A16, None) == QR_ERR_UNSUPPORTED
+    assert f(A16, A16, 16, A16, A16, 16, 4096, 1024, A16, None) == QR_ERR_UNSUPPORTED
+    assert f(A16, A16, 16, A16, A16, 16, 4160, 128, A16, None) == QR_ERR_UNSUPPORTED  # 128 !| K
+    assert f(None, A16, 16, A16, A16, 16, 4096, 128, A16, None) == QR_ERR_NULL
+    assert f(A16, A16, -1, A16, A16, 16, 4096, 128, A16, None) == QR_ERR_SHAPE
 
 
 def test_w8a8_gemm_validation(lib):

@@ -92,3 +92,43 @@ def test_quant_groups_one_group_is_the_per_token_quantizer():
     q, sc = qr.hadamard_quant(dev(x), dev(s), 1.0)
     assert np.array_equal(host(qg), host(q))
     assert np.array_equal(host(sg)[:, 0].view(np.uint16), host(sc).view(np.uint16))
+
+
+def scales(seed, rows, groups, lo=1e-3, hi=1e-1):
+    g = np.random.default_rng(seed)
+    return np.exp(g.uniform(np.log(lo), np.log(hi), size=(rows, groups))).astype(np.float16)
+
+
+@pytest.mark.parametrize("group", [64, 128, 256, 512])
+@pytest.mark.parametrize("T,N,K", [(37, 100, 4096), (300, 260, 2048), (129, 513, 1536), (1, 64, 512),
+                                   (256, 256, 11008), (70, 90, 4160)])
+def test_gemm_groups_bit_exact(T, N, K, group):
+    if K % group:
+        pytest.skip("group does not divide K")
+    a = wl.packed_codes(83, T, T, K)
+    w = wl.packed_codes(83, 1000 + N, N, K)
+    asc, wsc = scales(T + group, T, K // group), scales(N + group, N, K // group)
+    y = host(qr.w4a4_gemm_groups(dev(a), dev(asc), dev(w), dev(wsc), group))
+    y_ref, _ = og.w4a4_gemm_groups_recipe(a, asc, w, wsc, group)
+    assert np.array_equal(y.view(np.uint16), y_ref.view(np.uint16))
+
+
+def test_linear_groups_end_to_end():
+    # rotated X and W quantized group-wise, then the grouped GEMM: bit-exact on
+    # the GPU's codes, and closer to X W^T than per-token / per-channel scales
+    T, N, K, group = 64, 512, 4096, 128
+    x = wl.activations(84, 0, T, K, n_outliers=4, lo=50, hi=50)
+    w = wl.weights(84, 1, N, K)
+    s = dev(wl.signs(84, K))
+    qa, sa = qr.hadamard_quant_groups(dev(x), s, 1.0, group)
+    qw, sw = qr.hadamard_quant_groups(dev(w), s, 1.0, group)
+    y = host(qr.w4a4_gemm_groups(qa, sa, qw, sw, group)).astype(np.float64)
+    y_ref, _ = og.w4a4_gemm_groups_recipe(host(qa), host(sa), host(qw), host(sw), group)
+    assert np.array_equal(y.astype(np.float16).view(np.uint16), y_ref.view(np.uint16))
+    qa1, sa1 = qr.hadamard_quant(dev(x), s, 1.0)
+    qw1, sw1 = qr.hadamard_quant(dev(w), s, 1.0)
+    y1 = host(qr.w4a4_gemm(qa1, sa1, qw1, sw1)).astype(np.float64)
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    err_g = np.linalg.norm(y - exact) / np.linalg.norm(exact)
+    err_t = np.linalg.norm(y1 - exact) / np.linalg.norm(exact)
+    assert err_g < err_t, (err_g, err_t)
