@@ -66,7 +66,8 @@ KERNEL_SOURCE = {"w4a4_gemm": "w4a4_gemm.hip", "hadamard_quant": "hadamard_quant
                  "kv_decode_attention": "kv_decode.hip", "rmsnorm_quant": "block_quant.hip",
                  "hadamard_heads_quant": "block_quant.hip", "w8a8_gemm": "w4a4_gemm.hip",
                  "hadamard_quant_i8": "hadamard_quant.hip", "rmsnorm_quant_i8": "block_quant.hip",
-                 "hadamard_heads_quant_i8": "block_quant.hip"}
+                 "hadamard_heads_quant_i8": "block_quant.hip",
+                 "hadamard_quant_groups": "hadamard_quant.hip", "w4a4_gemm_groups": "w4a4_gemm.hip"}
 
 
 def parse():
@@ -80,6 +81,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--group", type=int, default=0,
+                    help="prefill workloads: group-wise scales of this group size on both GEMM "
+                         "operands (group-wise quantizer and grouped GEMM)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the fp16 / hipBLASLt int8 context timings of the block workloads")
     ap.add_argument("--fp16-hadamard", action="store_true",
@@ -135,7 +139,8 @@ def gemm8_bytes(T, N, K):
     return T * K + N * K + 2 * T + 2 * N + 2 * T * N
 
 
-def make_block(torch, qr, wl, W, T, dev, with_kv, f16_down=False, quarot=False, bits=4):
+def make_block(torch, qr, wl, W, T, dev, with_kv, f16_down=False, quarot=False, bits=4,
+               group=0):
     lin = {l.name: l for l in W.linears}
     H, ffn, wid = W.hidden, lin["down"].k, W.wid
     inputs = {}
@@ -151,15 +156,23 @@ def make_block(torch, qr, wl, W, T, dev, with_kv, f16_down=False, quarot=False, 
     for i, (name, l) in enumerate(lin.items()):
         w = wl.weights_torch(torch, dev, wid, 1 + i, l.n, l.k)
         wq[name] = (qr.hadamard_quant_i8(w, signs[l.k], 1.0, bits) if i8
+                    else qr.hadamard_quant_groups(w, signs[l.k], 1.0, group) if group
                     else qr.hadamard_quant(w, signs[l.k], 1.0))
         del w
     qbuf = {n: (torch.empty((T, x.shape[1]) if i8 else (T, x.shape[1] // 2),
                             dtype=torch.int8 if i8 else torch.uint8, device=dev),
-                torch.empty((T,), dtype=torch.float16, device=dev)) for n, x in inputs.items()}
+                torch.empty((T, x.shape[1] // group) if group else (T,), dtype=torch.float16,
+                            device=dev)) for n, x in inputs.items()}
     ybuf = {n: torch.empty((T, l.n), dtype=torch.float16, device=dev) for n, l in lin.items()}
     L = []
     tag = f"T{T}:" if not with_kv else ""
     for name, x in inputs.items():
+        if group:
+            L.append(("hadamard_quant_groups", tag + name, T * (2 * x.shape[1] + x.shape[1] // 2
+                                                              + 2 * (x.shape[1] // group)), 0,
+                      (lambda x=x, name=name: qr.hadamard_quant_groups(
+                          x, signs[x.shape[1]], 1.0, group, out=qbuf[name])), qbuf[name]))
+            continue
         if i8:
             # b-bit codes one per byte: the model's online path with the _i8 quantizers
             if name in ("attn_in", "ffn_in"):
@@ -193,6 +206,13 @@ def make_block(torch, qr, wl, W, T, dev, with_kv, f16_down=False, quarot=False, 
                   (lambda x=x, name=name, f16=f16: qr.hadamard_quant(
                       x, signs[x.shape[1]], 1.0, out=qbuf[name], fp16_transform=f16)), qbuf[name]))
     for name, l in lin.items():
+        if group:
+            L.append(("w4a4_gemm_groups", tag + name,
+                      gemm_bytes(T, l.n, l.k) + 2 * (T + l.n) * (l.k // group - 1),
+                      gemm_ops(T, l.n, l.k),
+                      (lambda name=name, l=l: qr.w4a4_gemm_groups(*qbuf[l.input], *wq[name], group,
+                                                                   out=ybuf[name])), (ybuf[name],)))
+            continue
         if i8:
             L.append(("w8a8_gemm", tag + name, gemm8_bytes(T, l.n, l.k), gemm_ops(T, l.n, l.k),
                       (lambda name=name, l=l: qr.w8a8_gemm(*qbuf[l.input], *wq[name],
@@ -456,14 +476,18 @@ def main():
     config = {"workload": None}
     if wname in ("70b_prefill", "7b_prefill") or quarot:
         T = W.tokens[0]
+        group = args.group if wname in ("70b_prefill", "7b_prefill") else 0
         launches, lin, kvdesc = make_block(torch, qr, wl, W, T, dev, True, args.fp16_hadamard,
-                                           quarot, bits)
+                                           quarot, bits, group)
         inputs_desc = ("RMSNorm (no scale) + INT4 before QKV and gate/up, Hadamard heads "
                        f"({W.hidden // 128} heads of 128) + INT4 before O, online Hadamard "
                        f"d = {lin['down'].k} + INT4 before down" if quarot
                        else "4 fused rotate+quant")
         if bits != 4:
             inputs_desc = f"{bits}-bit codes one per byte: " + inputs_desc.replace(" + INT4", "")
+        if group:
+            inputs_desc = (f"group-wise scales (group {group} along K) on both operands: 4 "
+                           "rotate+quant")
         config.update({
             "workload": f"{W.name}{' (QuaRot online path)' if quarot else ''}: T={T} tokens, "
                         f"hidden {W.hidden}, FFN {lin['down'].k}, QKV {lin['qkv'].n}; "
@@ -471,7 +495,8 @@ def main():
             "tokens": T, "hidden": W.hidden, "ffn": lin["down"].k,
             "hadamard_arithmetic": (f"fp16 for d = {lin['down'].k}, fp32 otherwise"
                                     if args.fp16_hadamard else "fp32")})
-        dominant, bound = ("w4a4_gemm" if bits == 4 else "w8a8_gemm"), "mfma"
+        dominant, bound = ("w4a4_gemm_groups" if group else "w4a4_gemm" if bits == 4
+                           else "w8a8_gemm"), "mfma"
     elif wname == "7b_decode":
         launches = []
         for T in W.tokens:
@@ -524,7 +549,7 @@ def main():
         "roofline": roofline(dominant, wname, launches, per, bound),
     }
     for k in ("hadamard_quant", "rmsnorm_quant", "hadamard_heads_quant", "hadamard_quant_i8",
-              "rmsnorm_quant_i8", "hadamard_heads_quant_i8"):
+              "rmsnorm_quant_i8", "hadamard_heads_quant_i8", "hadamard_quant_groups"):
         if any(l[0] == k for l in launches):
             out["roofline_" + k] = roofline(k, wname, launches, per, "hbm")
     if dominant != "kv_rotate_quant" and any(l[0] == "kv_rotate_quant" for l in launches):
@@ -533,7 +558,7 @@ def main():
         k: {"ms": round(sum(p for l, p in zip(launches, per) if l[0] == k), 4),
             "launches": sum(1 for l in launches if l[0] == k)}
         for k in sorted({l[0] for l in launches})}
-    if wname in ("70b_prefill", "7b_prefill") and not args.no_context:
+    if wname in ("70b_prefill", "7b_prefill") and not args.no_context and not args.group:
         out["quality"] = quality_report(torch, qr, wl, W, dev)
     if quarot and not args.no_context:
         out["fp16_context"] = fp16_context(torch, wl, W, T, dev, launches, per, args)
@@ -541,7 +566,7 @@ def main():
     out["timing"] = ("HIP graph replay of the step; per-launch times from graphs of 20 "
                      "back-to-back launches (outputs checked equal to the eager run)" if graphed
                      else "eager launches, HIP events around each launch on its stream")
-    if not args.no_cpu_baseline and wname in ("70b_prefill", "70b_block"):
+    if not args.no_cpu_baseline and wname in ("70b_prefill", "70b_block") and not args.group:
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_sample_tokens, quarot=quarot)
     print(json.dumps(out), flush=True)
     return 0

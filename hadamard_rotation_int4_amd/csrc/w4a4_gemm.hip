@@ -205,36 +205,47 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
         for (int r = 0; r < 16; ++r) facc[i][j][r] = 0.0f;
   }
   const int ngroups = GROUPED ? K / kgroup : 1;
-  // after pair p of K step ks: if that closes group g, f += fp32(fp32(fp32(acc) * a_s[t, g]) * w_s[n, g])
-  auto rescale = [&](int ks, int p) {
+  // the scales of the next group to close, fetched one group ahead so that
+  // their loads are in flight while that group's MFMAs run
+  float asg[GW][16], wsg[GN];
+  auto load_scales = [&](int gi) __attribute__((always_inline)) {
     if constexpr (GROUPED) {
-      const int done = ks * CF::BKE + 64 * (p + 1);
-      if (done % kgroup != 0 || done > K) return;
-      const int gi = done / kgroup - 1;
-      float wsg[WN];
 #pragma unroll
       for (int j = 0; j < WN; ++j)
         wsg[j] = h2f(w_scale[(int64_t)min(n0 + wn + j * 32 + li, N - 1) * ngroups + gi]);
 #pragma unroll
-      for (int i = 0; i < WM; ++i) {
-        float asg[16];
+      for (int i = 0; i < WM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = min(m0 + wm + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3), T - 1);
-          asg[r] = h2f(a_scale[(int64_t)t * ngroups + gi]);
+          asg[i][r] = h2f(a_scale[(int64_t)t * ngroups + gi]);
         }
+    }
+  };
+  if constexpr (GROUPED) load_scales(0);
+  // after pair p of K step ks: if that closes group g,
+  // f += fp32(fp32(fp32(acc) * a_s[t, g]) * w_s[n, g]) and acc = 0 (f kept x256)
+  auto rescale = [&](int ks, int p) __attribute__((always_inline)) {
+    if constexpr (GROUPED) {
+      const int done = ks * CF::BKE + 64 * (p + 1);
+      if (done % kgroup != 0 || done > K) return;
+      const int gi = done / kgroup - 1;
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
 #pragma unroll
         for (int j = 0; j < WN; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float pr = __fmul_rn(__fmul_rn((float)(acc[i][j][r] >> CF::SHIFT), asg[r]), wsg[j]);
+            // the INT4 accumulator holds 256 * acc: converting and scaling it
+            // unshifted gives exactly 256 times each fp32 step (no fp32 value
+            // here comes near the subnormal range), undone exactly at the end
+            const float pr = __fmul_rn(__fmul_rn((float)acc[i][j][r], asg[i][r]), wsg[j]);
             facc[i][j][r] = __fadd_rn(facc[i][j][r], pr);
             acc[i][j][r] = 0;
           }
-      }
+      if (gi + 1 < ngroups) load_scales(gi + 1);
     }
   };
-
   // Register pipeline per chunk pair p: packed fragments f (read one pair
   // ahead), unpacked halves ua/ub[0] (e = 0) and [1] (e = 1).  While the MFMAs
   // of one half run, the VALU unpacks the other and the LDS reads of the next
@@ -364,7 +375,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
         const int t = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
         if (t < T) {
           if constexpr (GROUPED) {
-            Y[(int64_t)t * N + n] = f2h(facc[i][j][r]);
+            Y[(int64_t)t * N + n] = f2h(__fmul_rn(facc[i][j][r], 1.0f / (1 << CF::SHIFT)));
           } else {
             const int32_t a = acc[i][j][r] >> CF::SHIFT;  // exact (INT4: 256 * acc)
             Y[(int64_t)t * N + n] = f2h(__fmul_rn(__fmul_rn((float)a, asc[r]), wsc[j]));
