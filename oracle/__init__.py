@@ -19,9 +19,13 @@ LLMs Impossible"):
   invariance" and its outlier demo).
 * ``quant``: per-token symmetric INT4 round-to-nearest (QuaRot paper,
   activation-quantization paragraph; QuaRot blog, "The outlier problem,
-  stated precisely") and nibble packing.
+  stated precisely") and nibble packing; b-bit codes one per byte (the paper's
+  6- and 8-bit RTN results) and one scale per group of G consecutive elements
+  (the paper's group-wise quantization ablation).
 * ``gemm``: the exact INT4 x INT4 -> INT32 product and the per-token x
-  per-channel scale epilogue (QuaRot paper, activation-quantization paragraph).
+  per-channel scale epilogue (QuaRot paper, activation-quantization paragraph);
+  the int8 form (W8A8) and the group-wise form, whose per-group scaled
+  accumulators are summed in fp32.
 * ``kv``: head-wise rotation of keys and queries and asymmetric group-wise
   4-bit KV quantization (QuaRot paper, keys/queries paragraph and the
   implementation paragraph on clipping ratios and group size 128).
