@@ -207,19 +207,26 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
   const int ngroups = GROUPED ? K / kgroup : 1;
   // the scales of the next group to close, fetched one group ahead so that
   // their loads are in flight while that group's MFMAs run
+  // Raw buffer loads over the tile's own scale rows: rows past T (or N) read
+  // as zero (their outputs are never stored); one 32-bit offset per load.
   float asg[GW][16], wsg[GN];
+  const __amdgpu_buffer_rsrc_t rsrc_as = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a_scale + (int64_t)m0 * ngroups), 0, rows_a * ngroups * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_ws = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(w_scale + (int64_t)n0 * ngroups), 0, rows_w * ngroups * 2, 0x00020000);
+  const int as_off = (wm + 4 * lg) * ngroups * 2, ws_off = (wn + li) * ngroups * 2;
   auto load_scales = [&](int gi) __attribute__((always_inline)) {
     if constexpr (GROUPED) {
 #pragma unroll
       for (int j = 0; j < WN; ++j)
-        wsg[j] = h2f(w_scale[(int64_t)min(n0 + wn + j * 32 + li, N - 1) * ngroups + gi]);
+        wsg[j] = h2f(__builtin_amdgcn_raw_buffer_load_b16(
+            rsrc_ws, ws_off + (j * 32 * ngroups + gi) * 2, 0, 0));
 #pragma unroll
       for (int i = 0; i < WM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = min(m0 + wm + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3), T - 1);
-          asg[i][r] = h2f(a_scale[(int64_t)t * ngroups + gi]);
-        }
+        for (int r = 0; r < 16; ++r)
+          asg[i][r] = h2f(__builtin_amdgcn_raw_buffer_load_b16(
+              rsrc_as, as_off + ((i * 32 + 8 * (r >> 2) + (r & 3)) * ngroups + gi) * 2, 0, 0));
     }
   };
   if constexpr (GROUPED) load_scales(0);
