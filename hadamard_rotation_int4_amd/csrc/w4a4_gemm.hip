@@ -95,8 +95,10 @@ struct GemmTile {
 // GROUPED (INT4 only): one scale per group of `kgroup` consecutive k on both
 // operands (a_scale [T, K/kgroup], w_scale [N, K/kgroup]).  After each pair of
 // MFMA steps that closes a group, every accumulator is scaled by its group's
-// token and channel scales, added to an fp32 sum and reset.
-template <int WM, int WN, bool DBG, bool KTAIL, int BITS = 4, bool GROUPED = false>
+// token and channel scales, added to an fp32 sum and reset.  PG = kgroup / 64
+// pairs per group when a group fits in one K step (PG <= 4): then a group's
+// first MFMAs start from a zero accumulator instead of clearing it.
+template <int WM, int WN, bool DBG, bool KTAIL, int BITS = 4, bool GROUPED = false, int PG = 0>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
     const uint8_t* __restrict__ A, const uint16_t* __restrict__ a_scale, int T,
     const uint8_t* __restrict__ W, const uint16_t* __restrict__ w_scale, int N, int K,
@@ -205,6 +207,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
         for (int r = 0; r < 16; ++r) facc[i][j][r] = 0.0f;
   }
   const int ngroups = GROUPED ? K / kgroup : 1;
+  constexpr int NP = BITS == 4 ? KCH / 2 : KCH / 4;  // MFMA pairs per step
+  constexpr bool FRESH = GROUPED && PG >= 1 && PG <= NP;
   // the scales of the next group to close, fetched one group ahead so that
   // their loads are in flight while that group's MFMAs run
   // Raw buffer loads over the tile's own scale rows: rows past T (or N) read
@@ -235,7 +239,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
   auto rescale = [&](int ks, int p) __attribute__((always_inline)) {
     if constexpr (GROUPED) {
       const int done = ks * CF::BKE + 64 * (p + 1);
-      if (done % kgroup != 0 || done > K) return;
+      // a group longer than a K step (PG > NP) closes only at a step's last pair
+      if (FRESH ? (p + 1) % PG != 0 : (PG > NP && p + 1 != NP) || done % kgroup != 0) return;
+      if (done > K) return;
       const int gi = done / kgroup - 1;
 #pragma unroll
       for (int i = 0; i < WM; ++i)
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
             // here comes near the subnormal range), undone exactly at the end
             const float pr = __fmul_rn(__fmul_rn((float)acc[i][j][r], asg[i][r]), wsg[j]);
             facc[i][j][r] = __fadd_rn(facc[i][j][r], pr);
-            acc[i][j][r] = 0;
+            if (!FRESH) acc[i][j][r] = 0;
           }
       if (gi + 1 < ngroups) load_scales(gi + 1);
     }
@@ -274,14 +280,15 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
       for (int j = 0; j < WN; ++j) ob[j] = __builtin_bit_cast(v4i, xb[e][j]);
     }
   };
-  auto mfma_half = [&](const v4i* a, const v4i* b) {
+  // fresh: the first MFMAs of a group (FRESH only) start from zero
+  auto mfma_half = [&](const v4i* a, const v4i* b, bool fresh = false) {
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
       for (int j = 0; j < WN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+            a[i], b[j], fresh ? v16i{} : acc[i][j], 0, 0, 0);
   };
-  constexpr int NP = BITS == 4 ? KCH / 2 : KCH / 4;  // MFMA pairs per step
   const int ksteps = (K + CF::BKE - 1) / CF::BKE;
   // One K step from LDS stage `stage`.  MORE: a next step exists -- stage its
   // panels (loaded one step earlier) into the other LDS stage during the last
@@ -294,7 +301,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
       if (p + 1 < NP) {
         __builtin_amdgcn_sched_barrier(0);
         lread(stage, p + 1, fa[nxt], fb[nxt]);
-        mfma_half(ua[0], ub[0]);
+        mfma_half(ua[0], ub[0], FRESH && p % PG == 0);
         unpack_half(fa[cur], fb[cur], 1, ua[1], ub[1]);
         __builtin_amdgcn_sched_group_barrier(0x100, Tl::DSR, 0);  // DS reads first
 #pragma unroll
@@ -314,7 +321,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
         rescale(ks, p);
       } else {
         __builtin_amdgcn_sched_barrier(0);
-        mfma_half(ua[0], ub[0]);
+        mfma_half(ua[0], ub[0], FRESH && p % PG == 0);
         unpack_half(fa[cur], fb[cur], 1, ua[1], ub[1]);
         if (MORE) {
           lstore(stage ^ 1);
@@ -394,12 +401,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_w4a4_gemm(
   }
 }
 
-template <int WM, int WN, bool DBG, bool KTAIL, int BITS, bool GROUPED = false>
+template <int WM, int WN, bool DBG, bool KTAIL, int BITS, bool GROUPED = false, int PG = 0>
 static qr_status launch_gemm(const void* a_q, const void* a_scale, int64_t T, const void* w_q,
                              const void* w_scale, int64_t N, int64_t K, void* y, int32_t* acc,
                              hipStream_t stream, int group = 0) {
   using Tl = GemmTile<WM, WN, BITS>;
-  auto kern = k_w4a4_gemm<WM, WN, DBG, KTAIL, BITS, GROUPED>;
+  auto kern = k_w4a4_gemm<WM, WN, DBG, KTAIL, BITS, GROUPED, PG>;
   // Opting in to more than 64 KB of LDS is a per-kernel attribute; setting it
   // again on every call is cheap and keeps the entry point free of state.
   if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -703,6 +710,28 @@ extern "C" qr_status qr_w8a8_gemm(const void* a_q, const void* a_scale_f16, int6
   return launch_tile<2, 4, 8>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
 }
 
+// one instantiation per group size: 64, 128 and 256 fit in one K step of 256
+// k, 512 spans two
+template <bool KTAIL>
+static qr_status launch_groups(const void* a_q, const void* a_s, int64_t T, const void* w_q,
+                               const void* w_s, int64_t N, int64_t K, int group, void* y,
+                               hipStream_t stream) {
+  switch (group) {
+    case 64:
+      return launch_gemm<2, 2, false, KTAIL, 4, true, 1>(a_q, a_s, T, w_q, w_s, N, K, y, nullptr,
+                                                         stream, group);
+    case 128:
+      return launch_gemm<2, 2, false, KTAIL, 4, true, 2>(a_q, a_s, T, w_q, w_s, N, K, y, nullptr,
+                                                         stream, group);
+    case 256:
+      return launch_gemm<2, 2, false, KTAIL, 4, true, 4>(a_q, a_s, T, w_q, w_s, N, K, y, nullptr,
+                                                         stream, group);
+    default:  // 512 (the only other size the entry point accepts)
+      return launch_gemm<2, 2, false, KTAIL, 4, true, 8>(a_q, a_s, T, w_q, w_s, N, K, y, nullptr,
+                                                         stream, group);
+  }
+}
+
 extern "C" qr_status qr_w4a4_gemm_groups(const void* a_q, const void* a_scale_f16, int64_t T,
                                          const void* w_q, const void* w_scale_f16, int64_t N,
                                          int64_t K, int32_t group, void* y_f16,
@@ -718,8 +747,7 @@ extern "C" qr_status qr_w4a4_gemm_groups(const void* a_q, const void* a_scale_f1
     return QR_ERR_ALIGN;
   // 128 x 128 tiles: the fp32 sums sit beside the int32 accumulators
   const bool tail = (K % CodeFmt<4>::BKE) != 0;
-  return tail ? launch_gemm<2, 2, false, true, 4, true>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K,
-                                                        y_f16, nullptr, stream, (int)group)
-              : launch_gemm<2, 2, false, false, 4, true>(a_q, a_scale_f16, T, w_q, w_scale_f16, N,
-                                                         K, y_f16, nullptr, stream, (int)group);
+  return tail ? launch_groups<true>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, group, y_f16, stream)
+              : launch_groups<false>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, group, y_f16,
+                                     stream);
 }
