@@ -437,12 +437,6 @@ static qr_status launch_tile(const void* a_q, const void* a_scale, int64_t T, co
 
 // Fraction of the machine's workgroup slots a tile grid keeps busy, times a
 // per-tile efficiency (smaller tiles re-read more operand bytes per MAC).
-static double tile_score(int64_t T, int64_t N, int bm, int bn, double eff, int slots) {
-  const int64_t tiles = ((T + bm - 1) / bm) * ((N + bn - 1) / bn);
-  const int64_t rounds = (tiles + slots - 1) / slots;
-  return eff * (double)tiles / (double)(rounds * slots);
-}
-
 // Estimated time (arbitrary units) of a grid of bm x bn tiles when `slots`
 // workgroups run at once, each at relative throughput `eff`: rounds of
 // concurrent tiles times one tile's work.  Edge tiles count whole.
@@ -450,6 +444,27 @@ static double tile_time(int64_t T, int64_t N, int bm, int bn, double eff, int sl
   const int64_t tiles = ((T + bm - 1) / bm) * ((N + bn - 1) / bn);
   const int64_t rounds = (tiles + slots - 1) / slots;
   return (double)rounds * bm * bn / eff;
+}
+
+// The 256-row/column tiles run one workgroup per compute unit (their
+// accumulators fill the register file); 128 x 128 tiles run two, which hides
+// each tile's prologue and epilogue behind the other's MFMAs but costs 8% of
+// throughput per CU.  Launch the tile with the shortest estimated time.
+template <int BITS>
+static qr_status launch_best(const void* a_q, const void* a_scale, int64_t T, const void* w_q,
+                             const void* w_scale, int64_t N, int64_t K, void* y, int32_t* acc,
+                             hipStream_t stream) {
+  const double t44 = tile_time(T, N, 256, 256, 1.0, 256);
+  const double t42 = tile_time(T, N, 256, 128, 0.9, 256);
+  const double t24 = tile_time(T, N, 128, 256, 0.9, 256);
+  const double t22 = tile_time(T, N, 128, 128, 0.46, 512);
+  if (t22 <= t44 && t22 <= t42 && t22 <= t24)
+    return launch_tile<2, 2, BITS>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
+  if (t44 <= t42 && t44 <= t24)
+    return launch_tile<4, 4, BITS>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
+  if (t42 <= t24)
+    return launch_tile<4, 2, BITS>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
+  return launch_tile<2, 4, BITS>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
 }
 
 
@@ -683,21 +698,7 @@ extern "C" qr_status qr_w4a4_gemm(const void* a_q, const void* a_scale_f16, int6
       return launch_decode<2>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
     return launch_decode<4>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
   }
-  // The 256-row/column tiles run one workgroup per compute unit (their
-  // accumulators fill the register file); 128 x 128 tiles run two, which
-  // hides each tile's prologue and epilogue behind the other's MFMAs but
-  // costs 8% of throughput per CU.  Pick the shortest estimated time.
-  const double t44 = tile_time(T, N, 256, 256, 1.0, 256);
-  const double t42 = tile_time(T, N, 256, 128, 0.9, 256);
-  const double t24 = tile_time(T, N, 128, 256, 0.9, 256);
-  const double t22 = tile_time(T, N, 128, 128, 0.46, 512);
-  if (t22 <= t44 && t22 <= t42 && t22 <= t24)
-    return launch_tile<2, 2>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
-  if (t44 <= t42 && t44 <= t24)
-    return launch_tile<4, 4>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
-  if (t42 <= t24)
-    return launch_tile<4, 2>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
-  return launch_tile<2, 4>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
+  return launch_best<4>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
 }
 
 extern "C" qr_status qr_w8a8_gemm(const void* a_q, const void* a_scale_f16, int64_t T,
@@ -712,15 +713,7 @@ extern "C" qr_status qr_w8a8_gemm(const void* a_q, const void* a_scale_f16, int6
       !aligned(w_scale_f16, 2) || (acc_dbg && !aligned(acc_dbg, 4)))
     return QR_ERR_ALIGN;
   // no weight-streaming kernel for this format: every T goes through the tiles
-  constexpr int kSlots = 256;
-  const double s44 = tile_score(T, N, 256, 256, 1.0, kSlots);
-  const double s42 = tile_score(T, N, 256, 128, 0.9, kSlots);
-  const double s24 = tile_score(T, N, 128, 256, 0.9, kSlots);
-  if (s44 >= s42 && s44 >= s24)
-    return launch_tile<4, 4, 8>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
-  if (s42 >= s24)
-    return launch_tile<4, 2, 8>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
-  return launch_tile<2, 4, 8>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
+  return launch_best<8>(a_q, a_scale_f16, T, w_q, w_scale_f16, N, K, y_f16, acc_dbg, stream);
 }
 
 // one instantiation per group size: 64, 128 and 256 fit in one K step of 256
