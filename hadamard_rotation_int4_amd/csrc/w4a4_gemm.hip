@@ -19,10 +19,11 @@
 //    kernel on codes stored one per byte: chunks go to the matrix cores as
 //    loaded, one per MFMA step, and a K step covers 128 elements.
 //  * Tiles: (64 WM) x (64 WN) outputs per workgroup of 4 wavefronts (one per
-//    SIMD, 2 x 2), each owning a (32 WM) x (32 WN) block = WM x WN MFMA tiles
-//    whose accumulators live in the AGPR half of the register file.  256 x 256
-//    (WM = WN = 4) is the default; 256 x 128 and 128 x 256 are used when the
-//    big tile would leave compute units idle.  K advances 256 at a time
+//    SIMD, 2 x 2), each owning a (32 WM) x (32 WN) block = WM x WN MFMA tiles.
+//    256 x 256 (WM = WN = 4, accumulators in the AGPR half of the register
+//    file, one workgroup per CU) is the default; 128 x 128 (WM = WN = 2, two
+//    workgroups per CU) is used when its estimated time is shorter: small
+//    grids that would leave compute units idle.  K advances 256 at a time
 //    through two LDS stages; the next step's panels are fetched into
 //    registers while the current one is multiplied, and written to the other
 //    stage at the end.
@@ -446,25 +447,20 @@ static double tile_time(int64_t T, int64_t N, int bm, int bn, double eff, int sl
   return (double)rounds * bm * bn / eff;
 }
 
-// The 256-row/column tiles run one workgroup per compute unit (their
-// accumulators fill the register file); 128 x 128 tiles run two, which hides
-// each tile's prologue and epilogue behind the other's MFMAs but costs 8% of
-// throughput per CU.  Launch the tile with the shortest estimated time.
+// 256 x 256 tiles run one workgroup per compute unit (their accumulators fill
+// the register file); 128 x 128 tiles run two, which hides each tile's
+// prologue and epilogue behind the other's MFMAs but costs 8% of throughput
+// per CU.  Launch the one with the shorter estimated time.  (256 x 128 tiles,
+// one per CU at 0.9, lose to two 128 x 128 tiles at every shape.)
 template <int BITS>
 static qr_status launch_best(const void* a_q, const void* a_scale, int64_t T, const void* w_q,
                              const void* w_scale, int64_t N, int64_t K, void* y, int32_t* acc,
                              hipStream_t stream) {
   const double t44 = tile_time(T, N, 256, 256, 1.0, 256);
-  const double t42 = tile_time(T, N, 256, 128, 0.9, 256);
-  const double t24 = tile_time(T, N, 128, 256, 0.9, 256);
   const double t22 = tile_time(T, N, 128, 128, 0.46, 512);
-  if (t22 <= t44 && t22 <= t42 && t22 <= t24)
+  if (t22 <= t44)
     return launch_tile<2, 2, BITS>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
-  if (t44 <= t42 && t44 <= t24)
-    return launch_tile<4, 4, BITS>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
-  if (t42 <= t24)
-    return launch_tile<4, 2, BITS>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
-  return launch_tile<2, 4, BITS>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
+  return launch_tile<4, 4, BITS>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
 }
 
 
