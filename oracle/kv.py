@@ -68,7 +68,23 @@ def asym_quant_math(y: np.ndarray, group: int, clip: float = 1.0, bits: int = 4)
     return q.reshape(y.shape), s_h, m_h
 
 
+def asym_quant_with_params(y: np.ndarray, group: int, s_h, m_h, bits: int = 4) -> np.ndarray:
+    """Codes clamp(round_half_even((y - mn) / s), 0, 2^bits - 1) of float64 rows y [..., Dh]
+    for given fp16 (s, mn) per group [..., Dh/G] (float64 arithmetic); s = 0 gives 0."""
+    levels = (1 << bits) - 1
+    y = np.asarray(y, dtype=np.float64)
+    dh = y.shape[-1]
+    g = y.reshape(*y.shape[:-1], dh // group, group)
+    s = np.asarray(s_h, dtype=F16).astype(np.float64)[..., None]
+    m = np.asarray(m_h, dtype=F16).astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = np.where(s > 0, (g - m) / np.where(s > 0, s, 1.0), 0.0)
+    return np.clip(np.rint(u), 0, levels).astype(np.uint8).reshape(y.shape)
+
+
 def asym_tie_distance(y: np.ndarray, group: int, s_h, m_h) -> np.ndarray:
+    """| frac(|u|) - 0.5 | with u = (y - mn) / s per group (fp16 s, mn; u = 0 where s = 0):
+    how far each pre-round value is from a .5 boundary."""
     y = np.asarray(y, dtype=np.float64)
     dh = y.shape[-1]
     g = y.reshape(*y.shape[:-1], dh // group, group)

@@ -185,11 +185,3 @@ def dequant(codes: np.ndarray, scale_f16: np.ndarray) -> np.ndarray:
     """float64 codes * scale."""
     return np.asarray(codes, dtype=np.float64) * np.asarray(scale_f16, dtype=F16).astype(np.float64)[..., None]
 
-
-def rotate_quant_math(x: np.ndarray, signs, clip: float = 1.0, rotated: bool = True,
-                      bits: int = 4):
-    """Float64 reference of the fused op: (codes, fp16 scales, y64)."""
-    from .hadamard import rotate
-    y = rotate(x, signs) if rotated else np.asarray(x, dtype=np.float64)
-    q, s = sym_quant_math(y, clip, bits)
-    return q, s, y

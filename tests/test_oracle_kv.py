@@ -128,3 +128,34 @@ def test_bbit_range_and_error(bits):
     q4, s4, m4 = kv.asym_quant_math(y, 128)
     q4b, s4b, m4b = kv.asym_quant_math(y, 128, bits=4)
     assert np.array_equal(q4, q4b) and np.array_equal(s4, s4b) and np.array_equal(m4, m4b)
+
+
+# ------------------- asymmetric tie distance and given (s, mn) -------------------
+# s = 0.25 and mn = fp16(-0.9) = -0.89990234375, so mn / s is not an integer: a
+# helper that forgot to subtract mn, added it, or took another group's (s, mn)
+# would move these values.  Group 0's u = (y - mn) / s = 2.5, 2, 0, 14.5;
+# group 1 (s = 0.5, mn = 1) has u = 0.25, 3.5, 15.75 (clamped to 15), -1 (to 0).
+
+def _two_groups():
+    m0 = float(np.float16(-0.9))
+    y0 = m0 + 0.25 * np.array([2.5, 2.0, 0.0, 14.5])
+    y1 = 1.0 + 0.5 * np.array([0.25, 3.5, 15.75, -1.0])
+    s = np.array([[0.25, 0.5]], dtype=np.float16)
+    m = np.array([[m0, 1.0]], dtype=np.float16)
+    return np.concatenate([y0, y1])[None, :], s, m
+
+
+def test_asym_tie_distance_hand_values():
+    y, s, m = _two_groups()
+    got = kv.asym_tie_distance(y, 4, s, m)
+    assert np.allclose(got, [[0.0, 0.5, 0.5, 0.0, 0.25, 0.0, 0.25, 0.5]], rtol=0, atol=1e-12)
+
+
+def test_asym_quant_with_params_hand_values():
+    y, s, m = _two_groups()
+    q = kv.asym_quant_with_params(y, 4, s, m)
+    assert q.tolist() == [[2, 2, 0, 14, 0, 4, 15, 0]]
+    q3 = kv.asym_quant_with_params(y, 4, s, m, bits=3)  # 7 levels: 14 -> 7, 15 -> 7
+    assert q3.tolist() == [[2, 2, 0, 7, 0, 4, 7, 0]]
+    z = kv.asym_quant_with_params(y, 4, np.zeros_like(s), m)
+    assert not z.any()

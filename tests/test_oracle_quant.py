@@ -277,3 +277,38 @@ def test_groups_gemm_recipe_and_math(group):
     y1, _ = gemm.w4a4_gemm_groups_recipe(a, asc[:, :1], w, wsc[:, :1], K)
     assert np.array_equal(y1.view(np.uint16), gemm.epilogue_recipe(
         gemm.w4a4_acc(a, w), asc[:, 0], wsc[:, 0]).view(np.uint16))
+
+
+# ------------------------- tie distance (R3's window) -------------------------
+# Hand values of u = y / s: 2.5 and -2.5 sit on a .5 boundary (distance 0),
+# integers are as far from one as possible (0.5), -3.4996 is 4e-4 away.  The
+# scale is used as the fp16 value that is stored, so 0.1 acts as
+# 0.0999755859375 and y = 0.25 lands 6.1e-4 past 2.5, not on it.
+
+def test_tie_distance_hand_values():
+    y = np.array([[1.25, -1.25, 1.0, 3.5, -1.7498, 0.375, 0.0]])
+    got = quant.tie_distance(y, np.array([0.5], dtype=np.float16))
+    want = [0.0, 0.0, 0.5, 0.5, 4e-4, 0.25, 0.5]
+    assert np.allclose(got, [want], rtol=0, atol=1e-12)
+
+
+def test_tie_distance_uses_the_fp16_scale_of_each_row():
+    y = np.array([[0.25, 0.25], [0.25, 0.75]])
+    s = np.array([0.1, 0.5], dtype=np.float64)  # row 0's scale is not an fp16 number
+    got = quant.tie_distance(y, s)
+    u0 = 0.25 / 0.0999755859375                  # = 2.50061..., the stored fp16 scale
+    assert np.allclose(got[0], abs(u0 - 2.5), rtol=0, atol=1e-12) and abs(u0 - 2.5) > 6e-4
+    assert np.allclose(got[1], [0.0, 0.0], atol=0)  # 0.5 and 1.5
+
+
+def test_tie_distance_zero_scale_row_is_never_a_tie():
+    got = quant.tie_distance(np.array([[0.0, 3.0]]), np.array([0.0], dtype=np.float16))
+    assert got.tolist() == [[0.5, 0.5]]
+
+
+def test_quant_with_scale_hand_values():
+    # s = 0.5: u = (2.5, -2.5, 3.5, 7.6, -9, 0.26) -> RNE (2, -2, 4, 8 -> 7, -9 -> -8, 0)
+    y = np.array([[1.25, -1.25, 1.75, 3.8, -4.5, 0.13]])
+    q = quant.sym_quant_with_scale(y, np.array([0.5], dtype=np.float16))
+    assert q.tolist() == [[2, -2, 4, 7, -8, 0]]
+    assert quant.sym_quant_with_scale(y, np.array([0.0], dtype=np.float16)).tolist() == [[0] * 6]
