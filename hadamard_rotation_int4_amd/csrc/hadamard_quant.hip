@@ -236,9 +236,13 @@ __global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const u
             w[b + h][j] = u - v;
           }
     if (NB == KM) {
-      // keep a compiler-visible VALU op between the MFMA results and the DPP asm
+      // No register butterfly ran, so the DPP asm below would read MFMA results
+      // directly, and the compiler inserts no MFMA-to-VALU wait states in front
+      // of inline asm: pass every result through a compiler-visible VALU op.
 #pragma unroll
-      for (int j = 0; j < 8; ++j) w[0][j] = __fadd_rn(w[0][j], 0.0f);
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[b][j] = __fadd_rn(w[b][j], 0.0f);
     }
     // Butterflies over the chunk index (element bits 5..8), across lanes.
 #pragma unroll

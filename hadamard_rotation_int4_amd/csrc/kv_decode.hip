@@ -21,27 +21,30 @@
 //    unnormalised output) per query head; k_kv_decode_combine merges the
 //    records of a head.
 //  * Both products run on the matrix cores (v_mfma_f32_16x16x32_f16) on exact
-//    operands.  A 4-bit code c enters as the fp16 number 1024 + c (bit pattern
-//    0x6400 | c), or 1024 + 16 c for the high nibble of a byte, whose query
-//    operand is then divided by 16 (exact); the constant and the scale / min of
-//    the position are applied around the product, in fp32:
-//    q . k_j = scale_j (q . c_j) + min_j sum(q), the MFMA accumulator starting
-//    at -1024 times the sum of the query operands so that it ends at q . c_j.
+//    operands.  A 4-bit code c enters as the fp16 subnormal c 2^-24 (bit
+//    pattern c: the masked nibble itself), or 16 c 2^-24 for the high nibble
+//    of a byte, whose query operand is then divided by 16; every product is
+//    exact in fp32 and no constant has to be cancelled, so the fp32 sums carry
+//    only the magnitude of q . c.  The scale / min of the position are applied
+//    around the product, in fp32: q . k_j = (2^24 scale_j) (q . c_j 2^-24) +
+//    min_j sum(q).
 //  * Scores: keys are the M index (16 per tile, lane-major), query heads the N
 //    index, head dimensions the contraction; lane (head n, g) ends with the
 //    scores of positions 4 g .. 4 g + 3 of each tile.
 //  * Values: the product P V contracts over positions, which the cache holds
 //    row-wise.  Each 16-position tile is transposed on the matrix cores by a
-//    0/1 selection matrix (T = V_tile x Sel - 1024 = the codes, exact), which
-//    leaves position 4 g + r in register r of lane (dim, g): exactly the
-//    B-operand layout of P V for the position order the scores already have.
+//    selection matrix with entries 1024 (64 for a high nibble): T = V_tile x
+//    Sel = c 2^-14, exact and an fp16 normal number for c >= 1, which leaves
+//    position 4 g + r in register r of lane (dim, g): exactly the B-operand
+//    layout of P V for the position order the scores already have.  The
+//    output rows carry the factor 2^-14 until the wavefronts merge.
 //  * The weights P' = p * scale_v enter the product as fp16 (the pages' FP16
-//    dot product; QR_KD_SPLIT_WEIGHTS=1 carries them as hi + lo parts, about
-//    22 bits, at two MFMAs); sum_j p_j min_j is added in fp32.
+//    dot product); sum_j p_j min_j is added in fp32.
 //  * When one workgroup per KV head already fills the machine (B * Hkv >= 256
 //    compute units) the split is a single chunk run and the workgroup writes
 //    the normalised fp16 output itself: no workspace, no merge kernel.
 #include <cfloat>
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -50,13 +53,7 @@ namespace qr {
 
 constexpr int KD_DH = 128;     // head dimension
 constexpr int KD_CHUNK = 256;  // positions per workgroup pass: 4 wavefronts x 4 tiles x 16
-#ifndef QR_KD_SPLIT_WEIGHTS
-#define QR_KD_SPLIT_WEIGHTS 0
-#endif
-#ifndef QR_KD_TARGET_WG
-#define QR_KD_TARGET_WG 256
-#endif
-constexpr int KD_TARGET_WG = QR_KD_TARGET_WG;  // workgroups the split aims for
+constexpr int KD_TARGET_WG = 256;  // workgroups the split aims for: one per compute unit
 
 struct KdPlan {
   int chunks, cpw, splits;
@@ -74,17 +71,17 @@ static KdPlan kd_plan(int64_t B, int64_t Hkv, int64_t L) {
 }
 
 // Packed 4-bit codes (8 per dword: code 2i in the low nibble of byte i) ->
-// 8 fp16 values in the element order (c0, c4, c1, c5, c2, c6, c3, c7): even
-// codes as 1024 + c, odd codes as 1024 + 16 c (their nibble left in place), so
-// five bit operations per dword.  mlo = 0x000F000F, mhi = 0x00F000F0 and
-// bias = 0x64006400 come in registers (three-operand and-or).
-__device__ __forceinline__ v8h codes8_f16(uint32_t x, uint32_t mlo, uint32_t mhi, uint32_t bias) {
+// 8 fp16 subnormals in the element order (c0, c4, c1, c5, c2, c6, c3, c7): even
+// codes as c 2^-24, odd codes as 16 c 2^-24 (their nibble left in place), so
+// five bit operations per dword with no constant to add.  mlo = 0x000F000F and
+// mhi = 0x00F000F0 come in registers.
+__device__ __forceinline__ v8h codes8_f16(uint32_t x, uint32_t mlo, uint32_t mhi) {
   const uint32_t x8 = x >> 8;
   v4u r;
-  r[0] = (x & mlo) | bias;   // c0, c4
-  r[1] = (x & mhi) | bias;   // 16 c1, 16 c5
-  r[2] = (x8 & mlo) | bias;  // c2, c6
-  r[3] = (x8 & mhi) | bias;  // 16 c3, 16 c7
+  r[0] = x & mlo;   // c0, c4
+  r[1] = x & mhi;   // 16 c1, 16 c5
+  r[2] = x8 & mlo;  // c2, c6
+  r[3] = x8 & mhi;  // 16 c3, 16 c7
   return __builtin_bit_cast(v8h, r);
 }
 // Code index of fragment element j, and whether it carries the factor 16.
@@ -132,15 +129,15 @@ __global__ __launch_bounds__(64 * KD_WAVES) void k_kv_decode(
       __builtin_amdgcn_make_buffer_rsrc((void*)(vm + row0), 0, L * 4, 0x00020000);
 
   // Bit masks of the code unpacking, held in registers.
-  uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, bias = 0x64006400u;
-  asm volatile("" : "+v"(mlo), "+v"(mhi), "+v"(bias));
+  uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u;
+  asm volatile("" : "+v"(mlo), "+v"(mhi));
 
   // ---- query fragments (B operand of the scores): lane (head n, g), block kb,
   //      element j holds dim 32 g + 8 kb + pi(j), divided by 16 where the code
-  //      operand carries 16 c (exact: a power of two); heads >= GQ are zero.
-  //      qsum16 is the sum of these operands, qsum that of the query itself ----
+  //      operand carries 16 c; heads >= GQ are zero.  qsum is the sum of the
+  //      query itself ----
   v8h qf[4];
-  float qsum = 0.0f, qsum16 = 0.0f;
+  float qsum = 0.0f;
   {
     const bool real = n < GQ;
     const uint16_t* qh = q + ((int64_t)b * Hq + (int64_t)h * GQ + (real ? n : 0)) * KD_DH + 32 * g;
@@ -154,28 +151,22 @@ __global__ __launch_bounds__(64 * KD_WAVES) void k_kv_decode(
         const _Float16 o = (_Float16)(kd_odd(j) ? v * 0.0625f : v);
         qf[kb][j] = o;
         qsum += v;
-        qsum16 += (float)o;
       }
     }
     qsum += __shfl_xor(qsum, 16);
     qsum += __shfl_xor(qsum, 32);
-    qsum16 += __shfl_xor(qsum16, 16);
-    qsum16 += __shfl_xor(qsum16, 32);
   }
-  const float qc = -1024.0f * qsum16;
 
   // Selection matrices of the transpose: Sel_hs[k = 8 g + j][n'] = w_j iff
-  // g == 2 hs + (n' >> 3) and j == (n' & 7), with w_j = 1/16 on the elements
-  // that carry 16 c; the product then holds 1024 + c or 64 + c, and the
-  // accumulator's start value takes the constant off.
+  // g == 2 hs + (n' >> 3) and j == (n' & 7), with w_j = 1024 (64 on the
+  // elements that carry 16 c), so that the product holds c 2^-14.
   v8h sel[2];
 #pragma unroll
   for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       sel[hs][j] = (g == 2 * hs + (n >> 3) && j == (n & 7))
-                       ? (_Float16)(kd_odd(j) ? 0.0625f : 1.0f) : (_Float16)0.0f;
-  const float tneg = kd_odd(n & 7) ? -64.0f : -1024.0f;
+                       ? (_Float16)(kd_odd(j) ? 64.0f : 1024.0f) : (_Float16)0.0f;
 
   // Running state: max (log2 domain) for head n and for heads 4 g + r (the
   // output rows this lane accumulates), lane-partial sums of p and p * min_v.
@@ -212,8 +203,9 @@ __global__ __launch_bounds__(64 * KD_WAVES) void k_kv_decode(
   auto chunk = [&](const int c, v4u (&vcur)[4], v4u (&vnxt)[4]) {
     const int kw = c * KD_CHUNK + 64 * wq;  // first position of this wavefront's 64
     // metadata of the wavefront's 64 positions, converted once per position
-    // (the key's already carrying the log2-domain softmax scale)
-    s_meta[w][0][lane] = scale_log2e * fp16_lo(kmeta_reg);
+    // (the key's scale already carrying the log2-domain softmax scale and the
+    // 2^24 of the code operands: exact, a power of two)
+    s_meta[w][0][lane] = (scale_log2e * fp16_lo(kmeta_reg)) * 16777216.0f;
     s_meta[w][1][lane] = scale_log2e * fp16_hi(kmeta_reg);
     s_meta[w][2][lane] = fp16_lo(vmeta_reg);
     s_meta[w][3][lane] = fp16_hi(vmeta_reg);
@@ -224,10 +216,10 @@ __global__ __launch_bounds__(64 * KD_WAVES) void k_kv_decode(
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      v4f acc = {qc, qc, qc, qc};
+      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_f16(kraw[t][kb], mlo, mhi, bias), qf[kb],
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_f16(kraw[t][kb], mlo, mhi), qf[kb],
                                                      acc, 0, 0, 0);
       const v4f ks = *(const v4f*)&s_meta[w][0][16 * t + 4 * g];
       const v4f kmn = *(const v4f*)&s_meta[w][1][16 * t + 4 * g];
@@ -286,10 +278,10 @@ __global__ __launch_bounds__(64 * KD_WAVES) void k_kv_decode(
     }
     m_n = mnew_n;
 
-    // ---- weights P' = p * scale_v as fp16 hi + lo, A operands of P V: block
-    //      kp = tiles (2 kp, 2 kp + 1), element j -> position 4 g + (j & 3) of
-    //      tile 2 kp + (j >> 2) ----
-    v8h ph[2], pl[2];
+    // ---- weights P' = p * scale_v in fp16, A operands of P V: block kp =
+    //      tiles (2 kp, 2 kp + 1), element j -> position 4 g + (j & 3) of tile
+    //      2 kp + (j >> 2) ----
+    v8h ph[2];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const v4f vs = *(const v4f*)&s_meta[w][2][16 * t + 4 * g];
@@ -299,25 +291,22 @@ __global__ __launch_bounds__(64 * KD_WAVES) void k_kv_decode(
         const float p = __builtin_amdgcn_exp2f(sc[t][r] - m_n);
         l_n += p;
         ms_n = fmaf(p, vmn[r], ms_n);
-        const float pp = p * vs[r];
-        const _Float16 hi = (_Float16)pp;
-        ph[t >> 1][4 * (t & 1) + r] = hi;
-        if (QR_KD_SPLIT_WEIGHTS) pl[t >> 1][4 * (t & 1) + r] = (_Float16)(pp - (float)hi);
+        ph[t >> 1][4 * (t & 1) + r] = (_Float16)(p * vs[r]);
       }
     }
 
     // ---- P V: transpose each value tile on the matrix cores, then multiply ----
-    const v4f cneg = {tneg, tneg, tneg, tneg};
+    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const v8h va = codes8_f16(vcur[2 * kp][kb], mlo, mhi, bias);
-        const v8h vb = codes8_f16(vcur[2 * kp + 1][kb], mlo, mhi, bias);
+        const v8h va = codes8_f16(vcur[2 * kp][kb], mlo, mhi);
+        const v8h vb = codes8_f16(vcur[2 * kp + 1][kb], mlo, mhi);
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-          const v4f ta = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, sel[hs], cneg, 0, 0, 0);
-          const v4f tb = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb, sel[hs], cneg, 0, 0, 0);
+          const v4f ta = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, sel[hs], zero, 0, 0, 0);
+          const v4f tb = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb, sel[hs], zero, 0, 0, 0);
           v8h bop;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -325,8 +314,6 @@ __global__ __launch_bounds__(64 * KD_WAVES) void k_kv_decode(
             bop[4 + r] = (_Float16)tb[r];
           }
           O[kb][hs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[kp], bop, O[kb][hs], 0, 0, 0);
-          if (QR_KD_SPLIT_WEIGHTS)
-            O[kb][hs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[kp], bop, O[kb][hs], 0, 0, 0);
         }
       }
     }
@@ -357,7 +344,8 @@ __global__ __launch_bounds__(64 * KD_WAVES) void k_kv_decode(
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s_o[w][4 * g + r][kd_dim(kb, hs, n)] = O[kb][hs][r];
+      for (int r = 0; r < 4; ++r)  // the rows carried c 2^-14 (exact power of two)
+        s_o[w][4 * g + r][kd_dim(kb, hs, n)] = O[kb][hs][r] * 16384.0f;
   __syncthreads();
   for (int i = tid; i < GQ * KD_DH; i += 64 * KD_WAVES) {
     const int hd = i / KD_DH, d = i % KD_DH;
@@ -420,6 +408,91 @@ extern "C" int64_t qr_kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t H
   return (int64_t)B * Hq * p.splits * (Dh + 2) * (int64_t)sizeof(float);
 }
 
+namespace qr {
+
+// Validation shared by both entry points (everything but the workspace).
+static qr_status kd_validate(const void* q_f16, int32_t B, int32_t Hq, int32_t Hkv, int32_t Dh,
+                             int32_t S_max, int32_t L, int32_t group, float softmax_scale) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || S_max < 1 || L < 1 || L > S_max) return QR_ERR_SHAPE;
+  if (Hq % Hkv != 0) return QR_ERR_SHAPE;
+  if (Dh != KD_DH || group != KD_DH || Hq / Hkv > 16) return QR_ERR_UNSUPPORTED;
+  if (!(softmax_scale > 0.0f) || !(softmax_scale < 1e30f)) return QR_ERR_ARG;
+  if ((int64_t)S_max * 64 > INT32_MAX) return QR_ERR_SHAPE;
+  if ((int64_t)B * Hq > INT32_MAX || B > 65535 || Hkv > 65535) return QR_ERR_SHAPE;
+  (void)q_f16;
+  return QR_OK;
+}
+
+static qr_status kd_check_pointers(const void* q_f16, const void* k_cache_q,
+                                   const void* k_cache_meta, const void* v_cache_q,
+                                   const void* v_cache_meta, const void* out_f16) {
+  if (!q_f16 || !k_cache_q || !k_cache_meta || !v_cache_q || !v_cache_meta || !out_f16)
+    return QR_ERR_NULL;
+  if (!aligned(q_f16, 16) || !aligned(k_cache_q, 16) || !aligned(v_cache_q, 16) ||
+      !aligned(k_cache_meta, 4) || !aligned(v_cache_meta, 4) || !aligned(out_f16, 2))
+    return QR_ERR_ALIGN;
+  return QR_OK;
+}
+
+// The launches, on validated arguments; ws holds the split records (unused
+// when the plan has a single split).
+static qr_status kd_run(const void* q_f16, int32_t B, int32_t Hq, int32_t Hkv,
+                        const void* k_cache_q, const void* k_cache_meta, const void* v_cache_q,
+                        const void* v_cache_meta, int32_t S_max, int32_t L, float softmax_scale,
+                        void* out_f16, void* ws, hipStream_t stream) {
+  const KdPlan p = kd_plan(B, Hkv, L);
+  const float scale_log2e = softmax_scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(k_kv_decode, dim3(p.splits, Hkv, B), dim3(64 * KD_WAVES), 0, stream,
+                     (const uint16_t*)q_f16, Hq, Hkv, Hq / Hkv, (const uint8_t*)k_cache_q,
+                     (const uint32_t*)k_cache_meta, (const uint8_t*)v_cache_q,
+                     (const uint32_t*)v_cache_meta, S_max, L, scale_log2e, p.chunks, p.cpw,
+                     p.splits, (float*)ws, (uint16_t*)out_f16);
+  qr_status st = launch_status();
+  if (st != QR_OK || p.splits == 1) return st;
+  hipLaunchKernelGGL(k_kv_decode_combine, dim3((unsigned)(B * Hq)), dim3(KD_DH), 0, stream,
+                     (const float*)ws, p.splits, (uint16_t*)out_f16);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the split records live in a static device array,
+// one copy per GPU (each GPU the library runs on holds it until the process
+// ends).  The array's name is only a host-side handle; its device address is
+// looked up once per device with that device current and kept per device.
+// Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+// race.  No record has to start at zero (each split writes all of its
+// records before the merge reads them).
+// ---------------------------------------------------------------------------
+constexpr int64_t KD_SCRATCH_BYTES = QR_KV_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[KD_SCRATCH_BYTES];
+
+constexpr int KD_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[KD_MAX_DEVICES] = {};
+
+static qr_status kd_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= KD_MAX_DEVICES) {
+    (void)hipGetLastError();
+    return QR_ERR_LAUNCH;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return QR_ERR_LAUNCH;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return QR_OK;
+}
+
+}  // namespace qr
+
+using namespace qr;
+
 extern "C" qr_status qr_kv_decode_attention(const void* q_f16, int32_t B, int32_t Hq,
                                             int32_t Hkv, int32_t Dh, const void* k_cache_q,
                                             const void* k_cache_meta, const void* v_cache_q,
@@ -427,32 +500,40 @@ extern "C" qr_status qr_kv_decode_attention(const void* q_f16, int32_t B, int32_
                                             int32_t group, float softmax_scale, void* out_f16,
                                             void* workspace, int64_t workspace_bytes,
                                             hipStream_t stream) {
-  if (B < 0 || Hq < 1 || Hkv < 1 || S_max < 1 || L < 1 || L > S_max) return QR_ERR_SHAPE;
-  if (Hq % Hkv != 0) return QR_ERR_SHAPE;
-  if (Dh != KD_DH || group != KD_DH || Hq / Hkv > 16) return QR_ERR_UNSUPPORTED;
-  if (!(softmax_scale > 0.0f) || !(softmax_scale < 1e30f)) return QR_ERR_ARG;
-  if ((int64_t)S_max * 64 > INT32_MAX) return QR_ERR_SHAPE;
+  qr_status st = kd_validate(q_f16, B, Hq, Hkv, Dh, S_max, L, group, softmax_scale);
+  if (st != QR_OK) return st;
   if (B == 0) return QR_OK;
   const int64_t need = qr_kv_decode_workspace_bytes(B, Hq, Hkv, Dh, L);
-  if (!q_f16 || !k_cache_q || !k_cache_meta || !v_cache_q || !v_cache_meta || !out_f16 ||
-      (need > 0 && !workspace))
-    return QR_ERR_NULL;
+  st = kd_check_pointers(q_f16, k_cache_q, k_cache_meta, v_cache_q, v_cache_meta, out_f16);
+  if (st == QR_OK && need > 0 && !workspace) st = QR_ERR_NULL;
+  if (st != QR_OK) return st;
   if (workspace_bytes < need) return QR_ERR_SHAPE;
-  if (!aligned(q_f16, 16) || !aligned(k_cache_q, 16) || !aligned(v_cache_q, 16) ||
-      !aligned(k_cache_meta, 4) || !aligned(v_cache_meta, 4) || !aligned(out_f16, 2) ||
-      !aligned(workspace, 4))
-    return QR_ERR_ALIGN;
-  const KdPlan p = kd_plan(B, Hkv, L);
-  if ((int64_t)B * Hq > INT32_MAX || B > 65535 || Hkv > 65535) return QR_ERR_SHAPE;
-  const float scale_log2e = softmax_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(k_kv_decode, dim3(p.splits, Hkv, B), dim3(64 * KD_WAVES), 0, stream,
-                     (const uint16_t*)q_f16, Hq, Hkv, Hq / Hkv, (const uint8_t*)k_cache_q,
-                     (const uint32_t*)k_cache_meta, (const uint8_t*)v_cache_q,
-                     (const uint32_t*)v_cache_meta, S_max, L, scale_log2e, p.chunks, p.cpw,
-                     p.splits, (float*)workspace, (uint16_t*)out_f16);
-  qr_status st = launch_status();
-  if (st != QR_OK || p.splits == 1) return st;
-  hipLaunchKernelGGL(k_kv_decode_combine, dim3((unsigned)(B * Hq)), dim3(KD_DH), 0, stream,
-                     (const float*)workspace, p.splits, (uint16_t*)out_f16);
-  return launch_status();
+  if (!aligned(workspace, 4)) return QR_ERR_ALIGN;
+  return kd_run(q_f16, B, Hq, Hkv, k_cache_q, k_cache_meta, v_cache_q, v_cache_meta, S_max, L,
+                softmax_scale, out_f16, workspace, stream);
+}
+
+extern "C" qr_status qr_kv_decode_attention_noalloc(const void* q_f16, int32_t B, int32_t Hq,
+                                                    int32_t Hkv, int32_t Dh,
+                                                    const void* k_cache_q,
+                                                    const void* k_cache_meta,
+                                                    const void* v_cache_q,
+                                                    const void* v_cache_meta, int32_t S_max,
+                                                    int32_t L, int32_t group,
+                                                    float softmax_scale, void* out_f16,
+                                                    hipStream_t stream) {
+  qr_status st = kd_validate(q_f16, B, Hq, Hkv, Dh, S_max, L, group, softmax_scale);
+  if (st != QR_OK) return st;
+  if (B == 0) return QR_OK;
+  const int64_t need = qr_kv_decode_workspace_bytes(B, Hq, Hkv, Dh, L);
+  if (need > KD_SCRATCH_BYTES) return QR_ERR_SCRATCH;
+  st = kd_check_pointers(q_f16, k_cache_q, k_cache_meta, v_cache_q, v_cache_meta, out_f16);
+  if (st != QR_OK) return st;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = kd_scratch(&ws);
+    if (st != QR_OK) return st;
+  }
+  return kd_run(q_f16, B, Hq, Hkv, k_cache_q, k_cache_meta, v_cache_q, v_cache_meta, S_max, L,
+                softmax_scale, out_f16, ws, stream);
 }

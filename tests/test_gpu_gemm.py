@@ -29,17 +29,63 @@ def run(ap, asc, wp, wsc):
 SHAPES = [(1, 1, 64), (7, 100, 128), (300, 260, 192), (33, 17, 4096), (256, 256, 256),
           (513, 300, 1024), (64, 640, 11008), (257, 513, 320), (2, 4096, 128)]
 
-# Shapes that steer the entry point to each of its kernels (it picks the tile
-# whose grid keeps the 256 compute units busiest; T <= 64 streams the weights):
-#   (4096, 4096, 512)  -> 256 x 256 tiles (256 tiles fill the machine once)
-#   (2048, 4096, 512)  -> 256 x 128 tiles (128 big tiles would idle half of it)
-#   (640, 384, 256)    -> 128 x 256 tiles (more tiles than 256 x 128 gives)
+# Shapes that steer the entry point to each of its kernels.  T >= 65 runs the
+# tiled kernel, with 256 x 256 tiles (one workgroup per compute unit) or
+# 128 x 128 tiles (two per compute unit), whichever the launcher estimates
+# faster: 256 x 256 wins only when its grid fills the 256 compute units in
+# clearly fewer rounds.  The small shapes of SHAPES all take 128 x 128;
+#   (4096, 4096, 512)  -> 256 x 256 tiles (256 tiles fill the machine once);
+#   (2048, 4096, 512)  -> 128 x 128 tiles;
 #   (1 | 8 | 32 | 64, ...) -> weight-streaming kernel with 1, 1, 2, 4 row blocks,
 #   at the Llama-2-7B decode widths, including K = 11008 (K % 128 == 0) and
 #   K = 4160 (a final half block of 64).
+# The 256 x 256 tiles with ragged edges and a K tail are covered by
+# test_256_tiles_ragged_edges_and_k_tail below.
 KERNEL_SHAPES = [(4096, 4096, 512), (2048, 4096, 512), (640, 384, 256), (1, 12288, 4096),
                  (8, 4096, 4096), (32, 11008, 4096), (64, 4096, 11008), (17, 100, 4160),
                  (64, 33, 64)]
+
+
+def picks_256_tiles(T, N):
+    """The launcher's tile choice for T >= 65 (rounds of 256 tiles of 256 x 256
+    at throughput 1, against rounds of 512 tiles of 128 x 128 at 0.46 each)."""
+    r44 = -(-(-(-T // 256) * -(-N // 256)) // 256)
+    r22 = -(-(-(-T // 128) * -(-N // 128)) // 512)
+    return r22 * 128 * 128 / 0.46 > r44 * 256 * 256
+
+
+# 256 x 256 tiles whose last tile row and column are partial, with K tails of
+# 64 and 192 past the 256-element K step (and one without a tail).
+RAGGED_256 = [(4000, 4000, 320), (3000, 4100, 4160), (3900, 3850, 448), (4000, 4000, 512)]
+
+
+def _edge_sample(n, seed):
+    rest = np.random.default_rng(seed).choice(n, 40, replace=False)
+    return np.unique(np.r_[0, 1, 255, 256, n - 257, n - 256, n - 2, n - 1, rest])
+
+
+@pytest.mark.parametrize("T,N,K", RAGGED_256)
+@pytest.mark.parametrize("bits", [4, 8])
+def test_256_tiles_ragged_edges_and_k_tail(T, N, K, bits):
+    assert picks_256_tiles(T, N)
+    if bits == 4:
+        a = wl.packed_codes(3, 0, T, K)
+        w = wl.packed_codes(3, 1, N, K)
+    else:
+        a = wl.packed_codes(3, 2, T, 2 * K).view(np.int8)
+        w = wl.packed_codes(3, 3, N, 2 * K).view(np.int8)
+    asc = wl.positive_scales(3, 0, T)
+    wsc = wl.positive_scales(3, 1, N)
+    gemm = qr.w4a4_gemm if bits == 4 else qr.w8a8_gemm
+    y, acc = (host(t) for t in gemm(dev(a), dev(asc), dev(w), dev(wsc), acc_dbg=True))
+    rows, cols = _edge_sample(T, T + K), _edge_sample(N, N + K)
+    if bits == 4:
+        acc_ref = og.w4a4_acc(a[rows], w[cols])
+    else:
+        acc_ref = og.int_matmul_exact(a[rows], w[cols])
+    assert np.array_equal(acc[np.ix_(rows, cols)].astype(np.int64), acc_ref)
+    y_ref = og.epilogue_recipe(acc_ref, asc[rows], wsc[cols])
+    assert np.array_equal(y[np.ix_(rows, cols)].view(np.uint16), y_ref.view(np.uint16))
 
 
 @pytest.mark.parametrize("T,N,K", SHAPES + KERNEL_SHAPES)

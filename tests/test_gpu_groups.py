@@ -15,7 +15,7 @@ from oracle import gemm as og
 from oracle import hadamard as oh
 from oracle import quant as oq
 
-from parity import TIE_TOL, check_rotation, f16_ulp_diff
+from parity import check_codes_given_scale, check_rotation, check_scales
 
 pytestmark = pytest.mark.gpu
 
@@ -35,15 +35,8 @@ def host(t):
 def check_group_codes(q_packed, s_gpu, y64, group, clip):
     T, d = y64.shape
     yg = y64.reshape(T, d // group, group)
-    q_ref, s_ref = oq.sym_quant_math(yg, clip)
-    assert f16_ulp_diff(s_gpu, s_ref).max() <= 1
-    q = oq.unpack_int4(q_packed).reshape(T, d // group, group).astype(np.int64)
-    diff = q - q_ref.astype(np.int64)
-    assert np.abs(diff).max(initial=0) <= 1
-    tie = oq.tie_distance(yg, s_ref)
-    s_r = s_ref.astype(np.float64)
-    shift = np.where(s_r > 0, 7.5 * np.abs(s_gpu.astype(np.float64) - s_r) / np.where(s_r > 0, s_r, 1), 0)
-    assert not ((diff != 0) & (tie >= TIE_TOL + shift[..., None])).any()
+    check_scales(s_gpu, yg, clip)
+    check_codes_given_scale(oq.unpack_int4(q_packed).reshape(T, d // group, group), s_gpu, yg)
 
 
 @pytest.mark.parametrize("group", [64, 128, 256])

@@ -8,7 +8,7 @@ from oracle import attention as oatt
 from oracle import hadamard as oh
 from oracle import kv as okv
 
-from parity import check_asym, check_rotation
+from parity import check_asym, check_rotation, decode_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -87,7 +87,6 @@ def test_decode_over_low_bit_cache(kbits, vbits):
                      device="cuda")
     out = qr.kv_decode_attention(qrot, *caches, L, G, scale, workspace=ws)
     ref = oatt.decode_attention(host(qrot), *(host(c) for c in caches), L, G, scale)
-    vmax = np.abs(okv.asym_dequant(okv.unpack_uint4(host(caches[2])),
-                                   host(caches[3])[..., 0], host(caches[3])[..., 1], G)).max()
     err = np.abs(host(out).astype(np.float64) - ref)
-    assert (err <= 1e-3 * vmax + 2.0 ** -11 * np.abs(ref)).all(), err.max()
+    bound = decode_bound(host(qrot), *(host(c) for c in caches), L, G, scale, ref)
+    assert (err <= bound).all(), float((err / bound).max())

@@ -17,7 +17,7 @@ from oracle import gemm as og
 from oracle import hadamard as oh
 from oracle import quant as oq
 
-from parity import TIE_TOL, check_rotation, f16_ulp_diff
+from parity import check_codes_given_scale, check_rotation, check_scales
 
 pytestmark = pytest.mark.gpu
 
@@ -36,18 +36,8 @@ def host(t):
 
 def check_codes_bits(q_gpu, s_gpu, y64, clip, bits):
     """R2 + R3 for b-bit codes against float64."""
-    qmax = oq.code_range(bits)[0]
-    q_ref, s_ref = oq.sym_quant_math(y64, clip, bits)
-    ulps = f16_ulp_diff(s_gpu, s_ref)
-    assert ulps.max() <= 1, f"R2: scale off by {ulps.max()} ulp"
-    diff = q_gpu.astype(np.int64) - q_ref.astype(np.int64)
-    assert np.abs(diff).max(initial=0) <= 1, "R3: code off by more than 1"
-    tie = oq.tie_distance(y64, s_ref)
-    s_r = s_ref.astype(np.float64)
-    shift = np.where(s_r > 0, (qmax + 0.5) * np.abs(s_gpu.astype(np.float64) - s_r)
-                     / np.where(s_r > 0, s_r, 1), 0)
-    bad = (diff != 0) & (tie >= TIE_TOL + shift[..., None])
-    assert not bad.any(), f"R3: {int(bad.sum())} codes differ away from a .5 boundary"
+    check_scales(s_gpu, y64, clip, bits)
+    check_codes_given_scale(q_gpu, s_gpu, y64, bits)
 
 
 # ---------------------------------------------------------------------------
