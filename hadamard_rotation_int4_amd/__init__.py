@@ -20,6 +20,9 @@ Functions (same names as the C entry points without the ``qr_`` prefix):
   w8a8_gemm(a_q, a_scale, w_q, w_scale, acc_dbg=False) -> y_f16[, acc_i32]
   hadamard_quant_groups(x, signs, clip_ratio, group) -> (q_u8, scale_f16 [T, d/group][, z])
   w4a4_gemm_groups(a_q, a_scale [T, K/group], w_q, w_scale [N, K/group], group) -> y_f16
+  kv_decode_attention(q, k_q, k_meta, v_q, v_meta, L, group, scale, out=None, workspace=None)
+  kv_decode_attention_noalloc(q, k_q, k_meta, v_q, v_meta, L, group, scale, out=None)
+      -> out_f16: the same Decode routine with the library's static scratch
   hadamard_factor(d) -> (n, m);  abi_version();  status_str(code)
 """
 from __future__ import annotations
@@ -89,6 +92,9 @@ def _load():
     lib.qr_kv_decode_attention.restype = ctypes.c_int
     lib.qr_kv_decode_attention.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32, i32,
                                            f32, vp, vp, i64, vp]
+    lib.qr_kv_decode_attention_noalloc.restype = ctypes.c_int
+    lib.qr_kv_decode_attention_noalloc.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32,
+                                                   i32, i32, f32, vp, vp]
     _lib = lib
     return lib
 
@@ -465,14 +471,7 @@ def kv_decode_workspace_bytes(B: int, Hq: int, Hkv: int, Dh: int, L: int) -> int
     return int(_load().qr_kv_decode_workspace_bytes(B, Hq, Hkv, Dh, L))
 
 
-def kv_decode_attention(q, k_cache_q, k_cache_meta, v_cache_q, v_cache_meta, L: int,
-                        group: int = 128, softmax_scale: float | None = None, out=None,
-                        workspace=None, stream=None):
-    """Decode attention of q fp16 [B, Hq, Dh] over positions 0 .. L-1 of the 4-bit cache.
-
-    Caches as qr_kv_rotate_quant writes them: codes uint8 [B, Hkv, S_max, Dh/2],
-    meta fp16 [B, Hkv, S_max, Dh/group, 2].  Returns fp16 [B, Hq, Dh].
-    """
+def _decode_args(q, k_cache_q, k_cache_meta, v_cache_q, v_cache_meta, group, softmax_scale, out):
     torch = _torch()
     _need(q, torch.float16, "q", 3)
     for t, nm in ((k_cache_q, "k_cache_q"), (v_cache_q, "v_cache_q")):
@@ -494,6 +493,20 @@ def kv_decode_attention(q, k_cache_q, k_cache_meta, v_cache_q, v_cache_meta, L: 
         _need(o, torch.float16, "out", 3)
         if tuple(o.shape) != (B, Hq, Dh) or not o.is_contiguous():
             raise ValueError("out must be a contiguous fp16 [B, Hq, Dh] tensor")
+    return B, Hq, Hkv, Dh, S_max, scale, o
+
+
+def kv_decode_attention(q, k_cache_q, k_cache_meta, v_cache_q, v_cache_meta, L: int,
+                        group: int = 128, softmax_scale: float | None = None, out=None,
+                        workspace=None, stream=None):
+    """Decode attention of q fp16 [B, Hq, Dh] over positions 0 .. L-1 of the 4-bit cache.
+
+    Caches as qr_kv_rotate_quant writes them: codes uint8 [B, Hkv, S_max, Dh/2],
+    meta fp16 [B, Hkv, S_max, Dh/group, 2].  Returns fp16 [B, Hq, Dh].
+    """
+    torch = _torch()
+    B, Hq, Hkv, Dh, S_max, scale, o = _decode_args(q, k_cache_q, k_cache_meta, v_cache_q,
+                                                   v_cache_meta, group, softmax_scale, out)
     nbytes = kv_decode_workspace_bytes(B, Hq, Hkv, Dh, int(L)) if B > 0 else 0
     if workspace is None:
         workspace = torch.empty((max(nbytes, 4),), dtype=torch.uint8, device=q.device)
@@ -503,4 +516,20 @@ def kv_decode_attention(q, k_cache_q, k_cache_meta, v_cache_q, v_cache_meta, L: 
                                           _ptr(workspace), workspace.numel() * workspace.element_size(),
                                           _stream(stream))
     _check(code, "qr_kv_decode_attention")
+    return o
+
+
+def kv_decode_attention_noalloc(q, k_cache_q, k_cache_meta, v_cache_q, v_cache_meta, L: int,
+                                group: int = 128, softmax_scale: float | None = None, out=None,
+                                stream=None):
+    """kv_decode_attention through the allocation-free entry point (the library's
+    static per-GPU scratch instead of a workspace).  Pass ``out`` to allocate
+    nothing on this side either."""
+    B, Hq, Hkv, Dh, S_max, scale, o = _decode_args(q, k_cache_q, k_cache_meta, v_cache_q,
+                                                   v_cache_meta, group, softmax_scale, out)
+    code = _load().qr_kv_decode_attention_noalloc(_ptr(q), B, Hq, Hkv, Dh, _ptr(k_cache_q),
+                                                  _ptr(k_cache_meta), _ptr(v_cache_q),
+                                                  _ptr(v_cache_meta), S_max, int(L), int(group),
+                                                  scale, _ptr(o), _stream(stream))
+    _check(code, "qr_kv_decode_attention_noalloc")
     return o

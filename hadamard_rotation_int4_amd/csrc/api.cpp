@@ -20,6 +20,7 @@ extern "C" const char* qr_status_str(int status) {
     case QR_ERR_ALIGN: return "QR_ERR_ALIGN: pointer or stride misaligned";
     case QR_ERR_LAUNCH: return "QR_ERR_LAUNCH: kernel launch failed";
     case QR_ERR_ARG: return "QR_ERR_ARG: scalar argument out of range";
+    case QR_ERR_SCRATCH: return "QR_ERR_SCRATCH: needs more than the library's static scratch";
     default: return "unknown qr_status";
   }
 }

@@ -63,7 +63,9 @@ typedef enum {
   QR_ERR_UNSUPPORTED = 3, /* width/group/head size the kernels do not implement */
   QR_ERR_ALIGN = 4,       /* pointer or stride not aligned as required */
   QR_ERR_LAUNCH = 5,      /* the kernel launch itself failed */
-  QR_ERR_ARG = 6          /* a scalar argument is out of range (clip ratio, enum) */
+  QR_ERR_ARG = 6,         /* a scalar argument is out of range (clip ratio, enum) */
+  QR_ERR_SCRATCH = 7      /* the call needs more scratch than the library's static buffer
+                             holds (qr_kv_decode_attention_noalloc only) */
 } qr_status;
 
 typedef enum {
@@ -364,6 +366,33 @@ qr_status qr_kv_decode_attention(const void* q_f16, int32_t B, int32_t Hq, int32
                                  const void* v_cache_q, const void* v_cache_meta, int32_t S_max,
                                  int32_t L, int32_t group, float softmax_scale, void* out_f16,
                                  void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * qr_kv_decode_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same computation, arguments, requirements
+ * and errors as qr_kv_decode_attention, and bit-identical output.  The split
+ * records live in a static device array of QR_KV_DECODE_SCRATCH_BYTES bytes
+ * that the library holds on each GPU it runs on until the process ends; its
+ * device address is looked up on the first call on each device (with that
+ * device current).  The call allocates and frees nothing.
+ *   Size limit: a call whose qr_kv_decode_workspace_bytes(B, Hq, Hkv, Dh, L)
+ *   exceeds QR_KV_DECODE_SCRATCH_BYTES returns QR_ERR_SCRATCH and launches
+ *   nothing (the limit covers every shape whose B * Hkv divides 256 or is at
+ *   least 256, for any L and Hq / Hkv <= 16).
+ *   Concurrency: every call on one GPU shares that GPU's array, so calls that
+ *   overlap on one GPU (on different streams, or from several host threads
+ *   without ordering) race.  No scratch content has to start at zero.
+ *   The array's address could not be obtained: QR_ERR_LAUNCH.
+ */
+#define QR_KV_DECODE_SCRATCH_BYTES ((int64_t)4 << 20)
+
+qr_status qr_kv_decode_attention_noalloc(const void* q_f16, int32_t B, int32_t Hq, int32_t Hkv,
+                                         int32_t Dh, const void* k_cache_q,
+                                         const void* k_cache_meta, const void* v_cache_q,
+                                         const void* v_cache_meta, int32_t S_max, int32_t L,
+                                         int32_t group, float softmax_scale, void* out_f16,
+                                         hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -13,7 +13,8 @@ import hadamard_rotation_int4_amd as qr
 ROOT = Path(__file__).resolve().parents[1]
 HEADER = ROOT / "include" / "qr.h"
 
-QR_OK, QR_ERR_NULL, QR_ERR_SHAPE, QR_ERR_UNSUPPORTED, QR_ERR_ALIGN, QR_ERR_LAUNCH, QR_ERR_ARG = range(7)
+QR_OK, QR_ERR_NULL, QR_ERR_SHAPE, QR_ERR_UNSUPPORTED, QR_ERR_ALIGN, QR_ERR_LAUNCH, QR_ERR_ARG, \
+    QR_ERR_SCRATCH = range(8)
 
 
 def declared_functions():
@@ -33,6 +34,7 @@ def test_header_declares_the_path():
     names = declared_functions()
     for must in ("qr_hadamard_quant", "qr_hadamard", "qr_w4a4_gemm", "qr_kv_rotate_quant",
                  "qr_kv_decode_attention", "qr_kv_decode_workspace_bytes",
+                 "qr_kv_decode_attention_noalloc",
                  "qr_rmsnorm_quant", "qr_hadamard_heads_quant", "qr_hadamard_quant_i8",
                  "qr_rmsnorm_quant_i8", "qr_hadamard_heads_quant_i8", "qr_w8a8_gemm",
                  "qr_kv_rotate_quant_bits", "qr_hadamard_quant_groups", "qr_w4a4_gemm_groups",
@@ -52,7 +54,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert qr.abi_version() == 1
-    for code in range(7):
+    for code in range(8):
         assert qr.status_str(code).startswith("QR_")
     assert "unknown" in qr.status_str(99)
 
@@ -322,3 +324,20 @@ def test_binding_refuses_cpu_tensors():
         qr.rmsnorm_quant(x)
     with pytest.raises(ValueError):
         qr.hadamard_heads_quant(x, 4)
+
+
+def test_noalloc_decode_rejects_calls_beyond_its_static_scratch(lib):
+    # 255 sequences x 1 KV head x 16 query heads over 512 positions need 4.2 MB of
+    # split records, more than the library's 4 MiB static buffer: QR_ERR_SCRATCH
+    # before any pointer is looked at or anything runs.
+    assert lib.qr_kv_decode_workspace_bytes(255, 16, 1, 128, 512) > 4 << 20
+    code = lib.qr_kv_decode_attention_noalloc(None, 255, 16, 1, 128, None, None, None, None, 512,
+                                              512, 128, 0.088, None, None)
+    assert code == QR_ERR_SCRATCH, qr.status_str(code)
+    assert "scratch" in qr.status_str(QR_ERR_SCRATCH)
+    # the same shape fits the entry point that takes a workspace (its pointers are
+    # checked next: NULL here)
+    assert lib.qr_kv_decode_attention(None, 255, 16, 1, 128, None, None, None, None, 512, 512, 128,
+                                      0.088, None, None, 0, None) == QR_ERR_NULL
+    assert lib.qr_kv_decode_attention_noalloc(None, 2, 16, 2, 128, None, None, None, None, 512,
+                                              512, 128, 0.088, None, None) == QR_ERR_NULL
