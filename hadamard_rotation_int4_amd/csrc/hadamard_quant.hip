@@ -1163,6 +1163,11 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
 // two between its column-tile registers.  Lane (n, g) of tile mt holds chunk
 // positions 16 mt + 4 g .. + 3, i.e. two bytes of packed codes per (mt, ct),
 // staged in LDS for coalesced row stores.
+// The workgroup reads each row from HBM once: every thread fetches its six
+// 16-byte chunks of the next row while the current one is transformed, then
+// writes them, sign-flipped, into one of two LDS row buffers, from which the
+// wavefronts read their B fragments.  The A fragments of a wavefront's three
+// output tiles stay in registers for the whole kernel.
 constexpr int K172_AFRAG = 11 * 6 * 64;  // A fragments [mt][kb][lane], 8 fp16 each: 66 KB
 
 // H_172 in MFMA A-fragment layout, built at compile time: tile mt row i ->
@@ -1201,7 +1206,12 @@ __global__ __launch_bounds__(256, 2) void k_hq_k172(const uint16_t* __restrict__
                                                     float* __restrict__ zdbg,
                                                     void* __restrict__ yout) {
   constexpr int D = 11008;
-  __shared__ uint32_t s_sbits[4 * 6 * 64];  // [ct][kb][lane]
+  constexpr int NCH = D / 8;                // 16-byte chunks per row: 1376
+  constexpr int SPT = (NCH + 255) / 256;    // chunks staged per thread: 6 (the last for tid < 96)
+  // The row, sign-flipped, double buffered: rows alternate between the two
+  // buffers, so the staging barrier of one row also orders every wavefront's
+  // last read of the buffer the row after next overwrites.
+  __shared__ __attribute__((aligned(16))) uint16_t s_row[2][D];  // 43 KB
   __shared__ uint16_t s_stage[D / 4];        // packed row: 5504 bytes
   __shared__ float s_red[4];
   const int tid = threadIdx.x;
@@ -1210,17 +1220,13 @@ __global__ __launch_bounds__(256, 2) void k_hq_k172(const uint16_t* __restrict__
   const int n = lane & 15, g = lane >> 4;
   const int gc = gmap(n);
   static_assert(!F16 || MODE == MODE_QUANT, "the fp16 transform is a quantizer variant");
-  // read through the caches each row
-  const v8h* afrag = (const v8h*)&(F16 ? g_h172_frags16 : g_h172_frags).v[0][0];
 
-  // Sign words of the B fragments, as in k_hq_k28: bit 15 - j / 31 - j hold the
-  // signs of elements 2 j / 2 j + 1 of the fragment.
-  for (int f = tid; f < 4 * 6 * 64; f += 256) {
-    const int fl = f & 63, ck = f >> 6;
-    const int ct = ck / 6, kb = ck % 6;
-    const int a = 16 * ct + gmap(fl & 15), gg = fl >> 4;
-    const int col = 32 * kb + 8 * gg;  // 8 columns, or 4 (168 .. 171), or none
-    s_sbits[f] = (signs && col < 172) ? sign_word8(signs + a * 172 + col, col + 8 <= 172) : 0u;
+  // Sign-bit masks of the chunks this thread stages (the same for every row).
+  v4u smask[SPT];
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int ch = tid + 256 * i;
+    smask[i] = (signs && ch < NCH) ? sign_masks8(signs + 8 * ch) : v4u{0u, 0u, 0u, 0u};
   }
   const float s0 = (gc & 1) ? -1.0f : 1.0f;
   const float s1 = (gc & 2) ? -1.0f : 1.0f;
@@ -1228,60 +1234,83 @@ __global__ __launch_bounds__(256, 2) void k_hq_k172(const uint16_t* __restrict__
   const float s3 = (gc & 8) ? -1.0f : 1.0f;
   const float sigma = (__builtin_popcount(gc) & 1) ? -1.0f : 1.0f;  // lane holds sigma * z
   const int nmt = (w < 3) ? 3 : 2;  // tiles w, w + 4, w + 8 (< 11)
-  __syncthreads();
+  // A fragments of this wavefront's output tiles, held in registers for the
+  // whole kernel (zero for the fourth wavefront's missing third tile).
+  v8h areg[3][6];
+  {
+    const v8h* afrag = (const v8h*)&(F16 ? g_h172_frags16 : g_h172_frags).v[0][0];
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int kb = 0; kb < 6; ++kb)
+        areg[t][kb] = t < nmt ? afrag[((w + 4 * t) * 6 + kb) * 64 + lane] : v8h{};
+  }
 
-  for (int64_t row = blockIdx.x; row < T; row += gridDim.x) {
-    const uint16_t* xr = x + row * ld;
-    // ---- B fragments (every wavefront reads the whole row) ----
-    v4u b[4][6];
+  // The next row's chunks, in flight while the current row is transformed.
+  v4u pre[SPT];
+  auto fetch = [&](int64_t r) {
+    const uint16_t* xr = x + r * ld;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int a = 16 * ct + gc;
+    for (int i = 0; i < SPT; ++i) {
+      const int ch = tid + 256 * i;
+      pre[i] = ch < NCH ? ld_stream(xr + 8 * ch) : v4u{0u, 0u, 0u, 0u};
+    }
+  };
+  if ((int64_t)blockIdx.x < T) fetch(blockIdx.x);
+
+  int buf = 0;
+  for (int64_t row = blockIdx.x; row < T; row += gridDim.x, buf ^= 1) {
+    uint16_t* srow = s_row[buf];
 #pragma unroll
-      for (int kb = 0; kb < 6; ++kb) {
-        const int col = 32 * kb + 8 * g;
+    for (int i = 0; i < SPT; ++i) {
+      const int ch = tid + 256 * i;
+      if (ch < NCH) *(v4u*)(srow + 8 * ch) = pre[i] ^ smask[i];
+    }
+    __syncthreads();
+    if (row + gridDim.x < T) fetch(row + gridDim.x);
+
+    // ---- H_172 on the matrix cores: B column n of block kb is chunk
+    //      a = 16 ct + gc, elements 32 kb + 8 g .. + 7 (zero past 171);
+    //      v[t][ct][r] = output 16 (w + 4 t) + 4 g + r ----
+    v4f acc[3][4];
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[t][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < 6; ++kb) {
+      const int col = 32 * kb + 8 * g;
+      v8h bq[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        // chunk starts are 8-byte aligned in LDS (172 elements = 344 bytes)
+        const uint2* p = (const uint2*)(srow + (16 * ct + gc) * 172 + col);
         v4u raw = {0u, 0u, 0u, 0u};
         if (col + 8 <= 172) {
-          raw = ld_stream(xr + a * 172 + col);
+          const uint2 lo = p[0], hi = p[1];
+          raw = v4u{lo.x, lo.y, hi.x, hi.y};
         } else if (col < 172) {  // 168 .. 171
-          const uint2 h = *(const uint2*)(xr + a * 172 + col);
-          raw[0] = h.x;
-          raw[1] = h.y;
+          const uint2 lo = p[0];
+          raw[0] = lo.x;
+          raw[1] = lo.y;
         }
-        const uint32_t e = s_sbits[(ct * 6 + kb) * 64 + lane];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) raw[j] ^= (e << j) & 0x80008000u;
-        b[ct][kb] = raw;
+        bq[ct] = __builtin_bit_cast(v8h, raw);
       }
-    }
-    // ---- H_172 on the matrix cores: v[t][ct][r] = output 16 (w + 4 t) + 4 g + r ----
-    float v[3][4][4];
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
-      if (t < nmt) {
-        const int mt = w + 4 * t;
-        v4f acc[4];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kb = 0; kb < 6; ++kb) {
-          const v8h a = afrag[(mt * 6 + kb) * 64 + lane];
+      for (int t = 0; t < 3; ++t)
+        if (t < nmt)
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct)
-            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(v8h, b[ct][kb]),
-                                                             acc[ct], 0, 0, 0);
-        }
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[t][ct][r] = acc[ct][r];
-      } else {
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[t][ct][r] = 0.0f;
-      }
+            acc[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[t][kb], bq[ct], acc[t][ct],
+                                                                0, 0, 0);
     }
+    float v[3][4][4];
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[t][ct][r] = acc[t][ct][r];
     // element index of v[t][ct][0]: chunk 16 ct + gc, position 16 (w + 4 t) + 4 g
     auto elem_of = [&](int t, int ct) { return (16 * ct + gc) * 172 + 16 * (w + 4 * t) + 4 * g; };
     auto valid = [&](int t) { return t < nmt && 16 * (w + 4 * t) + 4 * g < 172; };
