@@ -9,7 +9,10 @@
 // cache from the prompt and Append quantizes one new token per decode step
 // (attention-routines paragraph).  The exact fp32 recipe is in include/qr.h.
 //
-// Layout: one (token, head) row of Dh elements is spread over Dh/8 lanes, each
+// Dh = 128 with group 128 (the pages' configuration) runs k_kv_quant128: the
+// head-wise H_128 on the matrix cores, 16 rows per wavefront tile.  Other
+// shapes run k_kv_quant:
+// one (token, head) row of Dh elements is spread over Dh/8 lanes, each
 // lane loading 8 contiguous fp16 (16 bytes).  Three butterfly stages run inside
 // the lane, log2(Dh/8) across lanes.  Group min/max reduce over the G/8 lanes
 // of a group; each lane then writes one dword of codes and the first lane of a
@@ -216,11 +219,203 @@ __global__ __launch_bounds__(256) void k_kv_quant(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dh = 128 with one group per row (the pages' configuration): 16 (token, head)
+// rows per wavefront tile, H_128 on the matrix cores.
+// ---------------------------------------------------------------------------
+// Every row shares the sign vector s, so diag(s) folds into constant A
+// fragments: z = H_128 diag(s) x with H_128 = H_4 (x) H_32.  As in k_hq_pow2,
+// each of the four 32-element output blocks h is a chain of four
+// v_mfma_f32_16x16x32_f16, one per input block kb, on the fp16 input as
+// loaded (B column n = row n of the tile, lane (n, g) holding elements
+// 32 kb + 8 g .. + 7); the H_32 rows of the A fragments are permuted so that
+// lane (n, g) receives outputs 32 h + 8 g .. + 7, and the H_4 sign (-1)^|h & kb|
+// picks a negated copy.  Products are +-x and the accumulation fp32, as in the
+// butterfly form.  Per element the vector units then only scale, reduce,
+// round and pack.  Without rotation the same lane layout holds the input.
+// Workgroups of the Dh = 128 kernel: about four 16-row tiles per wavefront at the
+// 70B Init shape, so that each wavefront's next tile is in flight (one tile per
+// wavefront measured 25% slower).
+constexpr int KV128_GRID_CAP = 2048;
+template <bool ROT>
+__global__ __launch_bounds__(256) void k_kv_quant128(
+    const uint16_t* __restrict__ x, int64_t rows, int S_new, int H, int64_t ld_token,
+    const int8_t* __restrict__ signs, float c, float clip, float levels, uint8_t* __restrict__ cq,
+    uint16_t* __restrict__ meta, int S_max, int start_pos, float* __restrict__ zdbg, FastDiv fdH,
+    FastDiv fdS) {
+  constexpr int DH = 128;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+
+  // A fragments of H_32 diag(s_kb) (row i = n -> output o = 8 (i >> 2) + 4 m + (i & 3),
+  // columns k = 8 g + j of block kb) and their negations.
+  v8h ap[4][2], an[4][2];
+  if constexpr (ROT) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      uint32_t sw0 = 0u, sw1 = 0u;  // int8 signs of elements 32 kb + 8 g .. + 7
+      if (signs) {
+        sw0 = *(const uint32_t*)(signs + 32 * kb + 8 * g);
+        sw1 = *(const uint32_t*)(signs + 32 * kb + 8 * g + 4);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int o = 8 * (n >> 2) + 4 * m + (n & 3);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int k = 8 * g + j;
+          const bool neg_s = (((j < 4 ? sw0 : sw1) >> (8 * (j & 3) + 7)) & 1u) != 0u;
+          const bool neg = ((__builtin_popcount(o & k) & 1) != 0) != neg_s;
+          ap[kb][m][j] = neg ? (_Float16)-1.0f : (_Float16)1.0f;
+        }
+        an[kb][m] = -ap[kb][m];
+      }
+    }
+  }
+
+  const int64_t ntiles = (rows + 15) / 16;
+  const int64_t tstride = (int64_t)gridDim.x * 4;
+  // Rows in input order, r = (b S_new + s) H + h: a tile reads 4 KB of
+  // contiguous input (walking the rows in cache order instead, so that a
+  // tile's codes land contiguously, measured slower: the input is 4x the bytes).
+  struct RowIx {
+    uint32_t tok;   // b S_new + s: the input token
+    int h, s;
+    int64_t bh;     // b H + h
+  };
+  auto row_ix = [&](int64_t r) {
+    RowIx ix;
+    ix.tok = fast_div((uint32_t)r, fdH);
+    ix.h = (int)((uint32_t)r - ix.tok * (uint32_t)H);
+    const uint32_t b = fast_div(ix.tok, fdS);
+    ix.s = (int)(ix.tok - b * (uint32_t)S_new);
+    ix.bh = (int64_t)b * H + ix.h;
+    return ix;
+  };
+  // B fragments of a tile: row tile * 16 + n, elements 32 kb + 8 g .. + 7
+  auto load = [&](int64_t tile, v4u* b) {
+    const int64_t row = tile * 16 + n;
+    if (tile < ntiles && row < rows) {
+      const RowIx ix = row_ix(row);
+      const uint16_t* xr = x + (int64_t)ix.tok * ld_token + (int64_t)ix.h * DH + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)  // read once: non-temporal
+        b[kb] = __builtin_nontemporal_load((const v4u*)(xr + 32 * kb));
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) b[kb] = v4u{0u, 0u, 0u, 0u};
+    }
+  };
+  int64_t tile = (int64_t)blockIdx.x * 4 + wave;
+  v4u bcur[4], bnext[4];
+  load(tile, bcur);
+  for (; tile < ntiles; tile += tstride) {
+    load(tile + tstride, bnext);
+    const int64_t row = tile * 16 + n;
+    const bool valid = row < rows;
+    // z[h][j]: element 32 h + 8 g + j of row n
+    float z[4][8];
+    if constexpr (ROT) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        v4f r0 = {0.0f, 0.0f, 0.0f, 0.0f}, r1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const v8h bv = __builtin_bit_cast(v8h, bcur[kb]);
+          const bool neg = __builtin_popcount(h & kb) & 1;
+          r0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(neg ? an[kb][0] : ap[kb][0], bv, r0, 0, 0, 0);
+          r1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(neg ? an[kb][1] : ap[kb][1], bv, r1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          z[h][r] = r0[r];
+          z[h][4 + r] = r1[r];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          z[h][2 * j] = h2f((uint16_t)(bcur[h][j] & 0xffffu));
+          z[h][2 * j + 1] = h2f((uint16_t)(bcur[h][j] >> 16));
+        }
+    }
+    const RowIx ix = row_ix(valid ? row : 0);
+    if (valid && zdbg) {  // z_dbg is token-major, like the input
+      float* zr = zdbg + ((int64_t)ix.tok * H + ix.h) * DH + 8 * g;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        *(v4f*)(zr + 32 * h) = v4f{z[h][0], z[h][1], z[h][2], z[h][3]};
+        *(v4f*)(zr + 32 * h + 4) = v4f{z[h][4], z[h][5], z[h][6], z[h][7]};
+      }
+    }
+    // y = fp32(z * c) (the input itself without rotation); max / min of the row
+    float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (ROT) z[h][j] = __fmul_rn(z[h][j], c);
+        mx = fmaxf(mx, z[h][j]);
+        mn = fminf(mn, z[h][j]);
+      }
+    // the row's four lanes are n, n + 16, n + 32, n + 48
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mn = fminf(mn, __shfl_xor(mn, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mn = fminf(mn, __shfl_xor(mn, 32));
+    const float mxc = __fmul_rn(clip, mx);
+    const float mnc = __fmul_rn(clip, mn);
+    const uint16_t sh = f2h(__fdiv_rn(__fsub_rn(mxc, mnc), levels));
+    const uint16_t mh = f2h(mnc);
+    const float shf = h2f(sh);
+    const float mhf = h2f(mh);
+    const float inv = shf > 0.0f ? __fdiv_rn(1.0f, shf) : 0.0f;
+    if (valid) {
+      const int64_t crow = ix.bh * (int64_t)S_max + start_pos + ix.s;
+      uint8_t* crw = cq + crow * (DH / 2) + 4 * g;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        uint32_t f[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          // kMagic + rne((y - m_h) * inv), clamped to [0, levels] (m_h and s_h
+          // are rounded to fp16, so the clamp is needed even without clipping)
+          float t = fmaf(__fsub_rn(z[h][j], mhf), inv, kMagic);
+          t = __builtin_amdgcn_fmed3f(t, kMagic, kMagic + levels);
+          f[j] = __float_as_uint(t);
+        }
+        const uint32_t p0 = (f[1] << 4) | (f[0] & 0xfu);
+        const uint32_t p1 = (f[3] << 4) | (f[2] & 0xfu);
+        const uint32_t p2 = (f[5] << 4) | (f[4] & 0xfu);
+        const uint32_t p3 = (f[7] << 4) | (f[6] & 0xfu);
+        *(uint32_t*)(crw + 16 * h) = __builtin_amdgcn_perm(p1, p0, 0x0c0c0400u) |
+                                     __builtin_amdgcn_perm(p3, p2, 0x04000c0cu);
+      }
+      if (g == 0) *(uint32_t*)(meta + crow * 2) = (uint32_t)sh | ((uint32_t)mh << 16);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) bcur[kb] = bnext[kb];
+  }
+}
+
 template <bool ROT>
 static qr_status launch_kv(int dh, const uint16_t* x, int64_t rows, int S_new, int H,
                            int64_t ld_token, const int8_t* signs, int group, float c, float clip,
                            float levels, uint8_t* cq, uint16_t* meta, int S_max, int start_pos,
                            float* zdbg, hipStream_t st) {
+  if (dh == 128 && group == 128) {
+    const int64_t tiles = (rows + 15) / 16;
+    int64_t grid = (tiles + 3) / 4;
+    if (grid > KV128_GRID_CAP) grid = KV128_GRID_CAP;
+    hipLaunchKernelGGL((k_kv_quant128<ROT>), dim3((int)grid), dim3(256), 0, st, x, rows, S_new,
+                       H, ld_token, signs, c, clip, levels, cq, meta, S_max, start_pos, zdbg,
+                       make_fastdiv((uint32_t)H), make_fastdiv((uint32_t)S_new));
+    return launch_status();
+  }
   const int lpr = dh / 8;
   const int64_t rows_per_block = 4 * (64 / lpr);
   int64_t grid = (rows + rows_per_block - 1) / rows_per_block;
