@@ -494,11 +494,19 @@ def copy_calibration():
     a = torch.empty(n, dtype=torch.float16, device=dev).normal_()
     b = torch.empty_like(a)
     torch.cuda.synchronize()
-    for _ in range(10):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+    ev[0].record()
+    for i in range(10):
         b.copy_(a)
+        ev[i + 1].record()
     torch.cuda.synchronize()
+    ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(10))
+    med = 0.5 * (ms[4] + ms[5])
     print(json.dumps({"copy_calibration": True, "bytes_read_per_launch": 2 * n,
-                      "bytes_written_per_launch": 2 * n, "launches": 10}), flush=True)
+                      "bytes_written_per_launch": 2 * n, "launches": 10,
+                      "copy_ms_median": round(med, 4),
+                      "copy_GB/s_read_plus_write": round(4 * n / (med * 1e-3) / 1e9, 1)}),
+          flush=True)
     return 0
 
 

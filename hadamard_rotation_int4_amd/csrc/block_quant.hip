@@ -115,7 +115,7 @@ template <>
 struct HeadsIO<2> {
   typedef uint32_t raw_t;
   static __device__ __forceinline__ raw_t load(const uint16_t* p) {
-    return QR_NT ? __builtin_nontemporal_load((const uint32_t*)p) : *(const uint32_t*)p;
+    return __builtin_nontemporal_load((const uint32_t*)p);
   }
   static __device__ __forceinline__ uint32_t word(const raw_t& r, int i) { return r; }
 };
@@ -123,7 +123,7 @@ template <>
 struct HeadsIO<4> {
   typedef uint32_t raw_t __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ raw_t load(const uint16_t* p) {
-    return QR_NT ? __builtin_nontemporal_load((const raw_t*)p) : *(const raw_t*)p;
+    return __builtin_nontemporal_load((const raw_t*)p);
   }
   static __device__ __forceinline__ uint32_t word(const raw_t& r, int i) { return r[i]; }
 };
@@ -230,8 +230,7 @@ __global__ __launch_bounds__(256) void k_heads_quant(const uint16_t* __restrict_
       if constexpr (J == 2) {
         const uint32_t p = clamp ? quant_pack2_i8<true>(v[h], m, rg.lo, rg.hi)
                                  : quant_pack2_i8<false>(v[h], m, rg.lo, rg.hi);
-        if (QR_NT) __builtin_nontemporal_store((uint16_t)p, (uint16_t*)dst);
-        else *(uint16_t*)dst = (uint16_t)p;
+        __builtin_nontemporal_store((uint16_t)p, (uint16_t*)dst);
       } else if constexpr (J == 4) {
         const uint32_t p = clamp ? quant_pack4_i8<true>(v[h], m, rg.lo, rg.hi)
                                  : quant_pack4_i8<false>(v[h], m, rg.lo, rg.hi);
@@ -254,11 +253,9 @@ __global__ __launch_bounds__(256) void k_heads_quant(const uint16_t* __restrict_
     const uint32_t p = clamp ? quant_packJ<J, true>(v[h], m) : quant_packJ<J, false>(v[h], m);
     uint8_t* dst = qr_ + h * (DH / 2);
     if constexpr (J == 2) {
-      if (QR_NT) __builtin_nontemporal_store((uint8_t)p, dst);
-      else *dst = (uint8_t)p;
+      __builtin_nontemporal_store((uint8_t)p, dst);
     } else if constexpr (J == 4) {
-      if (QR_NT) __builtin_nontemporal_store((uint16_t)p, (uint16_t*)dst);
-      else *(uint16_t*)dst = (uint16_t)p;
+      __builtin_nontemporal_store((uint16_t)p, (uint16_t*)dst);
     } else {
       st_stream((uint32_t*)dst, p);
     }

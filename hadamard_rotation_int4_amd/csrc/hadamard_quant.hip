@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "dpp.hpp"
 #include "quant_common.hpp"
 
 namespace qr {
@@ -71,54 +72,26 @@ __device__ __forceinline__ uint32_t sign_word8(const int8_t* s, bool second_half
 // k_hq_pow2: d = NB * 512
 // ===========================================================================
 
-// Lane-in-row c (0..15) -> 32-element chunk index inside a 512-element block.
-// Linear over GF(2) with gmap(1) = 1, gmap(2) = 2, gmap(7) = 4, gmap(15) = 8, so
-// that the DPP partner patterns xor 1 (quad_perm), xor 2 (quad_perm), xor 7
-// (row_half_mirror) and xor 15 (row_mirror) each flip exactly one chunk bit.
-__device__ __forceinline__ int gmap(int c) {
-  const int c0 = c & 1, c1 = (c >> 1) & 1, c2 = (c >> 2) & 1, c3 = (c >> 3) & 1;
-  return (c0 ^ c2) | ((c1 ^ c2) << 1) | ((c2 ^ c3) << 2) | (c3 << 3);
-}
 
-// One butterfly stage across lanes for eight registers: r += dpp(r) * s.
-// The leading s_nop covers the VALU-write -> DPP-read hazard for values
-// produced just before; within the block every register is distinct.
-#define QR_DPP8(CTRL, r, s)                                                            \
-  asm volatile(                                                                        \
-      "s_nop 1\n\t"                                                                    \
-      "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"                  \
-      : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), \
-        "+v"(r[7])                                                                     \
-      : "v"(s))
-
-#ifndef QR_POW2_WAVES_PER_SIMD
-#define QR_POW2_WAVES_PER_SIMD 2
-#endif
-#ifndef QR_SMALL_UNROLL
-#define QR_SMALL_UNROLL 1
-#endif
-#ifndef QR_POW2_KM
-#define QR_POW2_KM 4
-#endif
-#ifndef QR_POW2_PF_EARLY
-#define QR_POW2_PF_EARLY 8
-#endif
-#ifndef QR_K28_WAVES_PER_SIMD
-#define QR_K28_WAVES_PER_SIMD 2
-#endif
+// Launch shapes and pipeline depths of the rotate+quant kernels (each the
+// fastest of the values measured at the Llama-2 shapes):
+//  * k_hq_pow2 holds a row in 128 + 64 VGPRs: two wavefronts per SIMD;
+//  * POW2_KM blocks are combined on the matrix cores (H_4 (x) H_32); 8 moves
+//    one more butterfly stage onto them but was slower at d = 8192;
+//  * POW2_PF_EARLY of the 16 blocks of the next 8192-wide row are fetched
+//    right after the MFMAs, the rest during quantization (4 or 16: slower);
+//  * k_hq_small works on one group of rows per wavefront at a time.
+constexpr int POW2_WAVES_PER_SIMD = 2;
+constexpr int POW2_KM = 4;
+constexpr int POW2_PF_EARLY = 8;
+constexpr int SMALL_UNROLL = 1;
+constexpr int K28_WAVES_PER_SIMD = 2;
 
 // Buffer-resource cache policy of the streaming accesses (gfx9 "nt" bit).
-#define QR_BUF_POLICY (QR_NT ? 2 : 0)
+constexpr int BUF_POLICY_NT = 2;
 
 template <int NB, int MODE, bool CLAMP, bool DBG>
-__global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const uint16_t* __restrict__ x, int64_t T,
+__global__ __launch_bounds__(256, POW2_WAVES_PER_SIMD) void k_hq_pow2(const uint16_t* __restrict__ x, int64_t T,
                                                  int64_t ld, const int8_t* __restrict__ signs,
                                                  float c, float clip, uint8_t* __restrict__ q,
                                                  uint16_t* __restrict__ scale,
@@ -128,9 +101,9 @@ __global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const u
   // Blocks of the next row fetched right after the MFMAs; the others are
   // fetched during quantization, as the registers of the current row free up
   // (quantization-only kernels: there is no later point, all are early).
-  constexpr int PF_EARLY = (MODE == MODE_QUANT && NB == 16) ? QR_POW2_PF_EARLY : NB;
+  constexpr int PF_EARLY = (MODE == MODE_QUANT && NB == 16) ? POW2_PF_EARLY : NB;
   // Blocks combined on the matrix cores (the rest by butterflies in the lane).
-  constexpr int KM = NB < QR_POW2_KM ? NB : QR_POW2_KM;
+  constexpr int KM = NB < POW2_KM ? NB : POW2_KM;
   __shared__ v4u s_mask[NB * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -188,7 +161,7 @@ __global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const u
     const __amdgpu_buffer_rsrc_t rs = row_rsrc(row < T ? row : 0, row < T);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
-      raw[b] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, b * 1024, QR_BUF_POLICY));
+      raw[b] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, b * 1024, BUF_POLICY_NT));
   }
   for (; row < T; row += rstride) {
     const bool more = row + rstride < T;
@@ -205,7 +178,7 @@ __global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const u
         const int b = grp * KM + kb;
         bop[kb] = __builtin_bit_cast(v8h, raw[b] ^ s_mask[b * 64 + lane]);
         if (b < PF_EARLY)
-          raw[b] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsn, voff, b * 1024, QR_BUF_POLICY));
+          raw[b] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsn, voff, b * 1024, BUF_POLICY_NT));
       }
 #pragma unroll
       for (int h = 0; h < KM; ++h) {
@@ -287,16 +260,16 @@ __global__ __launch_bounds__(256, QR_POW2_WAVES_PER_SIMD) void k_hq_pow2(const u
       if (CLAMP || (sh & 0x7fffu) < 0x0400u) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          __builtin_amdgcn_raw_buffer_store_b32(quant_pack8<true>(w[b], ml), rsq, qoff, b * 256, QR_BUF_POLICY);
+          __builtin_amdgcn_raw_buffer_store_b32(quant_pack8<true>(w[b], ml), rsq, qoff, b * 256, BUF_POLICY_NT);
           if (b >= PF_EARLY)
-            raw[b] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsn, voff, b * 1024, QR_BUF_POLICY));
+            raw[b] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsn, voff, b * 1024, BUF_POLICY_NT));
         }
       } else {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          __builtin_amdgcn_raw_buffer_store_b32(quant_pack8<false>(w[b], ml), rsq, qoff, b * 256, QR_BUF_POLICY);
+          __builtin_amdgcn_raw_buffer_store_b32(quant_pack8<false>(w[b], ml), rsq, qoff, b * 256, BUF_POLICY_NT);
           if (b >= PF_EARLY)
-            raw[b] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsn, voff, b * 1024, QR_BUF_POLICY));
+            raw[b] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsn, voff, b * 1024, BUF_POLICY_NT));
         }
       }
       if (lane == 0) scale[row] = sh;
@@ -363,9 +336,9 @@ __global__ __launch_bounds__(256) void k_hq_small(const uint16_t* __restrict__ x
     for (int j = 0; j < 8; ++j) sg[j] = (((j < 4 ? w0 : w1) >> (8 * (j & 3) + 7)) & 1u) ? -1.0f : 1.0f;
   }
 
-  // Grid-stride over groups of RPW rows per wavefront; QR_SMALL_UNROLL groups
+  // Grid-stride over groups of RPW rows per wavefront; SMALL_UNROLL groups
   // are loaded before any is processed, so that many loads are in flight.
-  constexpr int U = QR_SMALL_UNROLL;
+  constexpr int U = SMALL_UNROLL;
   const int64_t gstride = (int64_t)gridDim.x * 4 * RPW;
   for (int64_t base0 = ((int64_t)blockIdx.x * 4 + wave) * RPW; base0 < T; base0 += U * gstride) {
   v4u raws[U];
@@ -668,10 +641,11 @@ __global__ __launch_bounds__(256) void k_hq_lds(const uint16_t* __restrict__ x, 
 // is reduced through LDS, and each lane stores its chunks' 14 bytes of packed
 // codes directly (two-byte stores: measured faster than staging the row in
 // LDS for 16-byte stores, which costs two more barriers per row).
-#ifndef QR_K28_ROUNDS
-#define QR_K28_ROUNDS 4
-#endif
-constexpr int K28_RV = 28 / QR_K28_ROUNDS;             // chunk positions per exchange round
+// The exchange across the wavefronts runs in K28_ROUNDS rounds of K28_RV chunk
+// positions (its LDS buffer holds one round: more would not leave room for two
+// workgroups per CU).
+constexpr int K28_ROUNDS = 4;
+constexpr int K28_RV = 28 / K28_ROUNDS;               // chunk positions per exchange round
 constexpr int K28_XROUND = 4 * 4 * K28_RV * 64;       // floats per round: [w][ct][RV][lane]
 constexpr int K28_AFRAG = 7 * 4 * 64;                 // A fragments: [mt][kb][lane]
 
@@ -879,7 +853,7 @@ __device__ __forceinline__ void k28_finish_f16(const float (&v)[4][28], int64_t 
 }
 
 template <int MODE, bool CLAMP, bool F16>
-__global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uint16_t* __restrict__ x, int64_t T,
+__global__ __launch_bounds__(256, K28_WAVES_PER_SIMD) void k_hq_k28(const uint16_t* __restrict__ x, int64_t T,
                                                    int64_t ld, const int8_t* __restrict__ signs,
                                                    float c, float clip, int bits,
                                                    uint8_t* __restrict__ q,
@@ -1042,7 +1016,7 @@ __global__ __launch_bounds__(256, QR_K28_WAVES_PER_SIMD) void k_hq_k28(const uin
     //      chunk 4 G + g, G = (4 w'' + w) 16 + gmap(n), position k ----
     float o[4][28];
 #pragma unroll
-    for (int rnd = 0; rnd < QR_K28_ROUNDS; ++rnd) {
+    for (int rnd = 0; rnd < K28_ROUNDS; ++rnd) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -1531,10 +1505,8 @@ template <int MODE, bool CLAMP>
 static qr_status launch_pow2(int nb, const uint16_t* x, int64_t T, int64_t ld, const int8_t* s,
                              float c, float clip, uint8_t* q, uint16_t* sc, float* z, void* y,
                              hipStream_t st) {
-#ifndef QR_POW2_GRID
-#define QR_POW2_GRID 512
-#endif
-  const int grid = grid_for(T, 4, QR_POW2_GRID);
+  // two workgroups per CU, all resident (more workgroups measured no faster)
+  const int grid = grid_for(T, 4, 512);
   switch (nb) {
 #define QR_CASE(NBV)                                                                   \
   case NBV:                                                                            \
@@ -1563,10 +1535,7 @@ static qr_status launch_small(int d, int rot, const uint16_t* x, int64_t T, int6
                               float* z, void* y, hipStream_t st) {
   const int lpr = d / 8;
   const int rows_per_block = 4 * (64 / lpr);
-#ifndef QR_SMALL_GRID
-#define QR_SMALL_GRID 2048
-#endif
-  const int grid = grid_for(T, rows_per_block, QR_SMALL_GRID);
+  const int grid = grid_for(T, rows_per_block, 2048);
   switch (lpr) {
 #define QR_CASE(L)                                                                     \
   case L:                                                                              \
@@ -1604,14 +1573,11 @@ static qr_status launch_lds_t(int d, int n, const uint16_t* x, int64_t T, int64_
   return launch_status();
 }
 
-#ifndef QR_K28_GRID
-#define QR_K28_GRID 512
-#endif
 template <int MODE, bool CLAMP, bool F16>
 static qr_status launch_k28(const uint16_t* x, int64_t T, int64_t ld, const int8_t* signs, float c,
                             float clip, uint8_t* qq, uint16_t* ss, float* z, void* y,
                             hipStream_t st, int bits = 4) {
-  const int grid = grid_for(T, 1, QR_K28_GRID);
+  const int grid = grid_for(T, 1, 512);  // two workgroups per CU, all resident
   hipLaunchKernelGGL((k_hq_k28<MODE, CLAMP, F16>), dim3(grid), dim3(256), 0, st, x, T, ld, signs,
                      c, clip, bits, qq, ss, z, y);
   return launch_status();

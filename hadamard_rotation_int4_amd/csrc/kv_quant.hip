@@ -19,6 +19,7 @@
 // group writes its (scale, min) pair.  The kernel is HBM-bound: per element it
 // reads 2 bytes and writes 0.5 byte plus 4 bytes of metadata per group.
 #include "common.hpp"
+#include "dpp.hpp"
 
 namespace qr {
 
@@ -39,31 +40,6 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
   return (__umulhi(n, f.m) + n) >> f.s;
 }
 
-// One butterfly stage across lanes for eight registers: r += dpp(r) * s (the
-// leading s_nop covers the VALU-write -> DPP-read hazard).
-#define QR_KV_DPP8(CTRL, r, s)                                                         \
-  asm volatile(                                                                        \
-      "s_nop 1\n\t"                                                                    \
-      "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"                  \
-      : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), \
-        "+v"(r[7])                                                                     \
-      : "v"(s))
-
-// Lane-in-row c (0..15) -> 8-element chunk, linear over GF(2) with
-// kv_gmap(1) = 1, kv_gmap(2) = 2, kv_gmap(7) = 4, kv_gmap(15) = 8: the DPP
-// patterns xor 1, xor 2 (quad_perm), xor 7 (row_half_mirror) and xor 15
-// (row_mirror) then each flip exactly one chunk bit.
-__device__ __forceinline__ int kv_gmap(int c) {
-  const int c0 = c & 1, c1 = (c >> 1) & 1, c2 = (c >> 2) & 1, c3 = (c >> 3) & 1;
-  return (c0 ^ c2) | ((c1 ^ c2) << 1) | ((c2 ^ c3) << 2) | (c3 << 3);
-}
 // Max / min over the 16 lanes of a DPP row (quad_perm [1,0,3,2] and [2,3,0,1],
 // row_half_mirror, row_mirror).
 template <int CTRL>
@@ -95,11 +71,11 @@ __global__ __launch_bounds__(256) void k_kv_quant(
   const int lpg = group / 8;  // lanes per group
   const int ngroups = DH / group;
   // With 16 lanes per row and one group per row the lane holds chunk
-  // kv_gmap(sub) and both the butterflies and the min / max run through DPP
+  // gmap(sub) and both the butterflies and the min / max run through DPP
   // inside the 16-lane row; the lane then holds sigma * z.  Otherwise chunk
   // sub and lane shuffles.
   const bool dpp = LPR == 16 && group == DH;
-  const int gc = dpp ? kv_gmap(sub) : sub;
+  const int gc = dpp ? gmap(sub) : sub;
   const int coff = gc * 8;
   const float sigma = (ROT && dpp && (__builtin_popcount(gc) & 1)) ? -1.0f : 1.0f;
   float sg[8];
@@ -142,10 +118,10 @@ __global__ __launch_bounds__(256) void k_kv_quant(
       if (LPR == 16 && dpp) {
         const float s0 = (gc & 1) ? -1.0f : 1.0f, s1 = (gc & 2) ? -1.0f : 1.0f;
         const float s2 = (gc & 4) ? -1.0f : 1.0f, s3 = (gc & 8) ? -1.0f : 1.0f;
-        QR_KV_DPP8("quad_perm:[1,0,3,2]", v, s0);
-        QR_KV_DPP8("quad_perm:[2,3,0,1]", v, s1);
-        QR_KV_DPP8("row_half_mirror", v, s2);
-        QR_KV_DPP8("row_mirror", v, s3);
+        QR_DPP8("quad_perm:[1,0,3,2]", v, s0);
+        QR_DPP8("quad_perm:[2,3,0,1]", v, s1);
+        QR_DPP8("row_half_mirror", v, s2);
+        QR_DPP8("row_mirror", v, s3);
       } else {
 #pragma unroll
         for (int hh = 1; hh < LPR; hh <<= 1) {

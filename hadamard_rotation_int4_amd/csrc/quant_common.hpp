@@ -81,21 +81,16 @@ __host__ __device__ inline QRange q_range(int bits) {
 
 // Streaming accesses: every input row is read once and every output written
 // once, so both bypass cache retention (non-temporal).
-#ifndef QR_NT
-#define QR_NT 1
-#endif
 __device__ __forceinline__ v4u ld_stream(const uint16_t* p) {
-  return QR_NT ? __builtin_nontemporal_load((const v4u*)p) : *(const v4u*)p;
+  return __builtin_nontemporal_load((const v4u*)p);
 }
 __device__ __forceinline__ void st_stream(uint32_t* p, uint32_t v) {
-  if (QR_NT) __builtin_nontemporal_store(v, p);
-  else *p = v;
+  __builtin_nontemporal_store(v, p);
 }
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void st_stream8(void* p, uint32_t lo, uint32_t hi) {
   const v2u v = {lo, hi};
-  if (QR_NT) __builtin_nontemporal_store(v, (v2u*)p);
-  else *(v2u*)p = v;
+  __builtin_nontemporal_store(v, (v2u*)p);
 }
 
 }  // namespace qr

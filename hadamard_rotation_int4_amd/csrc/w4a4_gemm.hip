@@ -485,17 +485,15 @@ static qr_status launch_best(const void* a_q, const void* a_scale, int64_t T, co
 // one 2-byte store per accumulator element).
 constexpr int DEC_BN = 16;
 
-#ifndef QR_DEC_WAVES
-#define QR_DEC_WAVES 4
-#endif
-// Cache policy of the weight stream (2 = non-temporal measured no faster).
-#ifndef QR_DEC_WPOL
-#define QR_DEC_WPOL 0
-#endif
-#ifndef QR_DEC_LOADS
-#define QR_DEC_LOADS 16
-#endif
-constexpr int DEC_WAVES = QR_DEC_WAVES;
+constexpr int DEC_WAVES = 4;
+// 16-byte loads in flight per lane and chunk: blocks per chunk CH = DEC_LOADS /
+// (S + MT).  The weight stream uses the default cache policy (non-temporal
+// measured no faster).
+constexpr int DEC_LOADS = 16;
+// Strip grouping: strips per workgroup until one workgroup per compute unit
+// (DEC_SLOTS) covers N, at most DEC_SMAX.
+constexpr int DEC_SLOTS = 256;
+constexpr int DEC_SMAX = 4;
 
 template <int MT, int S, int CH, bool DBG>
 __global__ __launch_bounds__(64 * DEC_WAVES, 1) void k_w4a4_decode(
@@ -530,7 +528,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES, 1) void k_w4a4_decode(
       for (int s = 0; s < S; ++s)
         wv[b][c][s] = __builtin_bit_cast(
             v4u, __builtin_amdgcn_raw_buffer_load_b128(
-                     rsrc_w, ok ? (16 * s + i) * rowbytes + byte : INT32_MIN, 0, QR_DEC_WPOL));
+                     rsrc_w, ok ? (16 * s + i) * rowbytes + byte : INT32_MIN, 0, 0));
 #pragma unroll
       for (int m = 0; m < MT; ++m)
         av[b][c][m] = __builtin_bit_cast(
@@ -629,7 +627,7 @@ static qr_status launch_decode_s(const void* a_q, const void* a_scale, int64_t T
                                  const void* w_scale, int64_t N, int64_t K, void* y, int32_t* acc,
                                  hipStream_t stream) {
   // Blocks per load chunk: two chunks of (S + MT) 16-byte loads per lane in flight.
-  constexpr int CH = (QR_DEC_LOADS / (S + MT)) > 0 ? QR_DEC_LOADS / (S + MT) : 1;
+  constexpr int CH = (DEC_LOADS / (S + MT)) > 0 ? DEC_LOADS / (S + MT) : 1;
   const int64_t blocks = (N + DEC_BN * S - 1) / (DEC_BN * S);
   if (acc)
     hipLaunchKernelGGL((k_w4a4_decode<MT, S, CH, true>), dim3((unsigned)blocks), dim3(64 * DEC_WAVES),
@@ -653,17 +651,11 @@ template <int MT>
 static qr_status launch_decode(const void* a_q, const void* a_scale, int64_t T, const void* w_q,
                                const void* w_scale, int64_t N, int64_t K, void* y, int32_t* acc,
                                hipStream_t stream) {
-#ifndef QR_DEC_SLOTS
-#define QR_DEC_SLOTS 256
-#endif
-#ifndef QR_DEC_SMAX
-#define QR_DEC_SMAX 4
-#endif
   const int64_t strips = (N + DEC_BN - 1) / DEC_BN;
   const int64_t s =
       MT == 1 ? 1
-              : std::min<int64_t>(QR_DEC_SMAX,
-                                  std::max<int64_t>(1, (strips + QR_DEC_SLOTS - 1) / QR_DEC_SLOTS));
+              : std::min<int64_t>(DEC_SMAX,
+                                  std::max<int64_t>(1, (strips + DEC_SLOTS - 1) / DEC_SLOTS));
   switch (s) {
     case 1: return launch_decode_s<MT, 1>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
     case 2: return launch_decode_s<MT, 2>(a_q, a_scale, T, w_q, w_scale, N, K, y, acc, stream);
