@@ -41,7 +41,8 @@ matches the hash recorded there, else null.  ``cpu_baseline`` is the oracle
 timed on the host on a bounded sample.
 
 --copy-calibration runs only a plain device copy of 1 GiB (ten times), the
-reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters.
+reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters, and
+prints its rate: the practical HBM ceiling of a read + write stream.
 """
 from __future__ import annotations
 

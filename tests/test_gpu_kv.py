@@ -96,3 +96,24 @@ def test_untouched_positions_and_noop():
     assert not np.all(hq[:, :, 5:7] == SENT_Q)
     qr.kv_rotate_quant(dev(x[:, :0]), None, 128, 1.0, cq, cm, 8)   # S_new = 0 at the end: no-op
     assert np.array_equal(host(cq), hq)
+
+
+@pytest.mark.parametrize("signed", [True, False])
+def test_strided_tokens_and_plain_hadamard(signed):
+    # tokens padded to H * Dh + 64 elements (a slice of a wider projection
+    # output); signs NULL is the plain Hadamard (all +1).  Grid inputs: the
+    # cache is bit-exact against the oracle's recipe.
+    B, S, H, Dh, G, clip = 2, 21, 3, 128, 128, 0.95
+    ld = H * Dh + 64
+    x = wl.grid_activations(5, 77, B * S, ld).reshape(B, S, ld)
+    s = wl.signs(5, Dh) if signed else None
+    xt = dev(x)[:, :, :H * Dh].reshape(B, S, H, Dh)     # token stride ld, heads packed
+    assert xt.stride(1) == ld
+    cq, cm = fresh_cache(B, H, S + 3, Dh, G)
+    qr.kv_rotate_quant(xt, dev(s) if signed else None, G, clip, cq, cm, 2)
+    ref_q = np.full((B, H, S + 3, Dh // 2), SENT_Q, dtype=np.uint8)
+    ref_m = np.full((B, H, S + 3, 1, 2), SENT_M, dtype=np.float16)
+    okv.kv_rotate_quant_cache(x[:, :, :H * Dh].reshape(B, S, H, Dh), s, True, G, clip, ref_q, ref_m,
+                              2, mode="recipe")
+    assert np.array_equal(host(cq), ref_q)
+    assert np.array_equal(host(cm).view(np.uint16), ref_m.view(np.uint16))
