@@ -636,17 +636,16 @@ __global__ __launch_bounds__(256) void k_hq_lds(const uint16_t* __restrict__ x, 
 // H_256 over G remains, in fp32 VALU: G = 64 w + 16 ct + gmap(n) with w the
 // wavefront, ct the lane's column tile (4 per wavefront): four stages through
 // DPP across lanes, two between registers, and a radix-4 stage across the
-// wavefronts through LDS (four rounds of 7 chunk positions).  After it each
-// wavefront owns column tile ct = w of all four w'' and so whole chunks; amax
-// is reduced through LDS, and each lane stores its chunks' 14 bytes of packed
-// codes directly (two-byte stores: measured faster than staging the row in
-// LDS for 16-byte stores, which costs two more barriers per row).
-// The exchange across the wavefronts runs in K28_ROUNDS rounds of K28_RV chunk
-// positions (its LDS buffer holds one round: more would not leave room for two
-// workgroups per CU).
-constexpr int K28_ROUNDS = 4;
-constexpr int K28_RV = 28 / K28_ROUNDS;               // chunk positions per exchange round
-constexpr int K28_XROUND = 4 * 4 * K28_RV * 64;       // floats per round: [w][ct][RV][lane]
+// wavefronts through LDS (rounds of 8, 8, 8 and 4 chunk positions).  After it
+// each wavefront owns column tile ct = w of all four w'' and so whole chunks;
+// amax is reduced through LDS, and each lane stores its chunks' 14 bytes of
+// packed codes directly (two-byte stores: measured faster than staging the row
+// in LDS for 16-byte stores, which costs two more barriers per row).
+// The exchange moves each lane's values as 16-byte blocks [w][ct][kb][lane]
+// (four positions per block, two blocks per round); its LDS buffer holds one
+// round: more would not leave room for two workgroups per CU.
+constexpr int K28_XBLK = 2;                           // 16-byte blocks per (w, ct) and round
+constexpr int K28_XROUND = 4 * 4 * K28_XBLK * 4 * 64;  // floats per round
 constexpr int K28_AFRAG = 7 * 4 * 64;                 // A fragments: [mt][kb][lane]
 
 // H_112 = H_4 (x) H_28 in MFMA A-fragment layout, built at compile time: tile
@@ -862,7 +861,7 @@ __global__ __launch_bounds__(256, K28_WAVES_PER_SIMD) void k_hq_k28(const uint16
                                                    void* __restrict__ yout) {
   constexpr int D = 28672;
   __shared__ v8h s_afrag[K28_AFRAG];           // 28 KB
-  __shared__ float s_x[K28_XROUND];            // exchange rounds
+  __shared__ __attribute__((aligned(16))) float s_x[K28_XROUND];  // exchange rounds
   __shared__ v4u s_sbits[4 * 4 * 64];         // 16 KB
   __shared__ float s_red[4];
   const int tid = threadIdx.x;
@@ -1015,25 +1014,35 @@ __global__ __launch_bounds__(256, K28_WAVES_PER_SIMD) void k_hq_k28(const uint16
     // ---- H_4 over the wavefront index through LDS; afterwards v[w''][k] holds
     //      chunk 4 G + g, G = (4 w'' + w) 16 + gmap(n), position k ----
     float o[4][28];
+    v4f* s_x4 = (v4f*)s_x;
 #pragma unroll
-    for (int rnd = 0; rnd < K28_ROUNDS; ++rnd) {
+    for (int rnd = 0; rnd < 4; ++rnd) {
+      const int nb = rnd < 3 ? K28_XBLK : 1;  // blocks of 4 positions: 8, 8, 8, then 4
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int k = 0; k < K28_RV; ++k)
-          s_x[((w * 4 + ct) * K28_RV + k) * 64 + lane] = v[ct][K28_RV * rnd + k];
+        for (int kb = 0; kb < nb; ++kb) {
+          const int k0 = 8 * rnd + 4 * kb;
+          s_x4[((w * 4 + ct) * K28_XBLK + kb) * 64 + lane] =
+              v4f{v[ct][k0], v[ct][k0 + 1], v[ct][k0 + 2], v[ct][k0 + 3]};
+        }
       __syncthreads();
 #pragma unroll
-      for (int k = 0; k < K28_RV; ++k) {
-        const float a0 = s_x[((0 * 4 + w) * K28_RV + k) * 64 + lane];
-        const float a1 = s_x[((1 * 4 + w) * K28_RV + k) * 64 + lane];
-        const float a2 = s_x[((2 * 4 + w) * K28_RV + k) * 64 + lane];
-        const float a3 = s_x[((3 * 4 + w) * K28_RV + k) * 64 + lane];
-        const float p01 = a0 + a1, m01 = a0 - a1, p23 = a2 + a3, m23 = a2 - a3;
-        o[0][K28_RV * rnd + k] = p01 + p23;
-        o[1][K28_RV * rnd + k] = m01 + m23;
-        o[2][K28_RV * rnd + k] = p01 - p23;
-        o[3][K28_RV * rnd + k] = m01 - m23;
+      for (int kb = 0; kb < nb; ++kb) {
+        const int k0 = 8 * rnd + 4 * kb;
+        const v4f a0 = s_x4[((0 * 4 + w) * K28_XBLK + kb) * 64 + lane];
+        const v4f a1 = s_x4[((1 * 4 + w) * K28_XBLK + kb) * 64 + lane];
+        const v4f a2 = s_x4[((2 * 4 + w) * K28_XBLK + kb) * 64 + lane];
+        const v4f a3 = s_x4[((3 * 4 + w) * K28_XBLK + kb) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p01 = a0[j] + a1[j], m01 = a0[j] - a1[j];
+          const float p23 = a2[j] + a3[j], m23 = a2[j] - a3[j];
+          o[0][k0 + j] = p01 + p23;
+          o[1][k0 + j] = m01 + m23;
+          o[2][k0 + j] = p01 - p23;
+          o[3][k0 + j] = m01 - m23;
+        }
       }
       __syncthreads();
     }
