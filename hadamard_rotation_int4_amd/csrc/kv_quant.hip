@@ -213,6 +213,7 @@ __global__ __launch_bounds__(256) void k_kv_quant(
 // 70B Init shape, so that each wavefront's next tile is in flight (one tile per
 // wavefront measured 25% slower).
 constexpr int KV128_GRID_CAP = 2048;
+typedef uint32_t v4u_a4 __attribute__((ext_vector_type(4), aligned(4)));
 template <bool ROT>
 __global__ __launch_bounds__(256) void k_kv_quant128(
     const uint16_t* __restrict__ x, int64_t rows, int S_new, int H, int64_t ld_token,
@@ -350,27 +351,54 @@ __global__ __launch_bounds__(256) void k_kv_quant128(
     const float shf = h2f(sh);
     const float mhf = h2f(mh);
     const float inv = shf > 0.0f ? __fdiv_rn(1.0f, shf) : 0.0f;
+    // Code word h of lane (n, g) holds elements 32 h + 8 g .. + 7, bytes 16 h + 4 g of
+    // the row's 64.  A 4 x 4 transpose over the row's four lanes (g) and words (h)
+    // gives lane g bytes 16 g .. + 15, so each row is one 64-byte piece of a single
+    // store instruction (four 4-byte stores per lane cost 11% more time at the 70B
+    // Init shape).
+    uint32_t wd[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      uint32_t f[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // kMagic + rne((y - m_h) * inv), clamped to [0, levels] (m_h and s_h
+        // are rounded to fp16, so the clamp is needed even without clipping)
+        float t = fmaf(__fsub_rn(z[h][j], mhf), inv, kMagic);
+        t = __builtin_amdgcn_fmed3f(t, kMagic, kMagic + levels);
+        f[j] = __float_as_uint(t);
+      }
+      const uint32_t p0 = (f[1] << 4) | (f[0] & 0xfu);
+      const uint32_t p1 = (f[3] << 4) | (f[2] & 0xfu);
+      const uint32_t p2 = (f[5] << 4) | (f[4] & 0xfu);
+      const uint32_t p3 = (f[7] << 4) | (f[6] & 0xfu);
+      wd[h] = __builtin_amdgcn_perm(p1, p0, 0x0c0c0400u) | __builtin_amdgcn_perm(p3, p2, 0x04000c0cu);
+    }
+    {
+      // v_permlane32_swap(a, b) exchanges a of lanes 32..63 with b of lanes 0..31:
+      // lanes g < 2 give words 2, 3 for the upper lanes' words 0, 1.
+      // v_permlane16_swap(a, b) exchanges a of the odd 16-lane rows with b of the
+      // even ones: even g give word 1 (3) for the odd neighbour's word 0 (2).
+      const auto s0 = __builtin_amdgcn_permlane32_swap(wd[0], wd[2], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(wd[1], wd[3], false, false);
+      wd[0] = s0[0];
+      wd[2] = s0[1];
+      wd[1] = s1[0];
+      wd[3] = s1[1];
+      const auto t0 = __builtin_amdgcn_permlane16_swap(wd[0], wd[1], false, false);
+      const auto t1 = __builtin_amdgcn_permlane16_swap(wd[2], wd[3], false, false);
+      wd[0] = t0[0];
+      wd[1] = t0[1];
+      wd[2] = t1[0];
+      wd[3] = t1[1];
+    }
     if (valid) {
       const int64_t crow = ix.bh * (int64_t)S_max + start_pos + ix.s;
-      uint8_t* crw = cq + crow * (DH / 2) + 4 * g;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        uint32_t f[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          // kMagic + rne((y - m_h) * inv), clamped to [0, levels] (m_h and s_h
-          // are rounded to fp16, so the clamp is needed even without clipping)
-          float t = fmaf(__fsub_rn(z[h][j], mhf), inv, kMagic);
-          t = __builtin_amdgcn_fmed3f(t, kMagic, kMagic + levels);
-          f[j] = __float_as_uint(t);
-        }
-        const uint32_t p0 = (f[1] << 4) | (f[0] & 0xfu);
-        const uint32_t p1 = (f[3] << 4) | (f[2] & 0xfu);
-        const uint32_t p2 = (f[5] << 4) | (f[4] & 0xfu);
-        const uint32_t p3 = (f[7] << 4) | (f[6] & 0xfu);
-        *(uint32_t*)(crw + 16 * h) = __builtin_amdgcn_perm(p1, p0, 0x0c0c0400u) |
-                                     __builtin_amdgcn_perm(p3, p2, 0x04000c0cu);
-      }
+      // cache_q is only required to be 4-byte aligned: a dword-aligned vector type
+      __builtin_nontemporal_store(v4u_a4{wd[0], wd[1], wd[2], wd[3]},
+                                  (v4u_a4*)(cq + crow * (DH / 2) + 16 * g));
+      // (scale, min) pairs as plain stores: 4-byte pieces the L2 merges into lines
+      // (non-temporal was slower)
       if (g == 0) *(uint32_t*)(meta + crow * 2) = (uint32_t)sh | ((uint32_t)mh << 16);
     }
 #pragma unroll

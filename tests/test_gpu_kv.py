@@ -117,3 +117,30 @@ def test_strided_tokens_and_plain_hadamard(signed):
                               2, mode="recipe")
     assert np.array_equal(host(cq), ref_q)
     assert np.array_equal(host(cm).view(np.uint16), ref_m.view(np.uint16))
+
+
+@pytest.mark.parametrize("rot", [True, False])
+def test_cache_only_dword_aligned(rot):
+    # cache_q needs only 4-byte alignment: a view 4 bytes into a buffer (the Dh = 128
+    # kernel writes each row's 64 bytes as 16-byte pieces at that address); Init and
+    # one Append on grid inputs are bit-exact against the oracle's recipe, and the
+    # bytes around the view stay untouched.
+    B, S, H, Dh, G, clip = 2, 21, 3, 128, 128, 0.95
+    S_max = S + 4
+    x = wl.grid_activations(5, 91, B * (S + 1) * H, Dh).reshape(B, S + 1, H, Dh)
+    s = wl.signs(5, Dh)
+    n = B * H * S_max * (Dh // 2)
+    buf = torch.full((n + 16,), SENT_Q, dtype=torch.uint8, device="cuda")
+    cq = buf[4:4 + n].view(B, H, S_max, Dh // 2)
+    assert cq.data_ptr() % 16 == 4
+    cm = torch.full((B, H, S_max, 1, 2), float(SENT_M), dtype=torch.float16, device="cuda")
+    ref_q = np.full((B, H, S_max, Dh // 2), SENT_Q, dtype=np.uint8)
+    ref_m = np.full((B, H, S_max, 1, 2), SENT_M, dtype=np.float16)
+    qr.kv_rotate_quant(dev(x[:, :S]), dev(s), G, clip, cq, cm, 1, rotate=rot)
+    okv.kv_rotate_quant_cache(x[:, :S], s, rot, G, clip, ref_q, ref_m, 1, mode="recipe")
+    qr.kv_rotate_quant(dev(x[:, S:]), dev(s), G, clip, cq, cm, S + 1, rotate=rot)
+    okv.kv_rotate_quant_cache(x[:, S:], s, rot, G, clip, ref_q, ref_m, S + 1, mode="recipe")
+    assert np.array_equal(host(cq), ref_q)
+    assert np.array_equal(host(cm).view(np.uint16), ref_m.view(np.uint16))
+    hb = host(buf)
+    assert np.all(hb[:4] == SENT_Q) and np.all(hb[4 + n:] == SENT_Q)
