@@ -48,6 +48,8 @@
 
 namespace qr {
 
+// 16 bytes at 4-byte alignment (y_f16 rows are only required to be 4-byte aligned)
+typedef uint32_t v4u_a4 __attribute__((ext_vector_type(4), aligned(4)));
 constexpr int KCH = 8;             // 16-byte k-chunks per row and step
 constexpr int GEMM_THREADS = 256;
 // Codes per 16-byte chunk and per K step for BITS = 4 (packed) or 8 (one per byte).
@@ -364,43 +366,70 @@ __global__ __launch_bounds__(GEMM_THREADS, (WM * WN <= 4 && !GROUPED) ? 2 : 1) v
   kstep((ksteps - 1) & 1, ksteps - 1, std::false_type{});
 
   // ---- epilogue: 32x32 accumulator layout: lane (n = li, k-half lg), register r
-  //      holds row 8 (r / 4) + 4 lg + (r % 4) ----
+  //      holds row 8 (r / 4) + 4 lg + (r % 4).  The scaled fp16 tile is staged
+  //      row-major in the LDS stages (free after the K loop) and stored as 16-byte
+  //      row pieces: one 2-byte store per element, as the first version made, left
+  //      the matrix cores idle for longer (the 256 x 256 tile 5% slower overall). ----
   float wsc[WN];
   if constexpr (!GROUPED) {
 #pragma unroll
     for (int j = 0; j < WN; ++j) wsc[j] = h2f(w_scale[min(n0 + wn + j * 32 + li, N - 1)]);
   }
+  __syncthreads();  // every wavefront's last fragment reads are done
+  uint16_t* sy = (uint16_t*)smem;  // [BM][BN] fp16; 16-byte pieces XOR-swizzled by row bit 2
 #pragma unroll
   for (int i = 0; i < WM; ++i) {
-    float asc[16];  // [r]: rows 8 (r / 4) + 4 lg + (r % 4) of block i
+    // [r]: token scale of row 8 (r / 4) + 4 lg + (r % 4) of block i, times 2^-SHIFT:
+    // fp32(acc) is exact (|acc| < 2^24 * 2^SHIFT, a multiple of 2^SHIFT) and
+    // scaling by a power of two commutes with rounding, so
+    // fp32(fp32(acc) * (a_s 2^-SHIFT)) == fp32(fp32(acc >> SHIFT) * a_s)
+    float asc[16];
     if constexpr (!GROUPED) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int t0 = m0 + wm + i * 32 + 8 * q4 + 4 * lg;
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) asc[4 * q4 + s2] = h2f(a_scale[min(t0 + s2, T - 1)]);
+        for (int s2 = 0; s2 < 4; ++s2)
+          asc[4 * q4 + s2] = h2f(a_scale[min(t0 + s2, T - 1)]) * (1.0f / (1 << CF::SHIFT));
       }
     }
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      const int n = n0 + wn + j * 32 + li;
-      if (n >= N) continue;
+      const int cl = wn + j * 32 + li;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int t = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-        if (t < T) {
-          if constexpr (GROUPED) {
-            Y[(int64_t)t * N + n] = f2h(__fmul_rn(facc[i][j][r], 1.0f / (1 << CF::SHIFT)));
-          } else {
-            const int32_t a = acc[i][j][r] >> CF::SHIFT;  // exact (INT4: 256 * acc)
-            Y[(int64_t)t * N + n] = f2h(__fmul_rn(__fmul_rn((float)a, asc[r]), wsc[j]));
-            if (DBG) acc_dbg[(int64_t)t * N + n] = a;
-          }
+        const int rl = wm + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+        uint16_t yv;
+        if constexpr (GROUPED) {
+          yv = f2h(__fmul_rn(facc[i][j][r], 1.0f / (1 << CF::SHIFT)));
+        } else {
+          yv = f2h(__fmul_rn(__fmul_rn((float)acc[i][j][r], asc[r]), wsc[j]));
+          if (DBG && m0 + rl < T && n0 + cl < N)
+            acc_dbg[(int64_t)(m0 + rl) * N + n0 + cl] = acc[i][j][r] >> CF::SHIFT;  // exact
         }
+        sy[rl * BN + (((cl >> 3) ^ (((rl >> 2) & 1) << 2)) << 3) + (cl & 7)] = yv;
       }
     }
   }
+  __syncthreads();
+  constexpr int CPR = BN / 8;  // 16-byte pieces per tile row
+  const bool wide = (N & 1) == 0;  // rows then start 4-byte aligned, as y_f16 is
+  for (int c = tid; c < BM * CPR; c += GEMM_THREADS) {
+    const int rl = c / CPR, ck = c % CPR;
+    const int t = m0 + rl, n = n0 + ck * 8;
+    if (t >= T || n >= N) continue;
+    const v4u_a4 v = *(const v4u_a4*)(sy + rl * BN + ((ck ^ (((rl >> 2) & 1) << 2)) << 3));
+    uint16_t* yp = Y + (int64_t)t * N + n;
+    if (wide && n + 8 <= N) {
+      __builtin_nontemporal_store(v, (v4u_a4*)yp);  // written once, read by the next op
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < N) yp[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+    }
+  }
 }
+
 
 template <int WM, int WN, bool DBG, bool KTAIL, int BITS, bool GROUPED = false, int PG = 0>
 static qr_status launch_gemm(const void* a_q, const void* a_scale, int64_t T, const void* w_q,
