@@ -55,8 +55,10 @@ def picks_256_tiles(T, N):
 
 
 # 256 x 256 tiles whose last tile row and column are partial, with K tails of
-# 64 and 192 past the 256-element K step (and one without a tail).
-RAGGED_256 = [(4000, 4000, 320), (3000, 4100, 4160), (3900, 3850, 448), (4000, 4000, 512)]
+# 64 and 192 past the 256-element K step (and one without a tail); N = 3999 is
+# odd, so output rows are not 4-byte aligned and every store is per element.
+RAGGED_256 = [(4000, 4000, 320), (3000, 4100, 4160), (3900, 3850, 448), (4000, 4000, 512),
+              (4000, 3999, 320)]
 
 
 def _edge_sample(n, seed):
@@ -77,6 +79,7 @@ def test_256_tiles_ragged_edges_and_k_tail(T, N, K, bits):
     asc = wl.positive_scales(3, 0, T)
     wsc = wl.positive_scales(3, 1, N)
     gemm = qr.w4a4_gemm if bits == 4 else qr.w8a8_gemm
+    y_plain = host(gemm(dev(a), dev(asc), dev(w), dev(wsc)))      # the kernel without acc_dbg
     y, acc = (host(t) for t in gemm(dev(a), dev(asc), dev(w), dev(wsc), acc_dbg=True))
     rows, cols = _edge_sample(T, T + K), _edge_sample(N, N + K)
     if bits == 4:
@@ -86,6 +89,7 @@ def test_256_tiles_ragged_edges_and_k_tail(T, N, K, bits):
     assert np.array_equal(acc[np.ix_(rows, cols)].astype(np.int64), acc_ref)
     y_ref = og.epilogue_recipe(acc_ref, asc[rows], wsc[cols])
     assert np.array_equal(y[np.ix_(rows, cols)].view(np.uint16), y_ref.view(np.uint16))
+    assert np.array_equal(y_plain.view(np.uint16), y.view(np.uint16))
 
 
 @pytest.mark.parametrize("T,N,K", SHAPES + KERNEL_SHAPES)
