@@ -41,6 +41,10 @@
 //  * Tile order: workgroup ids are remapped so that the ids the hardware places
 //    on one XCD (id % 8) are consecutive, then grouped 8 tile-rows at a time, so
 //    the tiles running together on an XCD share A and W panels in its L2.
+//  * Epilogue: the scaled fp16 tile is written row-major into the LDS stages
+//    (free once the K loop ends; 256 x 256 x 2 bytes fill them exactly) and
+//    leaves as non-temporal 16-byte row pieces, not one 2-byte store per
+//    accumulator element.
 #include <algorithm>
 #include <type_traits>
 
