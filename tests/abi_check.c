@@ -25,7 +25,7 @@ int main(void) {
   int32_t n = -1, m = -1;
 
   EXPECT(qr_abi_version() == QR_ABI_VERSION);
-  for (int code = QR_OK; code <= QR_ERR_ARG; ++code)
+  for (int code = QR_OK; code <= QR_ERR_SCRATCH; ++code)
     EXPECT(qr_status_str(code) != NULL && strncmp(qr_status_str(code), "QR_", 3) == 0);
   EXPECT(qr_status_str(1234) != NULL);
 
