@@ -30,6 +30,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+// 16 bytes at 4-byte alignment, for outputs whose contract promises only dword alignment
+typedef uint32_t v4u_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // fp32 value 1.5 * 2^23: fma(z, m, kMagic) = kMagic + round_half_even(z * m)
 // exactly (one rounding of the exact product) whenever |z * m| < 2^22, and the

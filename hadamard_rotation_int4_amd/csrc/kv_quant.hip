@@ -213,7 +213,6 @@ __global__ __launch_bounds__(256) void k_kv_quant(
 // 70B Init shape, so that each wavefront's next tile is in flight (one tile per
 // wavefront measured 25% slower).
 constexpr int KV128_GRID_CAP = 2048;
-typedef uint32_t v4u_a4 __attribute__((ext_vector_type(4), aligned(4)));
 template <bool ROT>
 __global__ __launch_bounds__(256) void k_kv_quant128(
     const uint16_t* __restrict__ x, int64_t rows, int S_new, int H, int64_t ld_token,

@@ -52,8 +52,6 @@
 
 namespace qr {
 
-// 16 bytes at 4-byte alignment (y_f16 rows are only required to be 4-byte aligned)
-typedef uint32_t v4u_a4 __attribute__((ext_vector_type(4), aligned(4)));
 constexpr int KCH = 8;             // 16-byte k-chunks per row and step
 constexpr int GEMM_THREADS = 256;
 // Codes per 16-byte chunk and per K step for BITS = 4 (packed) or 8 (one per byte).
@@ -379,6 +377,7 @@ __global__ __launch_bounds__(GEMM_THREADS, (WM * WN <= 4 && !GROUPED) ? 2 : 1) v
 #pragma unroll
     for (int j = 0; j < WN; ++j) wsc[j] = h2f(w_scale[min(n0 + wn + j * 32 + li, N - 1)]);
   }
+  static_assert(BM * BN * 2 <= Tl::LDS, "the fp16 output tile must fit in the LDS stages");
   __syncthreads();  // every wavefront's last fragment reads are done
   uint16_t* sy = (uint16_t*)smem;  // [BM][BN] fp16; 16-byte pieces XOR-swizzled by row bit 2
 #pragma unroll
