@@ -209,6 +209,8 @@ __global__ __launch_bounds__(256) void k_kv_quant(
 // picks a negated copy.  Products are +-x and the accumulation fp32, as in the
 // butterfly form.  Per element the vector units then only scale, reduce,
 // round and pack.  Without rotation the same lane layout holds the input.
+// The codes of a row leave as one 64-byte piece: a 4 x 4 transpose across the
+// row's four lanes gives each lane 16 contiguous bytes.
 // Workgroups of the Dh = 128 kernel: about four 16-row tiles per wavefront at the
 // 70B Init shape, so that each wavefront's next tile is in flight (one tile per
 // wavefront measured 25% slower).
