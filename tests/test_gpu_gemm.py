@@ -141,6 +141,27 @@ def test_output_without_debug_matches():
     assert np.array_equal(y.view(np.uint16), y_ref.view(np.uint16))
 
 
+@pytest.mark.parametrize("T,N,K", [(300, 260, 448), (4000, 4000, 320)])
+def test_output_only_dword_aligned(T, N, K):
+    # y_f16 needs only 4-byte alignment: an output 4 bytes into a buffer (the
+    # epilogue writes 16-byte row pieces at that alignment), for the 128 x 128 and
+    # the 256 x 256 tiles; bit-exact against the oracle's epilogue on sampled rows
+    # and columns, and the bytes around the view untouched.
+    ap = wl.packed_codes(3, 4, T, K)
+    wp = wl.packed_codes(3, 5, N, K)
+    asc = wl.positive_scales(3, 4, T)
+    wsc = wl.positive_scales(3, 5, N)
+    buf = torch.full((T * N + 8,), -2.0, dtype=torch.float16, device="cuda")
+    y = buf[2:2 + T * N].view(T, N)
+    assert y.data_ptr() % 16 == 4
+    qr.w4a4_gemm(dev(ap), dev(asc), dev(wp), dev(wsc), out=y)
+    rows, cols = _edge_sample(T, 7), _edge_sample(N, 8)
+    y_ref = og.epilogue_recipe(og.w4a4_acc(ap[rows], wp[cols]), asc[rows], wsc[cols])
+    assert np.array_equal(host(y)[np.ix_(rows, cols)].view(np.uint16), y_ref.view(np.uint16))
+    hb = host(buf)
+    assert np.all(hb[:2] == -2.0) and np.all(hb[2 + T * N:] == -2.0)
+
+
 def test_empty():
     z = dev(np.zeros((0, 32), dtype=np.uint8))
     w = dev(np.zeros((5, 32), dtype=np.uint8))
