@@ -43,6 +43,21 @@ def test_gaussian_with_outliers(d):
     check_sym_codes(q, sc, z64 / np.sqrt(d), 1.0)
 
 
+# Row counts just past one full pass of each kernel's grid: 2048 rows for the
+# d = 2^n kernel (512 workgroups x 4 wavefronts), 512 rows for d = 28672 and 11008
+# (512 workgroups, a row each); the first workgroup then carries one more row,
+# through its prefetch / double-buffer path.  Every row is checked.
+@pytest.mark.parametrize("d,T", [(8192, 2049), (4096, 2049), (28672, 513), (11008, 513),
+                                 (28672, 1025)])
+def test_one_row_past_a_full_grid_pass(d, T):
+    x = wl.activations(7, 1, T, d, n_outliers=5, lo=20, hi=100)
+    s = wl.signs(7, d)
+    q, sc, z = run(x, s)
+    z64 = oh.rotate_unnormalised(x.astype(np.float64), s)
+    check_rotation(z, z64)
+    check_sym_codes(q, sc, z64 / np.sqrt(d), 1.0)
+
+
 @pytest.mark.parametrize("d", [128, 512, 4096, 8192, 28672, 11008])
 def test_grid_inputs_bit_exact(d):
     T = 21
