@@ -3,7 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--workload 70b_prefill|7b_prefill|7b_decode|70b_kv|70b_block|7b_block|
                                 70b_block_w8a8|7b_block_w8a8]
-                    [--no-cpu-baseline] [--copy-calibration] [--fp16-hadamard]
+                    [--no-cpu-baseline] [--copy-calibration] [--mfma-calibration]
+                    [--fp16-hadamard]
 
 One step is one pass of the whole hot path over one batch of synthetic input
 (inputs resident in HBM; weights prepared offline and not timed):
@@ -43,6 +44,12 @@ timed on the host on a bounded sample.
 --copy-calibration runs only a plain device copy of 1 GiB (ten times), the
 reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters, and
 prints its rate: the practical HBM ceiling of a read + write stream.
+
+--mfma-calibration runs only the library's register-only loop of the GEMM's
+int8 MFMA (qr_calibrate_mfma_i8: no memory traffic, 8 wavefronts per SIMD)
+and prints the int-op rate it sustains, the shader clock it ran at and the
+fraction of the int8 peak at that clock: the practical ceiling of the matrix
+cores under the chip's power limit.
 """
 from __future__ import annotations
 
@@ -85,6 +92,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--mfma-calibration", action="store_true")
     ap.add_argument("--group", type=int, default=0,
                     help="prefill workloads: group-wise scales of this group size on both GEMM "
                          "operands (group-wise quantizer and grouped GEMM)")
@@ -511,6 +519,56 @@ def copy_calibration():
     return 0
 
 
+def mfma_calibration():
+    import numpy as np
+    import torch
+
+    import hadamard_rotation_int4_amd as qr
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(7)
+    # 16 q, q uniform in -8..7: the values the GEMM's unpacked INT4 operands take
+    frag = torch.from_numpy((16 * rng.integers(-8, 8, size=(64, 16))).astype(np.int8)).to(dev)
+    grid, iters = 2048, 4096
+    ops = 2.0 * 32 * 32 * 32 * 4 * iters * grid * 4
+    qr.calibrate_mfma_i8(frag, grid, 16)
+    torch.cuda.synchronize()
+    # 16 launches back to back (about 40 ms, as long as a block step's GEMMs),
+    # each bracketed by events and with its own clock counters
+    nl = 16
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)]
+    outs = []
+    ev[0].record()
+    for i in range(nl):
+        outs.append(qr.calibrate_mfma_i8(frag, grid, iters, clocks=True))
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    runs = []
+    for i, (chk, clk) in enumerate(outs):
+        ms = ev[i].elapsed_time(ev[i + 1])
+        c = clk.view(torch.int64).cpu().numpy().astype(np.float64)
+        mhz = float(np.mean((c[:, 1] - c[:, 0]) / ((c[:, 3] - c[:, 2]) / 100.0)))
+        pops = ops / (ms * 1e-3) / 1e15
+        runs.append({"ms": round(ms, 3), "POP/s": round(pops, 3), "clock_MHz": round(mhz),
+                     "frac_of_peak_at_clock": round(pops / (256 * 8192 * mhz * 1e6 / 1e15), 3)})
+    # every wavefront's checksums against the exact sum (include/qr.h)
+    f = frag.cpu().numpy().astype(np.int64)
+    total = 0
+    for j in range(4):
+        b = f[(np.arange(64) + 7 + 16 * j) % 64]
+        total += int((np.concatenate([f[:32], f[32:]], 1) @ np.concatenate([b[:32], b[32:]], 1).T).sum())
+    exact = all(bool(((c.cpu().numpy().astype(np.int64).reshape(-1, 64).sum(1) % 2**32)
+                      == (iters * total) % 2**32).all()) for c, _ in outs)
+    pops = sorted(r["POP/s"] for r in runs)
+    print(json.dumps({"mfma_calibration": True, "instruction": "v_mfma_i32_32x32x32_i8",
+                      "grid": grid, "wavefronts_per_simd": grid * 4 // 1024, "iters": iters,
+                      "int_ops_per_launch": ops, "checksums_exact": exact,
+                      "median_POP/s": pops[len(pops) // 2], "min_POP/s": pops[0], "max_POP/s": pops[-1],
+                      "median_clock_MHz": sorted(r["clock_MHz"] for r in runs)[len(runs) // 2],
+                      "peak_POP/s": INT8_PEAK_TOPS / 1e3,
+                      "runs": runs}), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -520,6 +578,8 @@ def main():
         return 2
     if args.copy_calibration:
         return copy_calibration()
+    if args.mfma_calibration:
+        return mfma_calibration()
     import torch
 
     import hadamard_rotation_int4_amd as qr

@@ -95,6 +95,8 @@ def _load():
     lib.qr_kv_decode_attention_noalloc.restype = ctypes.c_int
     lib.qr_kv_decode_attention_noalloc.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32,
                                                    i32, i32, f32, vp, vp]
+    lib.qr_calibrate_mfma_i8.restype = ctypes.c_int
+    lib.qr_calibrate_mfma_i8.argtypes = [vp, i32, i32, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -533,3 +535,21 @@ def kv_decode_attention_noalloc(q, k_cache_q, k_cache_meta, v_cache_q, v_cache_m
                                                   scale, _ptr(o), _stream(stream))
     _check(code, "qr_kv_decode_attention_noalloc")
     return o
+
+
+def calibrate_mfma_i8(fragments, grid: int, iters: int, clocks: bool = False, stream=None):
+    """Register-only loop of the GEMM's int8 MFMA (measurement support, not part
+    of the method): ``fragments`` is int8 [64, 16] on the GPU.  Returns the
+    int32 [grid * 256] per-thread checksums and, with ``clocks``, the uint64
+    [grid, 4] counters (shader clock start/end, 100 MHz counter start/end)."""
+    torch = _torch()
+    _need(fragments, torch.int8, "fragments", 2)
+    if tuple(fragments.shape) != (64, 16) or not fragments.is_contiguous():
+        raise ValueError("fragments must be a contiguous int8 [64, 16] tensor")
+    dev = fragments.device
+    chk = torch.empty((int(grid) * 256,), dtype=torch.int32, device=dev)
+    clk = torch.empty((int(grid), 4), dtype=torch.uint64, device=dev) if clocks else None
+    code = _load().qr_calibrate_mfma_i8(_ptr(fragments), int(grid), int(iters), _ptr(chk),
+                                        _ptr(clk), _stream(stream))
+    _check(code, "qr_calibrate_mfma_i8")
+    return (chk, clk) if clocks else chk

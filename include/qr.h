@@ -394,6 +394,30 @@ qr_status qr_kv_decode_attention_noalloc(const void* q_f16, int32_t B, int32_t H
                                          int32_t group, float softmax_scale, void* out_f16,
                                          hipStream_t stream);
 
+/*
+ * Measurement support, not a step of the method: the rate the int8 matrix
+ * cores that qr_w4a4_gemm runs on sustain with no memory traffic.  grid
+ * workgroups of 256 threads each run iters iterations of four independent
+ * chains of v_mfma_i32_32x32x32_i8 (4 x 65536 int ops per wavefront and
+ * iteration) on register-held fragments:
+ *   fragments_i8  [64, 16] int8 (input): lane l's A fragment is row l; its
+ *                 B fragment in chain j is row (l + 7 + 16 j) mod 64.  Each
+ *                 fragment is the lane's 16 bytes of the 32 x 32 x 32 operand
+ *                 (rows l mod 32; the lanes l < 32 and l >= 32 hold the two
+ *                 16-element halves of k).
+ *   checksum_i32  [grid * 256] int32 (output): per thread, the sum, modulo
+ *                 2^32, of its 4 x 16 accumulator values.  Over the 64 lanes
+ *                 of a wavefront this sums to iters * sum_j sum_{h, e}
+ *                 (sum_{l in half h} A_l[e]) (sum_{l in half h} B_{j,l}[e]).
+ *   clocks_u64    NULL, or [grid, 4] uint64 (output): per workgroup, the
+ *                 shader clock counter before and after wavefront 0's loop,
+ *                 then the 100 MHz constant counter before and after it.
+ * Requirements: grid >= 1 and iters >= 1 (else QR_ERR_SHAPE); fragments 16-,
+ * checksum 4- and clocks 8-byte aligned.
+ */
+qr_status qr_calibrate_mfma_i8(const void* fragments_i8, int32_t grid, int32_t iters,
+                               int32_t* checksum_i32, uint64_t* clocks_u64, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,6 +67,10 @@ int main(void) {
                                  0, NULL, st) == QR_ERR_ARG);
   EXPECT(qr_hadamard_quant_i8(A, 4, 8192, 8192, QR_ROT_HADAMARD, NULL, 1.0f, 8,
                               (char*)A + 4, A, NULL, st) == QR_ERR_ALIGN);
+  EXPECT(qr_calibrate_mfma_i8(A, 0, 100, (int32_t*)A, NULL, st) == QR_ERR_SHAPE);
+  EXPECT(qr_calibrate_mfma_i8(A, 8, 0, (int32_t*)A, NULL, st) == QR_ERR_SHAPE);
+  EXPECT(qr_calibrate_mfma_i8(NULL, 8, 100, (int32_t*)A, NULL, st) == QR_ERR_NULL);
+  EXPECT(qr_calibrate_mfma_i8((char*)A + 4, 8, 100, (int32_t*)A, NULL, st) == QR_ERR_ALIGN);
 
   if (failures) return 1;
   printf("abi_check: ok\n");
