@@ -24,20 +24,21 @@
 //    file, one workgroup per CU) is the default; 128 x 128 (WM = WN = 2, two
 //    workgroups per CU) is used when its estimated time is shorter: small
 //    grids that would leave compute units idle.  K advances 256 at a time
-//    through two LDS stages; the next step's panels are fetched into
-//    registers while the current one is multiplied, and written to the other
-//    stage at the end.
+//    through two LDS stages.  The buffer unit copies the next step's panels
+//    straight into the other stage (buffer_load ... lds: no registers, no LDS
+//    write instructions) while the current one is multiplied; each wavefront
+//    waits for its own copies before the barrier that ends the step.
 //  * Each lane reads whole 16-byte k-chunks (32 codes) and feeds two MFMAs from
 //    one chunk: lane (row, half h) takes chunk 2p + h for MFMA steps 2p and
 //    2p + 1, identically for A and W, so every k is summed exactly once.  The
 //    reads of the next chunk pair and the unpacking of the next half are
-//    interleaved with the current MFMAs (pinned with sched_group_barrier), and
-//    the staging of the next step's panels (LDS writes, global reads) is
-//    spread over the last half-step's MFMAs.
-//  * LDS layout [chunk][row ^ f(chunk)][16 bytes] with f(c) = 2c | parity(c):
-//    a half wavefront reads 32 rows of one chunk (512 contiguous bytes), and the
-//    staging writes -- 8 lanes per row, one per chunk -- land in distinct banks
-//    for both 8- and 16-lane LDS passes (f mod 8 and f >> 1 are permutations).
+//    interleaved with the current MFMAs (pinned with sched_group_barrier).
+//  * LDS layout: rows of 128 bytes, chunk c of row r at position c ^ h(r) with
+//    h(r) = (r mod 8) ^ (bit 3 of r).  A copy instruction fills 1 KB = 8 whole
+//    rows (lane l lands at 16 l, so each lane fetches the chunk the layout puts
+//    there and 8 lanes read one row's 128 contiguous bytes), and a fragment
+//    read -- 32 consecutive rows, one chunk -- hits distinct banks in both 8-
+//    and 16-lane LDS passes.
 //  * Tile order: workgroup ids are remapped so that the ids the hardware places
 //    on one XCD (id % 8) are consecutive, then grouped 8 tile-rows at a time, so
 //    the tiles running together on an XCD share A and W panels in its L2.
@@ -72,11 +73,14 @@ __device__ __forceinline__ v4i unpack16(uint2 d) {
   return r;
 }
 
-// LDS byte offset of 16-byte k-chunk `kk` of row r of a ROWS-row panel (swizzled).
-template <int ROWS>
+// LDS byte offset of 16-byte k-chunk `kk` of row r of a panel: rows of
+// KCH * 16 = 128 bytes, the chunk position XOR-swizzled by h(r) = (r mod 8) ^
+// (bit 3 of r).  h is a permutation on every 8 consecutive rows and on the even
+// (and the odd) rows of every 16, so the 8- and 16-lane passes of a fragment
+// read (consecutive rows, one chunk) hit distinct banks.
+__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int lds_off(int kk, int r) {
-  const int f = (kk << 1) | (__builtin_popcount(kk) & 1);
-  return kk * (ROWS * 16) + ((r ^ f) << 4);
+  return r * (KCH * 16) + ((kk ^ lds_swz(r)) << 4);
 }
 
 template <int WM, int WN, int BITS = 4>
@@ -90,7 +94,6 @@ struct GemmTile {
   // unpack VALU per MFMA (int8 operands go to the matrix cores as loaded)
   static constexpr int VPM = BITS == 4 ? (6 * (WM + WN) + MF - 1) / MF : 1;
   static constexpr int DSR = (WM + WN) * CodeFmt<BITS>::FR;  // fragment reads per pair
-  static constexpr int SPM = (PA + PW + MF - 1) / MF;     // staging writes/loads per MFMA
 };
 
 // BITS = 4: packed INT4 operands (K/2 bytes per row), unpacked in registers.
@@ -134,45 +137,57 @@ __global__ __launch_bounds__(GEMM_THREADS, (WM * WN <= 4 && !GROUPED) ? 2 : 1) v
   const int li = lane & 31, lg = lane >> 5;  // MFMA row/col lane, k-half
   const int64_t rowbytes = (int64_t)K * BITS / 8;
 
-  // ---- global -> register staging: 16-byte pieces, row = (tid >> 3) + 32 j,
-  //      k-chunk = tid & 7 (fixed per thread).  Raw buffer loads over the tile's
-  //      own rows: rows past T (or N) fall outside the buffer's range and read
-  //      as zero. ----
-  const int st_kk = tid & (KCH - 1);
-  const int st_r0 = tid / KCH;
+  // ---- global -> LDS, straight through the buffer unit: one wavefront
+  //      instruction fills one 1 KB block of 8 whole rows (lane l lands in slot
+  //      l: row 8 b + l / 8, position l % 8) and fetches the chunk the layout
+  //      puts there, so 8 lanes read one row's 128 contiguous bytes.  Block
+  //      b = 4 j + wave, so the lane's chunk ((l % 8) ^ h(row)) is the same for
+  //      every j.  Raw buffer loads over the tile's own rows: rows past T (or N)
+  //      fall outside the buffer's range (their outputs are never stored). ----
   const int rows_a = min(T - m0, BM), rows_w = min(N - n0, BN);
   const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(A + (int64_t)m0 * rowbytes), 0, (int)(rows_a * rowbytes), 0x00020000);
   const __amdgpu_buffer_rsrc_t rsrc_w = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(W + (int64_t)n0 * rowbytes), 0, (int)(rows_w * rowbytes), 0x00020000);
-  const int voff = st_r0 * (int)rowbytes + st_kk * 16;
-  const int rstep = (GEMM_THREADS / KCH) * (int)rowbytes;
-  v4u ra[Tl::PA], rw[Tl::PW];
-  auto gload = [&](int k0, bool last) {  // k0 in elements
-    // the whole offset goes in the VGPR operand: the range check of a raw
-    // buffer covers the VGPR offset, not the SGPR one
-#pragma unroll
-    for (int j = 0; j < Tl::PA; ++j)
-      ra[j] = __builtin_bit_cast(
-          v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff + j * rstep + k0 * BITS / 8, 0, 0));
-#pragma unroll
-    for (int j = 0; j < Tl::PW; ++j)
-      rw[j] = __builtin_bit_cast(
-          v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc_w, voff + j * rstep + k0 * BITS / 8, 0, 0));
-    if (KTAIL && last && k0 + st_kk * CF::EPC >= K) {  // chunk past K (K is a multiple of EPC)
-#pragma unroll
-      for (int j = 0; j < Tl::PA; ++j) ra[j] = v4u{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int j = 0; j < Tl::PW; ++j) rw[j] = v4u{0u, 0u, 0u, 0u};
-    }
-  };
-  auto lstore = [&](int stage) {
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int dl_kk = (lane & 7) ^ (lane >> 3) ^ (wave_u & 1);   // chunk of the lane's slot
+  const int voff = (8 * wave_u + (lane >> 3)) * (int)rowbytes + dl_kk * 16;
+  const int rstep = 32 * (int)rowbytes;                          // 4 blocks of 8 rows
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  auto dload = [&](int stage, int k0, bool last) {  // k0 in elements
     uint8_t* pa = smem + stage * Tl::STAGE;
     uint8_t* pw = pa + Tl::A_BYTES;
+    // the whole global offset goes in the VGPR operand: the range check of a
+    // raw buffer covers the VGPR offset, not the SGPR one.  The uniform part
+    // is formed per step (readfirstlane keeps the compiler from hoisting one
+    // VGPR per j out of the K loop).
 #pragma unroll
-    for (int j = 0; j < Tl::PA; ++j) *(v4u*)(pa + lds_off<BM>(st_kk, st_r0 + 32 * j)) = ra[j];
+    for (int j = 0; j < Tl::PA; ++j) {
+      const int so = __builtin_amdgcn_readfirstlane(j * rstep + k0 * BITS / 8);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_ptr_t)(pa + (4 * j + wave_u) * 1024), 16,
+                                               voff + so, 0, 0, 0);
+    }
 #pragma unroll
-    for (int j = 0; j < Tl::PW; ++j) *(v4u*)(pw + lds_off<BN>(st_kk, st_r0 + 32 * j)) = rw[j];
+    for (int j = 0; j < Tl::PW; ++j) {
+      const int so = __builtin_amdgcn_readfirstlane(j * rstep + k0 * BITS / 8);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_w, (lds_ptr_t)(pw + (4 * j + wave_u) * 1024), 16,
+                                               voff + so, 0, 0, 0);
+    }
+    (void)last;
+  };
+  // Wait for this wavefront's copies; in the last step of a K with a tail,
+  // clear the slots of chunks past K (they hold the next row's codes), each
+  // lane its own slot, which its own copy has already written.
+  auto dwait = [&](int stage, int k0, bool last) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (KTAIL && last && k0 + dl_kk * CF::EPC >= K) {
+      uint8_t* pa = smem + stage * Tl::STAGE;
+      uint8_t* pw = pa + Tl::A_BYTES;
+#pragma unroll
+      for (int j = 0; j < Tl::PA; ++j) *(v4u*)(pa + (4 * j + wave_u) * 1024 + lane * 16) = v4u{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < Tl::PW; ++j) *(v4u*)(pw + (4 * j + wave_u) * 1024 + lane * 16) = v4u{0u, 0u, 0u, 0u};
+    }
   };
   // fragments of chunk pair p: WM of A (rows wm + 32 i + li) and WN of W.
   // INT4: the lane takes chunk 2p + lg, both halves of which feed the pair's
@@ -185,10 +200,10 @@ __global__ __launch_bounds__(GEMM_THREADS, (WM * WN <= 4 && !GROUPED) ? 2 : 1) v
       const int kk = BITS == 4 ? 2 * p + lg : 4 * p + 2 * f + lg;
 #pragma unroll
       for (int i = 0; i < WM; ++i)
-        fa[f][i] = *(const v4u*)(pa + lds_off<BM>(kk, wm + i * 32 + li));
+        fa[f][i] = *(const v4u*)(pa + lds_off(kk, wm + i * 32 + li));
 #pragma unroll
       for (int j = 0; j < WN; ++j)
-        fb[f][j] = *(const v4u*)(pw + lds_off<BN>(kk, wn + j * 32 + li));
+        fb[f][j] = *(const v4u*)(pw + lds_off(kk, wn + j * 32 + li));
     }
   };
 
@@ -300,6 +315,8 @@ __global__ __launch_bounds__(GEMM_THREADS, (WM * WN <= 4 && !GROUPED) ? 2 : 1) v
   // half-step, fetch the step after it, and start reading the other stage.
   auto kstep = [&](int stage, int ks, auto more_tag) {
     constexpr bool MORE = decltype(more_tag)::value;
+    // the other stage was last read before the barrier that ended step ks - 1
+    if (MORE) dload(stage ^ 1, (ks + 1) * CF::BKE, ks + 2 == ksteps);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int cur = p & 1, nxt = cur ^ 1;
@@ -329,16 +346,13 @@ __global__ __launch_bounds__(GEMM_THREADS, (WM * WN <= 4 && !GROUPED) ? 2 : 1) v
         mfma_half(ua[0], ub[0], FRESH && p % PG == 0);
         unpack_half(fa[cur], fb[cur], 1, ua[1], ub[1]);
         if (MORE) {
-          lstore(stage ^ 1);
-          gload(min(ks + 2, ksteps - 1) * CF::BKE, ks + 3 >= ksteps);
 #pragma unroll
           for (int m = 0; m < Tl::MF; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
             __builtin_amdgcn_sched_group_barrier(0x002, Tl::VPM, 2);
-            __builtin_amdgcn_sched_group_barrier(0x200, Tl::SPM, 2);  // DS writes
-            __builtin_amdgcn_sched_group_barrier(0x020, Tl::SPM, 2);  // VMEM reads
           }
           __builtin_amdgcn_sched_barrier(0);
+          dwait(stage ^ 1, (ks + 1) * CF::BKE, ks + 2 == ksteps);
           __syncthreads();
           lread(stage ^ 1, 0, fa[nxt], fb[nxt]);
           mfma_half(ua[1], ub[1]);
@@ -358,10 +372,9 @@ __global__ __launch_bounds__(GEMM_THREADS, (WM * WN <= 4 && !GROUPED) ? 2 : 1) v
     }
   };
 
-  gload(0, ksteps == 1);
-  lstore(0);
+  dload(0, 0, ksteps == 1);
+  dwait(0, 0, ksteps == 1);
   __syncthreads();
-  gload(min(1, ksteps - 1) * CF::BKE, ksteps <= 2);
   lread(0, 0, fa[0], fb[0]);
   unpack_half(fa[0], fb[0], 0, ua[0], ub[0]);
   for (int ks = 0; ks + 1 < ksteps; ++ks) kstep(ks & 1, ks, std::true_type{});
