@@ -57,8 +57,10 @@ def picks_256_tiles(T, N):
 # 256 x 256 tiles whose last tile row and column are partial, with K tails of
 # 64 and 192 past the 256-element K step (and one without a tail); N = 3999 is
 # odd, so output rows are not 4-byte aligned and every store is per element.
+# K = 64, 192 and 256 are single K steps (the copies of the first step are the
+# only ones; 64 and 192 also clear the chunks past K in it).
 RAGGED_256 = [(4000, 4000, 320), (3000, 4100, 4160), (3900, 3850, 448), (4000, 4000, 512),
-              (4000, 3999, 320)]
+              (4000, 3999, 320), (4000, 4000, 64), (3900, 4000, 192), (4000, 4000, 256)]
 
 
 def _edge_sample(n, seed):
