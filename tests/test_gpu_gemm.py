@@ -119,6 +119,32 @@ def test_extreme_magnitude():
     assert np.array_equal(y.view(np.uint16), og.epilogue_recipe(og.w4a4_acc(ap, wp), asc, wsc).view(np.uint16))
 
 
+@pytest.mark.parametrize("T,N", [(40, 70), (300, 260), (4000, 4000)])
+def test_largest_k(T, N):
+    """K = 131008, the largest the entry point takes (|256 acc| < 2^31), on each of
+    the three kernels (weight streaming, 128 x 128 and 256 x 256 tiles): row 0 of
+    A all -8 against W rows of all -8 and all +7 gives acc = 64 K and -56 K, the
+    largest magnitudes; the other rows are random.  Sampled rows and columns
+    against the exact integer product and the epilogue recipe."""
+    K = 131008
+    print(f"gemm largest K: T={T} N={N} K={K}", flush=True)
+    ap = wl.packed_codes(4, 0, T, K)
+    wp = wl.packed_codes(4, 1, N, K)
+    ap[0] = 0x88
+    wp[0] = 0x88
+    wp[1] = 0x77
+    asc = wl.positive_scales(4, 0, T, 1e-6, 1e-4)
+    wsc = wl.positive_scales(4, 1, N, 1e-6, 1e-4)
+    y, acc = (host(t) for t in qr.w4a4_gemm(dev(ap), dev(asc), dev(wp), dev(wsc), acc_dbg=True))
+    assert acc[0, 0] == 64 * K and acc[0, 1] == -56 * K
+    rows = np.unique(np.r_[0, 1, T - 1, np.random.default_rng(T).choice(T, min(T, 24), replace=False)])
+    cols = np.unique(np.r_[0, 1, N - 1, np.random.default_rng(N).choice(N, min(N, 24), replace=False)])
+    acc_ref = og.w4a4_acc(ap[rows], wp[cols])
+    assert np.array_equal(acc[np.ix_(rows, cols)].astype(np.int64), acc_ref)
+    y_ref = og.epilogue_recipe(acc_ref, asc[rows], wsc[cols])
+    assert np.array_equal(y[np.ix_(rows, cols)].view(np.uint16), y_ref.view(np.uint16))
+
+
 def test_epilogue_overflow_and_zero_scales():
     T, N, K = 9, 33, 256
     ap = wl.packed_codes(2, 0, T, K)
