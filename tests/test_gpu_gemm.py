@@ -120,26 +120,38 @@ def test_extreme_magnitude():
 
 
 @pytest.mark.parametrize("T,N", [(40, 70), (300, 260), (4000, 4000)])
-def test_largest_k(T, N):
-    """K = 131008, the largest the entry point takes (|256 acc| < 2^31), on each of
-    the three kernels (weight streaming, 128 x 128 and 256 x 256 tiles): row 0 of
-    A all -8 against W rows of all -8 and all +7 gives acc = 64 K and -56 K, the
+@pytest.mark.parametrize("bits", [4, 8])
+def test_largest_k(T, N, bits):
+    """K = 131008, the largest the entry points take (|256 acc| < 2^31 for INT4,
+    |acc| < 2^31 for codes down to -128), on each kernel (weight streaming for
+    INT4, 128 x 128 and 256 x 256 tiles): row 0 of A at the most negative code
+    against W rows at the most negative and the most positive code gives the
     largest magnitudes; the other rows are random.  Sampled rows and columns
     against the exact integer product and the epilogue recipe."""
     K = 131008
-    print(f"gemm largest K: T={T} N={N} K={K}", flush=True)
-    ap = wl.packed_codes(4, 0, T, K)
-    wp = wl.packed_codes(4, 1, N, K)
-    ap[0] = 0x88
-    wp[0] = 0x88
-    wp[1] = 0x77
+    print(f"gemm largest K: bits={bits} T={T} N={N} K={K}", flush=True)
+    if bits == 4:
+        ap = wl.packed_codes(4, 0, T, K)
+        wp = wl.packed_codes(4, 1, N, K)
+        lo, hi, fill_lo, fill_hi = -8, 7, 0x88, 0x77
+    else:
+        ap = wl.packed_codes(4, 2, T, 2 * K).view(np.int8)
+        wp = wl.packed_codes(4, 3, N, 2 * K).view(np.int8)
+        lo, hi, fill_lo, fill_hi = -128, 127, -128, 127
+    ap[0] = fill_lo
+    wp[0] = fill_lo
+    wp[1] = fill_hi
     asc = wl.positive_scales(4, 0, T, 1e-6, 1e-4)
     wsc = wl.positive_scales(4, 1, N, 1e-6, 1e-4)
-    y, acc = (host(t) for t in qr.w4a4_gemm(dev(ap), dev(asc), dev(wp), dev(wsc), acc_dbg=True))
-    assert acc[0, 0] == 64 * K and acc[0, 1] == -56 * K
+    gemm = qr.w4a4_gemm if bits == 4 else qr.w8a8_gemm
+    y, acc = (host(t) for t in gemm(dev(ap), dev(asc), dev(wp), dev(wsc), acc_dbg=True))
+    assert acc[0, 0] == lo * lo * K and acc[0, 1] == lo * hi * K
     rows = np.unique(np.r_[0, 1, T - 1, np.random.default_rng(T).choice(T, min(T, 24), replace=False)])
     cols = np.unique(np.r_[0, 1, N - 1, np.random.default_rng(N).choice(N, min(N, 24), replace=False)])
-    acc_ref = og.w4a4_acc(ap[rows], wp[cols])
+    if bits == 4:
+        acc_ref = og.w4a4_acc(ap[rows], wp[cols])
+    else:
+        acc_ref = og.int_matmul_exact(ap[rows], wp[cols])
     assert np.array_equal(acc[np.ix_(rows, cols)].astype(np.int64), acc_ref)
     y_ref = og.epilogue_recipe(acc_ref, asc[rows], wsc[cols])
     assert np.array_equal(y[np.ix_(rows, cols)].view(np.uint16), y_ref.view(np.uint16))
