@@ -479,17 +479,43 @@ def profiled_traffic(kernel, workload):
         return None
 
 
+def calibrated_mfma_tops():
+    """Steady-state rate of the register-only int8 MFMA loop, from the committed
+    profiles/mfma_i8_calibration.txt (None if missing or taken on another source)."""
+    f = ROOT / "profiles" / "mfma_i8_calibration.txt"
+    if not f.exists():
+        return None
+    kv = {}
+    for line in f.read_text().splitlines():
+        if ":" in line and not line.startswith(("#", " ")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = CSRC / "calibrate.hip"
+    if not src.exists() or kv.get("source_sha256") != hashlib.sha256(src.read_bytes()).hexdigest():
+        return None
+    try:
+        return 1e3 * float(kv["steady_state_pops"])
+    except (KeyError, ValueError):
+        return None
+
+
 def roofline(kernel, workload, launches, per, bound):
     ms, nbytes, ops, n = kernel_totals(launches, per, kernel)
     tr = profiled_traffic(kernel, workload)
     if bound == "mfma":
         ach = ops / (ms * 1e-3) / 1e12
+        cal = calibrated_mfma_tops()
         return {"bound": "mfma", "kernel": kernel, "launches_per_step": n,
                 "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                 "op_note": "int8 MFMA operations (2 per multiply-accumulate) over the step's "
                            "launches of the kernel / their summed event time",
                 "frac": round(ach / INT8_PEAK_TOPS, 4),
-                "traffic": None if tr is None else round(tr)}
+                "traffic": None if tr is None else round(tr),
+                "practical_peak": None if cal is None else round(cal, 1),
+                "practical_frac": None if cal is None else round(ach / cal, 4),
+                "practical_note": "steady-state rate of the same MFMA instruction in a "
+                                  "register-only loop at the chip's power limit "
+                                  "(bench.py --mfma-calibration; profiles/mfma_i8_calibration.txt)"}
     ach = nbytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "kernel": kernel, "launches_per_step": n,
             "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -47,3 +47,11 @@ def test_decode_bytes(b, hkv, hq, L, dh, group):
     cache = nbytes(((b, hkv, L, dh // 2), np.uint8), ((b, hkv, L, dh // group, 2), np.float16))
     assert bench.decode_bytes(b, hkv, hq, L, dh, group) == 2 * cache + nbytes(
         ((b, hq, dh), np.float16), ((b, hq, dh), np.float16))
+
+
+def test_calibrated_mfma_ceiling_matches_its_source():
+    # the committed register-loop calibration was taken on the current calibration
+    # kernel source, and lies between the datasheet peak's power-limited share and it
+    tops = bench.calibrated_mfma_tops()
+    assert tops is not None
+    assert 3000.0 < tops < bench.INT8_PEAK_TOPS
