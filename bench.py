@@ -4,7 +4,7 @@
                     [--workload 70b_prefill|7b_prefill|7b_decode|70b_kv|70b_block|7b_block|
                                 70b_block_w8a8|7b_block_w8a8]
                     [--no-cpu-baseline] [--copy-calibration] [--mfma-calibration]
-                    [--fp16-hadamard]
+                    [--stream-calibration] [--fp16-hadamard]
 
 One step is one pass of the whole hot path over one batch of synthetic input
 (inputs resident in HBM; weights prepared offline and not timed):
@@ -50,6 +50,10 @@ int8 MFMA (qr_calibrate_mfma_i8: no memory traffic, 8 wavefronts per SIMD)
 and prints the int-op rate it sustains, the shader clock it ran at and the
 fraction of the int8 peak at that clock: the practical ceiling of the matrix
 cores under the chip's power limit.
+
+--stream-calibration runs only the library's plain stream with the rotate+quant
+traffic mix (qr_calibrate_stream: 1 GiB read, 256 MiB written, non-temporal)
+and prints its rate: the practical HBM ceiling of that mix.
 """
 from __future__ import annotations
 
@@ -93,6 +97,7 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--mfma-calibration", action="store_true")
+    ap.add_argument("--stream-calibration", action="store_true")
     ap.add_argument("--group", type=int, default=0,
                     help="prefill workloads: group-wise scales of this group size on both GEMM "
                          "operands (group-wise quantizer and grouped GEMM)")
@@ -479,10 +484,10 @@ def profiled_traffic(kernel, workload):
         return None
 
 
-def calibrated_mfma_tops():
-    """Steady-state rate of the register-only int8 MFMA loop, from the committed
-    profiles/mfma_i8_calibration.txt (None if missing or taken on another source)."""
-    f = ROOT / "profiles" / "mfma_i8_calibration.txt"
+def calibrated_value(name, key):
+    """A figure from a committed calibration summary profiles/<name>, or None if
+    it is missing or was taken on a different calibration-kernel source."""
+    f = ROOT / "profiles" / name
     if not f.exists():
         return None
     kv = {}
@@ -494,9 +499,21 @@ def calibrated_mfma_tops():
     if not src.exists() or kv.get("source_sha256") != hashlib.sha256(src.read_bytes()).hexdigest():
         return None
     try:
-        return 1e3 * float(kv["steady_state_pops"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
+
+
+def calibrated_stream_gbs():
+    """Median rate of the 16:4 read/write stream (profiles/hbm_stream_calibration.txt)."""
+    return calibrated_value("hbm_stream_calibration.txt", "median_gbs")
+
+
+def calibrated_mfma_tops():
+    """Steady-state rate of the register-only int8 MFMA loop, from the committed
+    profiles/mfma_i8_calibration.txt (None if missing or taken on another source)."""
+    v = calibrated_value("mfma_i8_calibration.txt", "steady_state_pops")
+    return None if v is None else 1e3 * v
 
 
 def roofline(kernel, workload, launches, per, bound):
@@ -517,9 +534,15 @@ def roofline(kernel, workload, launches, per, bound):
                                   "register-only loop at the chip's power limit "
                                   "(bench.py --mfma-calibration; profiles/mfma_i8_calibration.txt)"}
     ach = nbytes / (ms * 1e-3) / 1e9
+    cal = calibrated_stream_gbs()
     return {"bound": "hbm", "kernel": kernel, "launches_per_step": n,
             "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None if tr is None else round(tr)}
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None if tr is None else round(tr),
+            "practical_peak": None if cal is None else round(cal, 1),
+            "practical_frac": None if cal is None else round(ach / cal, 4),
+            "practical_note": "rate of a plain non-temporal stream reading 16 bytes for every 4 "
+                              "written (bench.py --stream-calibration; "
+                              "profiles/hbm_stream_calibration.txt)"}
 
 
 def copy_calibration():
@@ -595,6 +618,39 @@ def mfma_calibration():
     return 0
 
 
+def stream_calibration():
+    import numpy as np
+    import torch
+
+    import hadamard_rotation_int4_amd as qr
+    dev = torch.device("cuda:0")
+    n16 = (1 << 30) // 16  # the input bytes of one d = 8192 rotate+quant launch at T = 65536
+    src = torch.empty(n16 * 4, dtype=torch.int32, device=dev).random_()
+    out = torch.empty(n16, dtype=torch.uint32, device=dev)
+    grid = 2048
+    qr.calibrate_stream(src, grid, out=out)
+    torch.cuda.synchronize()
+    nl = 16
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)]
+    ev[0].record()
+    for i in range(nl):
+        qr.calibrate_stream(src, grid, out=out)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    nbytes = n16 * 20
+    runs = [round(nbytes / (ev[i].elapsed_time(ev[i + 1]) * 1e-3) / 1e9, 1) for i in range(nl)]
+    sv = src[: 4 * 4096].view(4096, 4).cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    ref = sv[:, 0] ^ sv[:, 1] ^ sv[:, 2] ^ sv[:, 3]
+    exact = bool((out[:4096].cpu().numpy().astype(np.int64) == ref).all())
+    srt = sorted(runs)
+    print(json.dumps({"stream_calibration": True, "bytes_read_per_launch": n16 * 16,
+                      "bytes_written_per_launch": n16 * 4, "grid": grid, "launches": nl,
+                      "first_4096_outputs_exact": exact,
+                      "median_GB/s": srt[nl // 2], "min_GB/s": srt[0], "max_GB/s": srt[-1],
+                      "runs_GB/s": runs}), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -606,6 +662,8 @@ def main():
         return copy_calibration()
     if args.mfma_calibration:
         return mfma_calibration()
+    if args.stream_calibration:
+        return stream_calibration()
     import torch
 
     import hadamard_rotation_int4_amd as qr

@@ -97,6 +97,8 @@ def _load():
                                                    i32, i32, f32, vp, vp]
     lib.qr_calibrate_mfma_i8.restype = ctypes.c_int
     lib.qr_calibrate_mfma_i8.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.qr_calibrate_stream.restype = ctypes.c_int
+    lib.qr_calibrate_stream.argtypes = [vp, i64, vp, i32, vp]
     _lib = lib
     return lib
 
@@ -553,3 +555,24 @@ def calibrate_mfma_i8(fragments, grid: int, iters: int, clocks: bool = False, st
                                         _ptr(clk), _stream(stream))
     _check(code, "qr_calibrate_mfma_i8")
     return (chk, clk) if clocks else chk
+
+
+def calibrate_stream(src, grid: int, out=None, stream=None):
+    """Plain stream with the rotate+quant traffic mix (measurement support, not
+    part of the method): ``src`` is a contiguous GPU tensor whose byte size is a
+    multiple of 16; returns uint32 [bytes / 16], the XOR of each 16-byte chunk's
+    four dwords."""
+    torch = _torch()
+    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    if nbytes % 16:
+        raise ValueError("src must hold a whole number of 16-byte chunks")
+    n16 = nbytes // 16
+    if out is None:
+        out = torch.empty((n16,), dtype=torch.uint32, device=src.device)
+    elif out.dtype != torch.uint32 or out.numel() != n16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint32 tensor of bytes / 16 elements")
+    code = _load().qr_calibrate_stream(_ptr(src), n16, _ptr(out), int(grid), _stream(stream))
+    _check(code, "qr_calibrate_stream")
+    return out

@@ -1,8 +1,10 @@
-// Measurement support for the W4A4 GEMM's roofline, not a step of the method:
-// the rate the int8 matrix cores sustain on this chip when nothing else runs
-// (qr_calibrate_mfma_i8).
+// Measurement support for the rooflines, not steps of the method:
+//  * qr_calibrate_mfma_i8: the rate the int8 matrix cores of the W4A4 GEMM
+//    sustain on this chip when nothing else runs;
+//  * qr_calibrate_stream: the rate of a plain stream with the rotate+quant
+//    kernels' mix of traffic, 16 bytes read for every 4 written.
 //
-// Every wavefront keeps its fragments in registers and issues four
+// The matrix-core loop: every wavefront keeps its fragments in registers and issues four
 // independent chains of v_mfma_i32_32x32x32_i8, the instruction the tiled GEMM
 // uses, with no memory traffic inside the loop.  Each chain has its own B
 // fragment, so no two chains compute the same product.  The operands are
@@ -52,7 +54,34 @@ __global__ __launch_bounds__(256) void k_calib_mfma_i8(const v4i* __restrict__ f
   }
 }
 
+// Grid-stride stream: chunk i (16 bytes) of src is read once (non-temporal) and
+// the XOR of its four dwords is written to dst[i] (non-temporal); each lane
+// keeps two chunks in flight.
+__global__ __launch_bounds__(256) void k_calib_stream(const v4u* __restrict__ src, int64_t n16,
+                                                      uint32_t* __restrict__ dst) {
+  const int64_t stride = (int64_t)gridDim.x * 512;
+  for (int64_t i = (int64_t)blockIdx.x * 512 + threadIdx.x; i < n16; i += stride) {
+    const int64_t i1 = i + 256;
+    const v4u a = __builtin_nontemporal_load(src + i);
+    const v4u b = i1 < n16 ? __builtin_nontemporal_load(src + i1) : v4u{0u, 0u, 0u, 0u};
+    __builtin_nontemporal_store(a[0] ^ a[1] ^ a[2] ^ a[3], dst + i);
+    if (i1 < n16) __builtin_nontemporal_store(b[0] ^ b[1] ^ b[2] ^ b[3], dst + i1);
+  }
+}
+
 }  // namespace qr
+
+extern "C" qr_status qr_calibrate_stream(const void* src, int64_t n16, void* dst_u32, int32_t grid,
+                                         hipStream_t stream) {
+  using namespace qr;
+  if (n16 < 0 || grid < 1) return QR_ERR_SHAPE;
+  if (n16 == 0) return QR_OK;
+  if (!src || !dst_u32) return QR_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(dst_u32, 4)) return QR_ERR_ALIGN;
+  hipLaunchKernelGGL(k_calib_stream, dim3(grid), dim3(256), 0, stream, (const v4u*)src, n16,
+                     (uint32_t*)dst_u32);
+  return launch_status();
+}
 
 extern "C" qr_status qr_calibrate_mfma_i8(const void* fragments_i8, int32_t grid, int32_t iters,
                                           int32_t* checksum_i32, uint64_t* clocks_u64,

@@ -418,6 +418,20 @@ qr_status qr_kv_decode_attention_noalloc(const void* q_f16, int32_t B, int32_t H
 qr_status qr_calibrate_mfma_i8(const void* fragments_i8, int32_t grid, int32_t iters,
                                int32_t* checksum_i32, uint64_t* clocks_u64, hipStream_t stream);
 
+/*
+ * Measurement support, not a step of the method: a plain stream with the
+ * rotate+quant kernels' traffic mix (16 bytes read for every 4 written), the
+ * practical HBM ceiling those kernels are measured against.
+ *   src      [n16] 16-byte chunks (input), read once, non-temporally.
+ *   dst_u32  [n16] uint32 (output): dst[i] = XOR of the four dwords of chunk i,
+ *            written once, non-temporally.
+ * grid workgroups of 256 threads stride over the chunks, two in flight per
+ * thread.  Requirements: n16 >= 0 (0 launches nothing) and grid >= 1 (else
+ * QR_ERR_SHAPE); src 16-byte and dst 4-byte aligned.
+ */
+qr_status qr_calibrate_stream(const void* src, int64_t n16, void* dst_u32, int32_t grid,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -71,6 +71,11 @@ int main(void) {
   EXPECT(qr_calibrate_mfma_i8(A, 8, 0, (int32_t*)A, NULL, st) == QR_ERR_SHAPE);
   EXPECT(qr_calibrate_mfma_i8(NULL, 8, 100, (int32_t*)A, NULL, st) == QR_ERR_NULL);
   EXPECT(qr_calibrate_mfma_i8((char*)A + 4, 8, 100, (int32_t*)A, NULL, st) == QR_ERR_ALIGN);
+  EXPECT(qr_calibrate_stream(A, 0, A, 8, st) == QR_OK);
+  EXPECT(qr_calibrate_stream(A, -1, A, 8, st) == QR_ERR_SHAPE);
+  EXPECT(qr_calibrate_stream(A, 16, A, 0, st) == QR_ERR_SHAPE);
+  EXPECT(qr_calibrate_stream(NULL, 16, A, 8, st) == QR_ERR_NULL);
+  EXPECT(qr_calibrate_stream((char*)A + 4, 16, A, 8, st) == QR_ERR_ALIGN);
 
   if (failures) return 1;
   printf("abi_check: ok\n");

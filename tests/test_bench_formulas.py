@@ -55,3 +55,9 @@ def test_calibrated_mfma_ceiling_matches_its_source():
     tops = bench.calibrated_mfma_tops()
     assert tops is not None
     assert 3000.0 < tops < bench.INT8_PEAK_TOPS
+
+
+def test_calibrated_stream_ceiling_matches_its_source():
+    gbs = bench.calibrated_stream_gbs()
+    assert gbs is not None
+    assert 4000.0 < gbs < bench.HBM_PEAK_GBS

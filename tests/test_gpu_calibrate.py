@@ -1,6 +1,8 @@
-"""qr_calibrate_mfma_i8, the register-only loop of the GEMM's int8 MFMA that
-calibrates the GEMM's roofline: every wavefront's checksums add up to the exact
-integer sum that include/qr.h states, and the clock counters advance."""
+"""The calibration kernels behind the practical ceilings the rooflines quote:
+qr_calibrate_mfma_i8 (the GEMM's int8 MFMA in a register-only loop): every
+wavefront's checksums add up to the exact integer sum include/qr.h states, and
+the clock counters advance; qr_calibrate_stream (the rotate+quant traffic mix):
+every output dword is the XOR fold of its 16-byte input chunk."""
 import numpy as np
 import pytest
 import torch
@@ -49,3 +51,13 @@ def test_without_clocks():
     torch.cuda.synchronize()
     per_wave = chk.cpu().numpy().astype(np.int64).reshape(16, 64).sum(1) % 2**32
     assert (per_wave == wave_sum(frag, 10)).all()
+
+
+@pytest.mark.parametrize("n16,grid", [(1, 1), (511, 1), (513, 1), (100003, 7), (1 << 20, 2048)])
+def test_stream_xor_fold(n16, grid):
+    print(f"calibrate stream n16={n16} grid={grid}", flush=True)
+    src = np.random.default_rng(n16).integers(0, 2**32, size=(n16, 4), dtype=np.uint32)
+    out = qr.calibrate_stream(torch.from_numpy(src).cuda(), grid)
+    torch.cuda.synchronize()
+    ref = src[:, 0] ^ src[:, 1] ^ src[:, 2] ^ src[:, 3]
+    assert np.array_equal(out.cpu().numpy(), ref)
