@@ -101,8 +101,12 @@ def test_quant_only(d):
     check_sym_exact(q, sc, x.astype(np.float64), d, False, 1.0)
 
 
-def test_row_stride_and_views():
-    d, T = 4096, 10
+@pytest.mark.parametrize("d", [128, 512, 4096, 344, 3584, 11008, 28672])
+def test_row_stride_and_views(d):
+    # every kernel family (d/8 lanes per row, one wavefront per row, LDS-staged,
+    # H_172 and H_4 (x) H_28 on the matrix cores) on rows 16 elements into a
+    # wider buffer, with a row stride of d + 64
+    T = 10
     big = wl.activations(6, 0, T, d + 64)
     view = dev(big)[:, 16:16 + d]
     s = wl.signs(6, d)
