@@ -56,6 +56,23 @@ def test_quant_groups(d, group):
     assert np.array_equal(q, oq.pack_int4(q_rec))
 
 
+@pytest.mark.parametrize("d", [4096, 11008])
+def test_quant_groups_row_stride(d):
+    # rows 16 elements into a wider buffer (row stride d + 64)
+    T, group = 7, 128
+    big = wl.activations(81, 0, T, d + 64, n_outliers=5)
+    s = wl.signs(81, d)
+    q, sc, z = (host(t) for t in qr.hadamard_quant_groups(dev(big)[:, 16:16 + d], dev(s), 1.0,
+                                                          group, z_dbg=True))
+    z64 = oh.rotate_unnormalised(big[:, 16:16 + d].astype(np.float64), s)
+    check_rotation(z, z64)
+    check_group_codes(q, sc, z64 / np.sqrt(d), group, 1.0)
+    c = np.full(T, oq.norm_constant(d, True), np.float32)
+    q_rec, s_rec = oq.sym_quant_groups_recipe(z, c, group)
+    assert np.array_equal(sc.view(np.uint16), s_rec.view(np.uint16))
+    assert np.array_equal(q, oq.pack_int4(q_rec))
+
+
 @pytest.mark.parametrize("clip", [1.0, 0.5])
 def test_quant_groups_no_rotation_edge_rows(clip):
     d, group = 4096, 128

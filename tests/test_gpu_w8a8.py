@@ -59,6 +59,24 @@ def test_hadamard_quant_i8_gaussian(d, bits):
     assert np.array_equal(q, q_rec)
 
 
+@pytest.mark.parametrize("d", [1024, 3584, 11008, 28672])
+def test_hadamard_quant_i8_row_stride(d):
+    # rows 16 elements into a wider buffer (row stride d + 64) on every kernel
+    # family of the b-bit quantizer
+    T, bits = 9, 8
+    big = wl.activations(42, 0, T, d + 64, n_outliers=4)
+    s = wl.signs(42, d)
+    q, sc, z = (host(t) for t in qr.hadamard_quant_i8(dev(big)[:, 16:16 + d], dev(s), 1.0, bits,
+                                                      z_dbg=True))
+    x = big[:, 16:16 + d]
+    z64 = oh.rotate_unnormalised(x.astype(np.float64), s)
+    check_rotation(z, z64)
+    check_codes_bits(q, sc, z64 / np.sqrt(d), 1.0, bits)
+    q_rec, s_rec = oq.sym_quant_recipe(z, d, True, 1.0, bits)
+    assert np.array_equal(sc.view(np.uint16), s_rec.view(np.uint16))
+    assert np.array_equal(q, q_rec)
+
+
 @pytest.mark.parametrize("bits", [8, 6, 4])
 def test_hadamard_quant_i8_clip_and_no_rotation(bits):
     d = 4096
